@@ -1,0 +1,183 @@
+/*
+ * nbattn -- neighbourhood attention for one context-parallel rank (MI355X / gfx950).
+ *
+ * A local query shard Q attends over its collected K/V neighbourhood: the
+ * causally valid ring chunks (owners <= cp_rank) concatenated in ascending
+ * order, or a left halo plus the local chunk.  The query shard is the suffix of
+ * the neighbourhood, so local query row i sits at neighbourhood position
+ * p = S - L + i (bottom-right alignment).  Sources, all NeMo AutoModel API pages:
+ *   - cp_local_ring page, module docstring: one bottom-right causal call with a
+ *     left window over the concatenated neighbourhood; per-document varlen
+ *     segments; a forward that saves what its backward needs (no recompute);
+ *   - cp_local_ring page, sliding_ring_compute_fa_fwd / _bwd: out[B,Hq,L,D] and
+ *     (dQ, dK by owner, dV by owner);
+ *   - cp_local_ring page, _fold_pad and _owner_grad_dict;
+ *   - blockdiag_cp.kernels page, _cp_blockdiag_mask and _cp_blockdiag_varlen:
+ *     a query attends a key iff same document, neither is padding (id 0), key
+ *     not after the query; the varlen form equals that mask + attention on the
+ *     real rows, padding rows are zeros;
+ *   - blockdiag_cp.kernels page, _varlen_backend_unavailable_reason and
+ *     _varlen_metadata_unavailable_reason: failures are found before any
+ *     kernel is launched.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises (except nb_segment_header, a debug
+ *     helper that does synchronise).  Work is enqueued on `stream` (a
+ *     hipStream_t, NULL = the default stream) and the call returns at once.
+ *   - Layouts are contiguous row-major: Q/O/dO/dQ [B,Hq,L,D]; K/V/dK/dV
+ *     [B,Hkv,S,D]; LSE [B,Hq,L] float32; doc ids / pad mask [B,S].
+ *   - GQA: q head h reads kv head h / (Hq / Hkv).
+ *   - window_left W >= 0: key j is visible from position p iff p - j <= W
+ *     (FlashAttention's window_size[0]: W+1 keys including the query's own);
+ *     W < 0: no window.
+ *   - Errors are detected before anything is enqueued: a non-OK return leaves
+ *     the stream untouched.  NB_ERR_LAUNCH reports a HIP launch failure.
+ *   - Thread-safe and stateless; calls on one stream are ordered by the stream.
+ */
+#ifndef NBATTN_H
+#define NBATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum nb_status {
+  NB_OK = 0,
+  NB_ERR_INVALID_ARG = 1,  /* null pointer, bad size, Hq % Hkv != 0, L > S, ... */
+  NB_ERR_UNSUPPORTED = 2,  /* D not in {64,128,256}, unknown dtype, dropout != 0 */
+  NB_ERR_WORKSPACE = 3,    /* workspace or segment buffer smaller than required */
+  NB_ERR_LAUNCH = 4,       /* a HIP launch failed (hipGetLastError) */
+  NB_ERR_DEVICE = 5        /* no usable gfx950 device / HIP runtime error */
+};
+
+enum nb_dtype {
+  NB_BF16 = 0, /* bfloat16 inputs/outputs, fp32 accumulation (main path) */
+  NB_F32 = 1   /* float32 inputs/outputs (debug path, same kernels) */
+};
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* nb_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int nb_version(void);
+
+/* ------------------------------------------------------------------------ *
+ * Segment buffer (int32), produced by nb_segment_build, read by the kernels.
+ * Offsets are in int32 elements, with N = B * L:
+ *   [0, 16)            header: n_seg, max_q, max_k, status, lo, B, L, S,
+ *                      window_left, n_real, then 6 reserved words
+ *   cu_q   [N + 1]     cumulative query-segment lengths (cu_seqlens_q)
+ *   cu_k   [N + 1]     cumulative key-segment lengths (cu_seqlens_k); cu_q[i]
+ *                      pairs with cu_k[i]
+ *   q_row0 [N]         b * L + first local query row of segment i
+ *   k_row0 [N]         b * S + first key of segment i
+ *   row_seg[N]         segment of local query row (b, i), -1 for padding rows
+ *   row_klo[N]         first key of that row's segment (neighbourhood position);
+ *                      p + 1 for padding rows (an empty key range)
+ *   kcov_lo[B]         first covered key of batch row b (S if none)
+ *   scratch            builder-private (duplicate-id detection)
+ * Entries past n_seg (past n_seg + 1 for cu_q / cu_k) are unspecified.
+ * ------------------------------------------------------------------------ */
+#define NB_SEG_HEADER 16
+enum {
+  NB_HDR_NSEG = 0, NB_HDR_MAXQ = 1, NB_HDR_MAXK = 2, NB_HDR_STATUS = 3, NB_HDR_LO = 4,
+  NB_HDR_B = 5, NB_HDR_L = 6, NB_HDR_S = 7, NB_HDR_WINDOW = 8, NB_HDR_NREAL = 9
+};
+/* status bit 0: some id > 0 occurs in two separate runs of one row (the
+ * per-document contract is violated; segments then follow runs). */
+#define NB_SEG_STATUS_SPLIT_DOC 1
+
+/* Element offsets of each array inside the segment buffer. */
+size_t nb_segment_offset_cu_q(int B, int L);
+size_t nb_segment_offset_cu_k(int B, int L);
+size_t nb_segment_offset_q_row0(int B, int L);
+size_t nb_segment_offset_k_row0(int B, int L);
+size_t nb_segment_offset_row_seg(int B, int L);
+size_t nb_segment_offset_row_klo(int B, int L);
+size_t nb_segment_offset_kcov_lo(int B, int L);
+
+/* int32 elements the caller must provide for seg_buf (0 on invalid sizes). */
+size_t nb_segment_buffer_elems(int B, int L, int S);
+
+/*
+ * Fold padding into the doc map and build the per-document varlen segments of
+ * the shard, on the device, without any device-to-host transfer.
+ *   cp_local_ring page, _fold_pad (pad -> id 0) and _cached_sliding_segments
+ *   (the key start of the straddling document is clipped at
+ *   lo = max(0, S - L - W) when W >= 0, else 0); blockdiag_cp.kernels page,
+ *   _cp_blockdiag_varlen (one segment per document the local rows touch: query
+ *   part = its local rows, key part = document start .. last local row) and
+ *   precompute_blockdiag_varlen_meta (built once per step, reused by every
+ *   layer and both passes).
+ * A document is a maximal run of one id > 0; ids <= 0 are padding.
+ *   doc_ids    [B,S] int32 device, neighbourhood doc map
+ *   pad_mask   [B,S] uint8 device, nonzero = padding, or NULL
+ *   folded_ids [B,S] int32 device, out: doc_ids with padding set to 0
+ *   seg_buf    device, out, seg_buf_elems >= nb_segment_buffer_elems(B, L, S)
+ * Requires 1 <= L <= S, B >= 1.  Segments are valid by construction.
+ */
+int nb_segment_build(const int32_t* doc_ids, const uint8_t* pad_mask, int B, int S, int L,
+                     int window_left, int32_t* folded_ids, int32_t* seg_buf,
+                     size_t seg_buf_elems, void* stream);
+
+/* Debug: copy the 16-word header to host memory (synchronises the stream). */
+int nb_segment_header(const int32_t* seg_buf, int32_t* host_header, void* stream);
+
+/* Bytes of workspace nb_attn_fwd needs (currently 0). */
+size_t nb_attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, int dtype);
+
+/*
+ * Forward: for every real query row and q head, softmax attention over the
+ * keys of its document band [max(row_klo, p - W), p]; saves LSE.
+ *   cp_local_ring page, sliding_ring_compute_fa_fwd; blockdiag_cp.kernels page,
+ *   _cp_blockdiag_varlen.
+ *   q   [B,Hq,L,D], k/v [B,Hkv,S,D]   (dtype), device
+ *   o   [B,Hq,L,D] out (dtype); padding rows written 0
+ *   o_resid [B,Hq,L,D] out (dtype) or NULL: the rounding residual of o (the
+ *       fp32 result minus the stored value, rounded to dtype).  Saved for the
+ *       backward, whose Delta = dO . O then uses an fp32-accurate O; for bf16
+ *       the backward is only within tolerance with it (for float32 pass NULL).
+ *   lse [B,Hq,L] float32 out: natural-log sum of exp(scale * q.k) over the
+ *       band; -inf for padding rows
+ *   seg_buf from nb_segment_build with the same B, L, S and window_left
+ *   scale > 0 (callers pass D^-0.5 for the default), dropout_p must be 0.
+ */
+int nb_attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_resid, float* lse,
+                const int32_t* seg_buf, int B, int Hq, int Hkv, int L, int S, int D, float scale,
+                int window_left, float dropout_p, int dtype, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* Bytes of workspace nb_attn_bwd needs (Delta rows: B * Hq * L floats, aligned). */
+size_t nb_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, int dtype);
+
+/*
+ * Backward with no forward recompute: dQ and dK/dV from the saved O and LSE.
+ *   cp_local_ring page, sliding_ring_compute_fa_bwd (returns dQ and per-owner
+ *   dK/dV) and _owner_grad_dict (owners this shard did not attend get zeros).
+ *   dout, q, o [B,Hq,L,D]; k, v [B,Hkv,S,D]; lse [B,Hq,L] (from nb_attn_fwd);
+ *   o_resid    the residual nb_attn_fwd saved, or NULL (Delta from o alone)
+ *   dq [B,Hq,L,D] out (0 on padding rows)
+ *   dk, dv [B,Hkv,S,D] out; every row is written, keys no query attended are 0
+ *   owner_off  HOST int32 [n_owner + 1], ascending neighbourhood offsets of the
+ *              owner chunks, owner_off[0] = 0, owner_off[n_owner] = S;
+ *              dK of owner o is dk[:, :, owner_off[o]:owner_off[o+1]]
+ *   owner_attended DEVICE uint8 [n_owner] out: 1 iff some real query attended
+ *              a key of chunk o (may be NULL when n_owner == 0)
+ *   1 <= n_owner <= 64, or n_owner == 0 with owner_off / owner_attended NULL.
+ *   ws: workspace of at least nb_attn_bwd_workspace_bytes bytes.
+ */
+int nb_attn_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o,
+                const void* o_resid, const float* lse, const int32_t* seg_buf, const int32_t* folded_ids, int B,
+                int Hq, int Hkv, int L, int S, int D, float scale, int window_left, int dtype,
+                void* dq, void* dk, void* dv, const int32_t* owner_off, int n_owner,
+                uint8_t* owner_attended, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NBATTN_H */

@@ -146,7 +146,8 @@ def attention_forward(q, k, v, folded, window, scale, heads=None, rows=None, row
     return O, LSE
 
 
-def attention_backward(q, k, v, dout, folded, window, scale, kv_heads=None, row_block=256):
+def attention_backward(q, k, v, dout, folded, window, scale, kv_heads=None, rows=None, keys=None,
+                       row_block=256):
     """Analytic gradients of ``sum(O * dO)`` (``sliding_ring_compute_fa_bwd`` by definition).
 
     With ``P`` the softmax probabilities above:
@@ -154,6 +155,9 @@ def attention_backward(q, k, v, dout, folded, window, scale, kv_heads=None, row_
     ``dQ = scale dS K``, ``dK = scale sum_{h in group} dS^T Q_h``,
     ``dV = sum_{h in group} P^T dO_h``.  Padding rows contribute nothing and get
     ``dQ = 0``.  ``kv_heads``: kv heads (and their q-head groups) to compute.
+    ``rows``: only these local query rows enter the sums (dQ of other rows is
+    left 0; dK/dV are then exact at every key no other real row attends).
+    ``keys``: dK/dV are accumulated only at these keys (others left 0).
     Returns ``(dQ [B,Hq,L,D], dK [B,Hkv,S,D], dV [B,Hkv,S,D])``; heads outside
     ``kv_heads`` are left zero.
     """
@@ -166,7 +170,8 @@ def attention_backward(q, k, v, dout, folded, window, scale, kv_heads=None, row_
     dQ = np.zeros_like(q)
     dK = np.zeros_like(k)
     dV = np.zeros_like(v)
-    rows = np.arange(L)
+    rows = np.arange(L) if rows is None else np.asarray(rows)
+    keys = np.arange(S) if keys is None else np.asarray(keys)
     for b in range(B):
         real_b = real_rows(folded[b:b + 1], L)[0]
         for kv in kv_heads:
@@ -178,8 +183,8 @@ def attention_backward(q, k, v, dout, folded, window, scale, kv_heads=None, row_
                     delta = (P * dP).sum(axis=1, keepdims=True)
                     dS = P * (dP - delta)
                     dQ[b, h, blk] = scale * (dS @ k[b, kv])
-                    dK[b, kv] += scale * (dS.T @ q[b, h, blk])
-                    dV[b, kv] += P.T @ dout[b, h, blk]
+                    dK[b, kv, keys] += scale * (dS[:, keys].T @ q[b, h, blk])
+                    dV[b, kv, keys] += P[:, keys].T @ dout[b, h, blk]
     return dQ, dK, dV
 
 

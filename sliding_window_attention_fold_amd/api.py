@@ -1,0 +1,254 @@
+"""Python binding of libnbattn: argument marshalling only.
+
+PyTorch provides device memory and the stream; every step of the computation
+runs in the HIP kernels behind the C-ABI.  The functions mirror the NeMo
+AutoModel ``cp_local_ring`` page: ``sliding_ring_compute_fa_fwd`` (forward,
+returns ``(out, saved)``), ``sliding_ring_compute_fa_bwd`` (backward, returns
+``dQ`` and per-owner dK/dV maps) and ``_owner_grad_dict`` (the full
+``owner -> grad`` map with zeros for owners the shard did not attend), with the
+per-step segment build of ``_cached_sliding_segments`` made explicit: the caller
+builds :class:`Segments` once per step and reuses it for every layer and both
+passes.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, field
+from typing import Dict, List, NamedTuple, Optional
+
+import torch
+
+from . import _lib
+
+__all__ = ["Segments", "OwnerTable", "Saved", "BwdResult", "segment_build", "attn_fwd", "attn_bwd",
+           "NeighbourhoodAttention", "neighbourhood_attention"]
+
+_DTYPES = {torch.bfloat16: _lib.NB_BF16, torch.float32: _lib.NB_F32}
+
+
+def _stream_ptr(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+@dataclass
+class Segments:
+    """Device segment buffer of one shard (built once per step, reused by every layer)."""
+
+    folded: torch.Tensor   # [B, S] int32, doc ids with padding folded to 0
+    buf: torch.Tensor      # int32 segment buffer (layout in include/nbattn.h)
+    B: int
+    L: int
+    S: int
+    window: int
+
+    def _view(self, fn: str, n: int) -> torch.Tensor:
+        off = getattr(_lib.load(), fn)(self.B, self.L)
+        return self.buf[off:off + n]
+
+    @property
+    def header(self) -> torch.Tensor:
+        return self.buf[:_lib.NB_SEG_HEADER]
+
+    def header_host(self) -> Dict[str, int]:
+        """Synchronising read of the header (debug)."""
+        h = (ctypes.c_int32 * _lib.NB_SEG_HEADER)()
+        _lib.check(_lib.load().nb_segment_header(_ptr(self.buf), ctypes.cast(h, ctypes.c_void_p),
+                                                 _stream_ptr(self.buf.device)), "nb_segment_header")
+        return {k: int(h[i]) for k, i in _lib.HDR.items()}
+
+    @property
+    def cu_q(self):
+        return self._view("nb_segment_offset_cu_q", self.B * self.L + 1)
+
+    @property
+    def cu_k(self):
+        return self._view("nb_segment_offset_cu_k", self.B * self.L + 1)
+
+    @property
+    def q_row0(self):
+        return self._view("nb_segment_offset_q_row0", self.B * self.L)
+
+    @property
+    def k_row0(self):
+        return self._view("nb_segment_offset_k_row0", self.B * self.L)
+
+    @property
+    def row_seg(self):
+        return self._view("nb_segment_offset_row_seg", self.B * self.L)
+
+    @property
+    def row_klo(self):
+        return self._view("nb_segment_offset_row_klo", self.B * self.L)
+
+    @property
+    def kcov_lo(self):
+        return self._view("nb_segment_offset_kcov_lo", self.B)
+
+
+def segment_build(nb_ids: torch.Tensor, L: int, window: int = -1,
+                  pad_mask: Optional[torch.Tensor] = None) -> Segments:
+    """Fold padding and build the per-document varlen segments on the device (no host sync)."""
+    lib = _lib.load()
+    _need(nb_ids.is_cuda and nb_ids.dtype == torch.int32 and nb_ids.dim() == 2 and nb_ids.is_contiguous(),
+          "nb_ids must be a contiguous [B, S] int32 device tensor")
+    B, S = nb_ids.shape
+    if pad_mask is not None:
+        _need(pad_mask.is_cuda and pad_mask.dtype == torch.uint8 and tuple(pad_mask.shape) == (B, S)
+              and pad_mask.is_contiguous(), "pad_mask must be a contiguous [B, S] uint8 device tensor")
+    n = lib.nb_segment_buffer_elems(B, L, S)
+    _need(n > 0, f"invalid sizes B={B} L={L} S={S}")
+    folded = torch.empty((B, S), dtype=torch.int32, device=nb_ids.device)
+    buf = torch.empty((n,), dtype=torch.int32, device=nb_ids.device)
+    w = -1 if window is None or window < 0 else int(window)
+    _lib.check(lib.nb_segment_build(_ptr(nb_ids), _ptr(pad_mask), B, S, L, w, _ptr(folded), _ptr(buf), n,
+                                    _stream_ptr(nb_ids.device)), "nb_segment_build")
+    return Segments(folded, buf, B, L, S, w)
+
+
+@dataclass
+class OwnerTable:
+    """Owner chunks of the neighbourhood, ascending (``_concat_neighborhood`` order).
+
+    ``offsets`` has ``len(owners) + 1`` entries from 0 to S.  ``cp_rank``,
+    ``cp_size`` and ``n_prior`` give the full map ``_owner_grad_dict`` returns:
+    every owner ``(cp_rank - d) % cp_size`` for ``d`` in ``0..n_prior``, with zeros
+    for owners outside the neighbourhood (future / wrapped).
+    """
+
+    offsets: List[int]
+    owners: List[int]
+    cp_rank: int = 0
+    cp_size: int = 1
+    n_prior: Optional[int] = None
+
+    @staticmethod
+    def ring(cp_rank: int, cp_size: int, chunk: int, n_prior: Optional[int] = None) -> "OwnerTable":
+        return OwnerTable([chunk * r for r in range(cp_rank + 2)], list(range(cp_rank + 1)),
+                          cp_rank, cp_size, cp_rank if n_prior is None else n_prior)
+
+    @staticmethod
+    def single(S: int) -> "OwnerTable":
+        return OwnerTable([0, S], [0], 0, 1, 0)
+
+
+class Saved(NamedTuple):
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    out: torch.Tensor
+    out_resid: Optional[torch.Tensor]  # rounding residual of out (bf16 path), None for float32
+    lse: torch.Tensor
+    seg: Segments
+    scale: float
+
+
+class BwdResult(NamedTuple):
+    dq: torch.Tensor
+    dk_by_owner: Dict[int, torch.Tensor]
+    dv_by_owner: Dict[int, torch.Tensor]
+    attended: Dict[int, bool]
+    dk: torch.Tensor
+    dv: torch.Tensor
+
+
+def _check_qkv(q, k, v, seg: Segments):
+    _need(all(t.is_cuda and t.is_contiguous() for t in (q, k, v)), "q, k, v must be contiguous device tensors")
+    _need(q.dtype in _DTYPES and k.dtype == q.dtype and v.dtype == q.dtype, "dtype must be bfloat16 or float32")
+    _need(q.dim() == 4 and k.dim() == 4 and k.shape == v.shape, "q [B,Hq,L,D], k/v [B,Hkv,S,D]")
+    B, Hq, L, D = q.shape
+    Bk, Hkv, S, Dk = k.shape
+    _need(B == Bk == seg.B and L == seg.L and S == seg.S and D == Dk,
+          f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} segments B={seg.B} L={seg.L} S={seg.S}")
+    return B, Hq, Hkv, L, S, D
+
+
+def attn_fwd(q: torch.Tensor, k_nb: torch.Tensor, v_nb: torch.Tensor, seg: Segments,
+             scale: Optional[float] = None, dropout_p: float = 0.0):
+    """Forward; returns ``(out [B,Hq,L,D], saved)``.  ``scale=None`` means ``D ** -0.5``."""
+    lib = _lib.load()
+    B, Hq, Hkv, L, S, D = _check_qkv(q, k_nb, v_nb, seg)
+    scale = D ** -0.5 if scale is None else float(scale)
+    out = torch.empty_like(q)
+    resid = torch.empty_like(q) if q.dtype == torch.bfloat16 else None
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    _lib.check(lib.nb_attn_fwd(_ptr(q), _ptr(k_nb), _ptr(v_nb), _ptr(out), _ptr(resid), _ptr(lse), _ptr(seg.buf),
+                               B, Hq, Hkv, L, S, D, scale, seg.window, float(dropout_p), _DTYPES[q.dtype],
+                               None, 0, _stream_ptr(q.device)), "nb_attn_fwd")
+    return out, Saved(q, k_nb, v_nb, out, resid, lse, seg, scale)
+
+
+def attn_bwd(saved: Saved, grad_out: torch.Tensor, owners: Optional[OwnerTable] = None) -> BwdResult:
+    """Backward from the saved forward (no recompute).
+
+    Returns ``BwdResult(dq, dk_by_owner, dv_by_owner, attended, dk, dv)``; the
+    per-owner entries are views of ``dk``/``dv`` (exact zeros for owners that were
+    not attended) plus zero tensors for owners outside the neighbourhood.
+    """
+    lib = _lib.load()
+    q, k, v, out, resid, lse, seg, scale = saved
+    B, Hq, Hkv, L, S, D = _check_qkv(q, k, v, seg)
+    _need(grad_out.shape == q.shape and grad_out.dtype == q.dtype and grad_out.is_contiguous(),
+          "grad_out must match q")
+    owners = OwnerTable.single(S) if owners is None else owners
+    off = [int(x) for x in owners.offsets]
+    n_owner = len(off) - 1
+    _need(n_owner == len(owners.owners), "offsets must have len(owners) + 1 entries")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    att = torch.empty((max(n_owner, 1),), dtype=torch.uint8, device=q.device)
+    ws_bytes = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, _DTYPES[q.dtype])
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=q.device)
+    off_c = (ctypes.c_int32 * len(off))(*off)
+    _lib.check(lib.nb_attn_bwd(_ptr(grad_out), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(resid), _ptr(lse),
+                               _ptr(seg.buf),
+                               _ptr(seg.folded), B, Hq, Hkv, L, S, D, scale, seg.window, _DTYPES[q.dtype],
+                               _ptr(dq), _ptr(dk), _ptr(dv), ctypes.cast(off_c, ctypes.c_void_p), n_owner,
+                               _ptr(att), _ptr(ws), ws_bytes, _stream_ptr(q.device)), "nb_attn_bwd")
+    att_host = att[:n_owner].tolist()
+    dk_by, dv_by, attended = {}, {}, {}
+    for o, rank in enumerate(owners.owners):
+        dk_by[rank] = dk[:, :, off[o]:off[o + 1]]
+        dv_by[rank] = dv[:, :, off[o]:off[o + 1]]
+        attended[rank] = bool(att_host[o])
+    n_prior = owners.n_prior if owners.n_prior is not None else len(owners.owners) - 1
+    for d in range(n_prior + 1):
+        r = (owners.cp_rank - d) % owners.cp_size
+        if r not in dk_by:
+            shape = (B, Hkv, L, D)  # a ring owner's chunk is one shard long
+            dk_by[r] = torch.zeros(shape, dtype=k.dtype, device=k.device)
+            dv_by[r] = torch.zeros(shape, dtype=v.dtype, device=v.device)
+            attended[r] = False
+    return BwdResult(dq, dk_by, dv_by, attended, dk, dv)
+
+
+class NeighbourhoodAttention(torch.autograd.Function):
+    """Autograd wrapper: forward saves (O, LSE), backward runs the library backward."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, seg: Segments, scale: Optional[float] = None):
+        out, saved = attn_fwd(q.contiguous(), k.contiguous(), v.contiguous(), seg, scale)
+        ctx.saved_meta = (seg, saved.scale, saved.out_resid is not None)
+        ctx.save_for_backward(saved.q, saved.k, saved.v, saved.out,
+                              saved.out_resid if saved.out_resid is not None else saved.lse, saved.lse)
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        q, k, v, out, resid, lse = ctx.saved_tensors
+        seg, scale, has_resid = ctx.saved_meta
+        r = attn_bwd(Saved(q, k, v, out, resid if has_resid else None, lse, seg, scale), grad_out.contiguous())
+        return r.dq, r.dk, r.dv, None, None
+
+
+def neighbourhood_attention(q, k, v, seg: Segments, scale: Optional[float] = None):
+    return NeighbourhoodAttention.apply(q, k, v, seg, scale)

@@ -1,0 +1,202 @@
+// C-ABI of nbattn: argument checks before any launch, then dispatch to the HIP
+// kernels on the caller's stream.  Nothing here allocates or synchronises
+// (except the debug header read).
+//
+// The checks mirror blockdiag_cp.kernels page, _varlen_backend_unavailable_reason
+// and _varlen_metadata_unavailable_reason (NeMo AutoModel): every reason a
+// kernel cannot run is found on the host without launching anything, and the
+// varlen metadata the kernels index with is produced on the device by the
+// segment builder, valid by construction, instead of being validated with a
+// device-to-host copy.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/nbattn.h"
+#include "nb_kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxIndex = (int64_t)1 << 30;  // positions and row counts stay in int32 math
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool dims_ok(int B, int L, int S) {
+  if (B < 1 || L < 1 || S < 1 || L > S) return false;
+  if (B > 65535) return false;
+  if ((int64_t)B * S >= kMaxIndex || (int64_t)S >= kMaxIndex) return false;
+  return true;
+}
+
+int map_hip(hipError_t e) {
+  if (e == hipSuccess) return NB_OK;
+  if (e == hipErrorNoDevice || e == hipErrorInvalidDevice || e == hipErrorNoBinaryForGpu) return NB_ERR_DEVICE;
+  return NB_ERR_LAUNCH;
+}
+
+int attn_common_checks(const void* const* ptrs, int nptrs, int B, int Hq, int Hkv, int L, int S, int D,
+                       float scale, int dtype) {
+  for (int x = 0; x < nptrs; ++x)
+    if (ptrs[x] == nullptr || !aligned16(ptrs[x])) return NB_ERR_INVALID_ARG;
+  if (!dims_ok(B, L, S)) return NB_ERR_INVALID_ARG;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Hq > 65535) return NB_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return NB_ERR_INVALID_ARG;
+  if (dtype != NB_BF16 && dtype != NB_F32) return NB_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128 && D != 256) return NB_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq * L >= kMaxIndex * 2 || (int64_t)B * Hkv * S >= kMaxIndex * 2) return NB_ERR_INVALID_ARG;
+  return NB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nb_status_string(int status) {
+  switch (status) {
+    case NB_OK: return "ok";
+    case NB_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or shape)";
+    case NB_ERR_UNSUPPORTED: return "unsupported (head dim not in {64,128,256}, unknown dtype, or dropout)";
+    case NB_ERR_WORKSPACE: return "workspace or segment buffer too small";
+    case NB_ERR_LAUNCH: return "HIP kernel launch failed";
+    case NB_ERR_DEVICE: return "no usable gfx950 device";
+    default: return "unknown status";
+  }
+}
+
+int nb_version(void) { return 100; }
+
+size_t nb_segment_offset_cu_q(int B, int L) { return nb::seg_layout(B, L, 1).cu_q; }
+size_t nb_segment_offset_cu_k(int B, int L) { return nb::seg_layout(B, L, 1).cu_k; }
+size_t nb_segment_offset_q_row0(int B, int L) { return nb::seg_layout(B, L, 1).q_row0; }
+size_t nb_segment_offset_k_row0(int B, int L) { return nb::seg_layout(B, L, 1).k_row0; }
+size_t nb_segment_offset_row_seg(int B, int L) { return nb::seg_layout(B, L, 1).row_seg; }
+size_t nb_segment_offset_row_klo(int B, int L) { return nb::seg_layout(B, L, 1).row_klo; }
+size_t nb_segment_offset_kcov_lo(int B, int L) { return nb::seg_layout(B, L, 1).kcov_lo; }
+
+size_t nb_segment_buffer_elems(int B, int L, int S) {
+  if (!dims_ok(B, L, S)) return 0;
+  return nb::seg_buffer_elems(B, L, S);
+}
+
+int nb_segment_build(const int32_t* doc_ids, const uint8_t* pad_mask, int B, int S, int L, int window_left,
+                     int32_t* folded_ids, int32_t* seg_buf, size_t seg_buf_elems, void* stream) {
+  if (doc_ids == nullptr || folded_ids == nullptr || seg_buf == nullptr) return NB_ERR_INVALID_ARG;
+  if (!dims_ok(B, L, S)) return NB_ERR_INVALID_ARG;
+  if (seg_buf_elems < nb::seg_buffer_elems(B, L, S)) return NB_ERR_WORKSPACE;
+  nb::SegParams p;
+  p.doc_ids = doc_ids;
+  p.pad_mask = pad_mask;
+  p.folded = folded_ids;
+  p.seg = seg_buf;
+  p.lay = nb::seg_layout(B, L, S);
+  p.B = B;
+  p.S = S;
+  p.L = L;
+  p.window = window_left < 0 ? -1 : window_left;
+  return map_hip(nb::launch_segment_build(p, (hipStream_t)stream));
+}
+
+int nb_segment_header(const int32_t* seg_buf, int32_t* host_header, void* stream) {
+  if (seg_buf == nullptr || host_header == nullptr) return NB_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(host_header, seg_buf, NB_SEG_HEADER * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return map_hip(e);
+}
+
+size_t nb_attn_fwd_workspace_bytes(int, int, int, int, int, int, int) { return 0; }
+
+int nb_attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_resid, float* lse, const int32_t* seg_buf, int B,
+                int Hq, int Hkv, int L, int S, int D, float scale, int window_left, float dropout_p, int dtype,
+                void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  const void* ptrs[] = {q, k, v, o, lse, seg_buf};
+  int st = attn_common_checks(ptrs, 6, B, Hq, Hkv, L, S, D, scale, dtype);
+  if (st != NB_OK) return st;
+  if (o_resid != nullptr && !aligned16(o_resid)) return NB_ERR_INVALID_ARG;
+  if (dropout_p != 0.f) return NB_ERR_UNSUPPORTED;
+  nb::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.o_lo = o_resid;
+  p.lse = lse;
+  p.row_klo = seg_buf + nb::seg_layout(B, L, S).row_klo;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.L = L;
+  p.S = S;
+  p.window = window_left < 0 ? -1 : window_left;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return map_hip(nb::launch_attn_fwd(p, D, dtype == NB_F32, (hipStream_t)stream));
+}
+
+size_t nb_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, int dtype) {
+  (void)Hkv;
+  (void)S;
+  (void)D;
+  (void)dtype;
+  if (B < 1 || Hq < 1 || L < 1) return 0;
+  const size_t delta = (size_t)B * Hq * L * sizeof(float);
+  return (delta + 255) & ~(size_t)255;
+}
+
+int nb_attn_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o, const void* o_resid,
+                const float* lse,
+                const int32_t* seg_buf, const int32_t* folded_ids, int B, int Hq, int Hkv, int L, int S, int D,
+                float scale, int window_left, int dtype, void* dq, void* dk, void* dv, const int32_t* owner_off,
+                int n_owner, uint8_t* owner_attended, void* ws, size_t ws_bytes, void* stream) {
+  const void* ptrs[] = {dout, q, k, v, o, lse, seg_buf, dq, dk, dv, ws};
+  int st = attn_common_checks(ptrs, 11, B, Hq, Hkv, L, S, D, scale, dtype);
+  if (st != NB_OK) return st;
+  if (o_resid != nullptr && !aligned16(o_resid)) return NB_ERR_INVALID_ARG;
+  if (ws_bytes < nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype)) return NB_ERR_WORKSPACE;
+  if (n_owner < 0 || n_owner > nb::kMaxOwners) return NB_ERR_INVALID_ARG;
+  nb::OwnerParams op;
+  if (n_owner > 0) {
+    if (owner_off == nullptr || owner_attended == nullptr || folded_ids == nullptr) return NB_ERR_INVALID_ARG;
+    if (owner_off[0] != 0 || owner_off[n_owner] != S) return NB_ERR_INVALID_ARG;
+    for (int x = 0; x < n_owner; ++x)
+      if (owner_off[x + 1] < owner_off[x]) return NB_ERR_INVALID_ARG;
+    std::memset(&op, 0, sizeof(op));
+    op.folded = folded_ids;
+    op.kcov_lo = seg_buf + nb::seg_layout(B, L, S).kcov_lo;
+    op.attended = owner_attended;
+    op.B = B;
+    op.S = S;
+    op.n_owner = n_owner;
+    for (int x = 0; x <= n_owner; ++x) op.off[x] = owner_off[x];
+  }
+  nb::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.o_lo = o_resid;
+  p.dout = dout;
+  p.lse = lse;
+  p.delta = reinterpret_cast<float*>(ws);
+  p.row_klo = seg_buf + nb::seg_layout(B, L, S).row_klo;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.L = L;
+  p.S = S;
+  p.window = window_left < 0 ? -1 : window_left;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+  st = map_hip(nb::launch_attn_bwd(p, D, dtype == NB_F32, s));
+  if (st != NB_OK || n_owner == 0) return st;
+  return map_hip(nb::launch_owner_flags(op, s));
+}
+
+}  // extern "C"

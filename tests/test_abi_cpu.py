@@ -1,0 +1,126 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, and its host-side preflight rejects bad arguments before launching."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from sliding_window_attention_fold_amd import _lib
+from sliding_window_attention_fold_amd import workloads as wl
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "nbattn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nb_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib.load()
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_status_strings_and_version():
+    lib = _lib.load()
+    assert lib.nb_version() == 100
+    assert _lib.status_string(0) == "ok"
+    for s in range(1, 6):
+        assert len(_lib.status_string(s)) > 10
+    assert _lib.status_string(99) == "unknown status"
+
+
+def test_segment_buffer_sizes():
+    lib = _lib.load()
+    assert lib.nb_segment_buffer_elems(0, 1, 1) == 0
+    assert lib.nb_segment_buffer_elems(1, 5, 4) == 0          # L > S
+    n = lib.nb_segment_buffer_elems(2, 8, 16)
+    N = 16
+    assert lib.nb_segment_offset_cu_q(2, 8) == 16
+    assert lib.nb_segment_offset_cu_k(2, 8) == 16 + N + 1
+    assert lib.nb_segment_offset_row_klo(2, 8) == 16 + 2 * (N + 1) + 3 * N
+    assert n >= lib.nb_segment_offset_kcov_lo(2, 8) + 2 + 2 * 16
+
+
+FAKE = 0x100000  # an aligned address that is never dereferenced: every call below fails preflight
+
+
+def _fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, seg=FAKE, B=1, Hq=2, Hkv=1, L=8, S=16, D=64,
+             scale=0.125, W=-1, drop=0.0, dtype=_lib.NB_BF16)
+    a.update(kw)
+    return _lib.load().nb_attn_fwd(a["q"], a["k"], a["v"], a["o"], None, a["lse"], a["seg"], a["B"], a["Hq"],
+                                   a["Hkv"], a["L"], a["S"], a["D"], a["scale"], a["W"], a["drop"],
+                                   a["dtype"], None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), _lib.NB_ERR_INVALID_ARG),
+    (dict(k=FAKE + 8), _lib.NB_ERR_INVALID_ARG),          # misaligned
+    (dict(Hq=3, Hkv=2), _lib.NB_ERR_INVALID_ARG),
+    (dict(L=17), _lib.NB_ERR_INVALID_ARG),
+    (dict(L=0), _lib.NB_ERR_INVALID_ARG),
+    (dict(scale=0.0), _lib.NB_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _lib.NB_ERR_INVALID_ARG),
+    (dict(D=96), _lib.NB_ERR_UNSUPPORTED),
+    (dict(dtype=7), _lib.NB_ERR_UNSUPPORTED),
+    (dict(drop=0.1), _lib.NB_ERR_UNSUPPORTED),
+])
+def test_fwd_preflight(kw, status):
+    assert _fwd(**kw) == status
+
+
+def _bwd(owner_off, n_owner, att=FAKE, ws_bytes=1 << 20, **kw):
+    a = dict(B=1, Hq=2, Hkv=1, L=8, S=16, D=64)
+    a.update(kw)
+    off = None if owner_off is None else (ctypes.c_int32 * len(owner_off))(*owner_off)
+    return _lib.load().nb_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, a["B"], a["Hq"], a["Hkv"],
+                                   a["L"], a["S"], a["D"], 0.125, -1, _lib.NB_BF16, FAKE, FAKE, FAKE,
+                                   None if off is None else ctypes.cast(off, ctypes.c_void_p), n_owner, att,
+                                   FAKE, ws_bytes, None)
+
+
+def test_bwd_preflight():
+    E = _lib.NB_ERR_INVALID_ARG
+    assert _bwd([0, 16], 1, ws_bytes=8) == _lib.NB_ERR_WORKSPACE
+    assert _bwd([0, 8, 15], 2) == E           # does not end at S
+    assert _bwd([1, 8, 16], 2) == E           # does not start at 0
+    assert _bwd([0, 9, 8, 16], 3) == E        # not ascending
+    assert _bwd([0, 16], 1, att=None) == E    # no flag output
+    assert _bwd(None, 65) == E                # too many owners
+    assert _bwd([0, 16], 1, D=80) == _lib.NB_ERR_UNSUPPORTED
+
+
+def test_segment_build_preflight():
+    lib = _lib.load()
+    need = lib.nb_segment_buffer_elems(1, 8, 16)
+    assert lib.nb_segment_build(FAKE, None, 1, 16, 8, -1, FAKE, FAKE, need - 1, None) == _lib.NB_ERR_WORKSPACE
+    assert lib.nb_segment_build(None, None, 1, 16, 8, -1, FAKE, FAKE, need, None) == _lib.NB_ERR_INVALID_ARG
+    assert lib.nb_segment_build(FAKE, None, 1, 16, 20, -1, FAKE, FAKE, need, None) == _lib.NB_ERR_INVALID_ARG
+
+
+def test_workload_generators_deterministic_and_shaped():
+    for c in range(1, 6):
+        w = wl.get(c)
+        a, b = wl.make_doc_map(w), wl.make_doc_map(w)
+        assert np.array_equal(a.doc_ids, b.doc_ids)
+        assert a.doc_ids.shape == (w.B, a.S) and a.doc_ids.dtype == np.int32
+        assert a.owner_off[0] == 0 and a.owner_off[-1] == a.S
+        if w.mode != "halo":
+            assert a.S == w.q_start + w.L
+        else:
+            assert w.L <= a.S <= 2 * w.L
+        if w.pad_tail:
+            assert a.pad_mask[:, -w.pad_tail:].all() and not a.pad_mask[:, :a.S - w.pad_tail].any()
+    w = wl.get(1)
+    q1 = wl.make_tensors(w, 256)
+    q2 = wl.make_tensors(w, 256)
+    assert all((x == y).all() for x, y in zip(q1, q2))
+    assert q1[0].shape == (1, 2, 128, 64) and q1[1].shape == (1, 1, 256, 64)

@@ -1,0 +1,196 @@
+"""HIP path vs the fp64 oracle, every element, at sizes the oracle finishes in
+seconds (several tiles and ragged tails), plus the edge cases of the method."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import nbattn_oracle as orc
+import sliding_window_attention_fold_amd as nb
+from sliding_window_attention_fold_amd import _lib
+from sliding_window_attention_fold_amd import workloads as wl
+
+from gpu_cases import assert_close, custom_inputs, full_parity, run_gpu, say, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+# Scaled-down versions of the five workloads (same document laws, heads ratio, head dim, window role).
+SMALL = {
+    "w1": wl.get(1),
+    "w2s": wl.Workload(2, "small ring", B=1, Hq=4, Hkv=2, D=256, L=320, S_global=1280, q_start=960,
+                       window=100, doc_len=("geometric", 1 / 160, 8, 1280), pad_tail=0, mode="ring",
+                       cp_rank=3, cp_size=4),
+    "w2s_d64": wl.Workload(2, "small d64", B=1, Hq=4, Hkv=2, D=64, L=320, S_global=1280, q_start=960,
+                           window=100, doc_len=("geometric", 1 / 160, 8, 1280), pad_tail=0, mode="ring",
+                           cp_rank=3, cp_size=4),
+    "w3s": wl.Workload(3, "small halo", B=1, Hq=4, Hkv=1, D=128, L=300, S_global=600, q_start=300, window=-1,
+                       doc_len=("lognormal", 4.6, 1.0, 4, 300), pad_tail=0, mode="halo", cp_rank=1, cp_size=2),
+    "w4s": wl.Workload(4, "small single doc", B=1, Hq=8, Hkv=2, D=128, L=200, S_global=800, q_start=600,
+                       window=-1, doc_len=("single",), pad_tail=0, mode="needed", cp_rank=3, cp_size=4),
+    "w5s": wl.Workload(5, "small batched pad", B=3, Hq=4, Hkv=2, D=128, L=192, S_global=384, q_start=192,
+                       window=40, doc_len=("uniform", 3, 40), pad_tail=57, mode="ring", cp_rank=1, cp_size=2,
+                       outliers=True, per_row_docs=True),
+}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_workloads(name, dtype):
+    w = SMALL[name]
+    say(f"[parity] {name} {dtype} B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} L={w.L} W={w.window}")
+    full_parity(workload_inputs(w, dtype), dtype)
+
+
+def _docs(rng, S, lo, hi):
+    ids = np.zeros(S, dtype=np.int32)
+    pos, d = 0, 1
+    while pos < S:
+        n = int(rng.integers(lo, hi + 1))
+        ids[pos:pos + n] = d
+        pos, d = pos + n, d + 1
+    return ids
+
+
+EDGE = {
+    # L = S: empty halo, one document, no window (plain causal attention)
+    "empty_halo": lambda: dict(ids=np.ones((1, 200)), L=200, W=-1),
+    # documents of length 1: every row attends only itself
+    "len1_docs": lambda: dict(ids=np.arange(1, 151)[None], L=100, W=-1),
+    "window0": lambda: dict(ids=_docs(np.random.default_rng(1), 260, 5, 70)[None], L=130, W=0),
+    "window_ge_S": lambda: dict(ids=_docs(np.random.default_rng(2), 260, 5, 70)[None], L=130, W=1000),
+    "L1": lambda: dict(ids=_docs(np.random.default_rng(3), 97, 5, 40)[None], L=1, W=-1),
+    "tile_edges": lambda: dict(ids=np.repeat(np.arange(1, 9), [64, 128, 64, 64, 32, 128, 64, 64])[None], L=256,
+                               W=-1),
+    "mid_pad_and_negative": lambda: dict(
+        ids=np.concatenate([np.full(70, 1), np.full(30, 2), np.zeros(25), np.full(40, 3), np.full(10, -4),
+                            np.full(45, 5)])[None], L=150, W=50),
+}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_cases(name, dtype):
+    e = EDGE[name]()
+    ids = np.asarray(e["ids"], dtype=np.int32)
+    say(f"[edge] {name} {dtype} S={ids.shape[1]} L={e['L']} W={e['W']}")
+    full_parity(custom_inputs(ids, None, 4, 2, 64, e["L"], e["W"], dtype, seed=11), dtype)
+
+
+@pytest.mark.parametrize("hkv", [8, 2, 1])
+def test_gqa_groups(hkv):
+    rng = np.random.default_rng(5)
+    ids = _docs(rng, 300, 10, 120)[None]
+    say(f"[gqa] Hq=8 Hkv={hkv}")
+    full_parity(custom_inputs(ids, None, 8, hkv, 128, 170, 60, "bf16", seed=12), "bf16")
+
+
+def test_all_pad_batch_row_and_pad_mask():
+    rng = np.random.default_rng(6)
+    ids = np.stack([_docs(rng, 200, 10, 60), _docs(rng, 200, 10, 60)])
+    pad = np.zeros_like(ids, dtype=np.uint8)
+    pad[1, :] = 1           # the whole second row is padding
+    pad[0, 180:] = 1        # pad tail on the first row
+    say("[edge] all-pad batch row")
+    inp = custom_inputs(ids, pad, 4, 2, 128, 120, 30, "bf16", seed=13, owner_off=[0, 80, 200])
+    full_parity(inp, "bf16")
+    seg, out, lse, res = run_gpu(inp)
+    assert (out[1].float() == 0).all() and torch.isneginf(lse[1]).all()
+    assert (res.dq[1].float() == 0).all() and (res.dk[1].float() == 0).all() and (res.dv[1].float() == 0).all()
+
+
+def test_nothing_attended_anywhere():
+    """n_seg = 0: every row is padding; all outputs zero, LSE -inf, no owner attended."""
+    ids = np.ones((1, 128), dtype=np.int32)
+    pad = np.ones((1, 128), dtype=np.uint8)
+    say("[edge] empty shard")
+    inp = custom_inputs(ids, pad, 2, 1, 64, 64, -1, "bf16", seed=14, owner_off=[0, 64, 128])
+    seg, out, lse, res = run_gpu(inp)
+    assert seg.header_host()["n_seg"] == 0
+    assert (out.float() == 0).all() and torch.isneginf(lse).all()
+    assert (res.dq.float() == 0).all() and (res.dk.float() == 0).all() and (res.dv.float() == 0).all()
+    assert not any(res.attended.values())
+
+
+def test_split_document_sets_status():
+    """An id in two separate runs of one row violates the per-document contract: status bit 0."""
+    ids = np.array([[3, 3, 0, 3, 3, 1, 1, 0]], dtype=np.int32)
+    say("[builder] split document status")
+    seg = nb.segment_build(torch.from_numpy(ids).cuda(), 4, -1)
+    h = seg.header_host()
+    ref = orc.segments_reference(ids, 4, -1)
+    assert h["status"] == 1 == ref["status"]
+    assert h["n_seg"] == ref["n_seg"]
+    assert seg.cu_q.cpu().numpy()[:3].tolist() == ref["cu_q"].tolist()
+
+
+def test_builder_random_maps():
+    rng = np.random.default_rng(7)
+    for trial in range(12):
+        B = int(rng.integers(1, 4))
+        S = int(rng.integers(1, 20000))
+        L = int(rng.integers(1, S + 1))
+        W = int(rng.choice([-1, 0, 3, 100, 5000]))
+        hi = int(rng.choice([1, 4, 50, 3000]))
+        ids = np.stack([_docs(rng, S, 1, hi) for _ in range(B)])
+        pad = (rng.random((B, S)) < 0.02).astype(np.uint8) if trial % 3 == 0 else None
+        say(f"[builder] trial {trial} B={B} S={S} L={L} W={W}")
+        seg = nb.segment_build(torch.from_numpy(ids).cuda(), L, W,
+                               None if pad is None else torch.from_numpy(pad).cuda())
+        folded = orc.fold_pad(ids, pad)
+        ref = orc.segments_reference(folded, L, W)
+        h = seg.header_host()
+        n = ref["n_seg"]
+        assert (h["n_seg"], h["max_q"], h["max_k"], h["status"]) == (n, ref["max_q"], ref["max_k"], ref["status"])
+        assert np.array_equal(seg.folded.cpu().numpy(), folded)
+        for key, m in (("cu_q", n + 1), ("cu_k", n + 1), ("q_row0", n), ("k_row0", n)):
+            assert np.array_equal(getattr(seg, key).cpu().numpy()[:m], ref[key][:m]), key
+        for key in ("row_seg", "row_klo", "kcov_lo"):
+            assert np.array_equal(getattr(seg, key).cpu().numpy(), ref[key]), key
+
+
+def test_deterministic_bitwise():
+    w = SMALL["w5s"]
+    inp = workload_inputs(w, "bf16")
+    say("[determinism] w5s twice")
+    a = run_gpu(inp)
+    b = run_gpu(inp)
+    for x, y in ((a[1], b[1]), (a[2], b[2]), (a[3].dq, b[3].dq), (a[3].dk, b[3].dk), (a[3].dv, b[3].dv)):
+        assert torch.equal(x, y)
+
+
+def test_autograd_function_matches_direct_calls():
+    w = SMALL["w2s"]
+    inp = workload_inputs(w, "bf16")
+    say("[autograd] w2s")
+    dev = torch.device("cuda:0")
+    seg = nb.segment_build(torch.from_numpy(inp.ids).to(dev), inp.L, inp.window)
+    q, k, v, do = (t.to(dev).clone().requires_grad_(True) for t in (inp.q, inp.k, inp.v, inp.do))
+    out = nb.neighbourhood_attention(q, k, v, seg)
+    out.backward(do.detach())
+    ref_out, saved = nb.attn_fwd(q.detach(), k.detach(), v.detach(), seg)
+    r = nb.attn_bwd(saved, do.detach())
+    assert torch.equal(out.detach(), ref_out)
+    assert torch.equal(q.grad, r.dq) and torch.equal(k.grad, r.dk) and torch.equal(v.grad, r.dv)
+
+
+def test_dropout_rejected_before_launch():
+    inp = workload_inputs(SMALL["w1"], "bf16")
+    dev = torch.device("cuda:0")
+    seg = nb.segment_build(torch.from_numpy(inp.ids).to(dev), inp.L, inp.window)
+    with pytest.raises(_lib.NbError) as ei:
+        nb.attn_fwd(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), seg, dropout_p=0.1)
+    assert ei.value.status == _lib.NB_ERR_UNSUPPORTED
+
+
+def test_owner_dict_wrapped_owners_are_zero():
+    """_owner_grad_dict: rank 1 of 4 with n_prior = 3 also returns the wrapped owners 3 and 2, as zeros."""
+    rng = np.random.default_rng(8)
+    ids = _docs(rng, 256, 20, 90)[None]
+    inp = custom_inputs(ids, None, 2, 1, 64, 128, 64, "bf16", seed=15, owner_off=[0, 128, 256])
+    dev = torch.device("cuda:0")
+    seg = nb.segment_build(torch.from_numpy(inp.ids).to(dev), inp.L, inp.window)
+    _, saved = nb.attn_fwd(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), seg)
+    r = nb.attn_bwd(saved, inp.do.to(dev), nb.OwnerTable([0, 128, 256], [0, 1], cp_rank=1, cp_size=4, n_prior=3))
+    assert sorted(r.dk_by_owner) == [0, 1, 2, 3]
+    for o in (2, 3):
+        assert r.dk_by_owner[o].shape == (1, 1, 128, 64) and (r.dk_by_owner[o].float() == 0).all()
+        assert not r.attended[o]

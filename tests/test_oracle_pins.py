@@ -473,3 +473,22 @@ def test_owner_split_zeros_and_sum():
     assert np.array_equal(np.concatenate(dk_l, axis=2), dK)
     # keys outside the attended set are exact zeros
     assert (dK[:, :, ~att[0]] == 0).all() and (dV[:, :, ~att[0]] == 0).all()
+
+
+def test_backward_row_and_key_restriction():
+    """Restricting the sums to the rows that attend a key set gives the full result at those keys."""
+    rng = np.random.default_rng(13)
+    B, Hq, Hkv, S, L, D = 1, 2, 1, 30, 20, 4
+    f = _rand_docmap(rng, B, S, pad_tail=2, lo=2, hi=8)
+    q, k, v = _rand_qkv(rng, B, Hq, Hkv, L, S, D)
+    dout = rng.standard_normal((B, Hq, L, D))
+    dQ, dK, dV = orc.attention_backward(q, k, v, dout, f, 3, 0.5)
+    keys = np.array([12, 20, 27])
+    M = orc.allow_mask(f, L, 3)[0, 0] & orc.real_rows(f, L)[0][:, None]
+    rows = np.nonzero(M[:, keys].any(axis=1))[0]
+    dQ2, dK2, dV2 = orc.attention_backward(q, k, v, dout, f, 3, 0.5, rows=rows, keys=keys, row_block=2)
+    assert np.allclose(dK2[:, :, keys], dK[:, :, keys], atol=1e-14)
+    assert np.allclose(dV2[:, :, keys], dV[:, :, keys], atol=1e-14)
+    assert np.allclose(dQ2[:, :, rows], dQ[:, :, rows], atol=1e-14)
+    other = np.setdiff1d(np.arange(S), keys)
+    assert (dK2[:, :, other] == 0).all()
