@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Throughput of one context-parallel rank's neighbourhood attention on one MI355X.
+
+One step is the whole hot path over one batch of synthetic input: pad fold +
+segment build, forward (O, LSE), backward (dQ pass with Delta, dK/dV pass with
+the GQA reduction) and the per-owner attended flags -- all on the device, no
+host synchronisation inside the step.  Inputs are resident in HBM before the
+timed region starts.
+
+Default workload: the Gemma-style sliding layer at rank 3 of a 4-way ring
+(B=1, Hq=16, Hkv=8, D=256, L=4096, S=16384, window 1024, geometric doc lengths
+with mean 2048), bf16.  The metric is useful fwd+bwd TFLOP/s with
+useful FLOPs = 14 * D * Hq * pairs (4D forward + 10D backward per allowed
+(query, key) pair per q head), pairs counted exactly from the seeded doc map.
+
+Prints ONE JSON line.  Only the `cpu_baseline` leg touches the fp64 oracle.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "fwd+bwd useful TFLOP/s per shard; % of bf16 MFMA peak (MI355X)"
+
+# kernel -> (symbol substring in rocprof, source file, algorithmic FLOPs per allowed pair per q head / D)
+KERNELS = {
+    "attn_fwd": ("attn_fwd_kernel", "attn_fwd.hip", 4),     # S = QK^T, O = PV
+    "bwd_dq": ("bwd_dq_kernel", "attn_bwd.hip", 2),         # dQ = dS K (S, dP recomputed, not counted)
+    "bwd_dkdv": ("bwd_dkdv_kernel", "attn_bwd.hip", 8),     # S, dP, dV = P^T dO, dK = dS^T Q
+}
+
+
+def kernel_source_hash(fname: str) -> str:
+    csrc = os.path.join(ROOT, "sliding_window_attention_fold_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (fname, "nb_device.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it matches the current source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != kernel_source_hash(KERNELS[kernel][1]):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, dm, tensors, rows: int):
+    """The fp64 oracle (as it stands) on a bounded sample: one kv-head group, the first `rows` query rows."""
+    import numpy as np
+    from oracle import nbattn_oracle as orc
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = sum(int(p.get("num_threads", 1)) for p in threadpool_info() if p.get("user_api") == "blas") or 1
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    q, k, v, do = tensors
+    folded = orc.fold_pad(dm.doc_ids, dm.pad_mask)
+    sel = np.arange(min(rows, w.L))
+    heads = list(range(w.g))                    # q heads of kv head 0
+    t0 = time.perf_counter()
+    orc.attention_forward(q[:, :w.g], k[:, :1], v[:, :1], folded, w.window, w.D ** -0.5, rows=sel)
+    orc.attention_backward(q[:, :w.g], k[:, :1], v[:, :1], do[:, :w.g], folded, w.window, w.D ** -0.5,
+                           rows=sel)
+    dt = time.perf_counter() - t0
+    M = orc.allow_mask(folded, w.L, w.window, rows=sel)[:, 0] & orc.real_rows(folded, w.L)[:, sel][:, :, None]
+    pairs = int(M.sum())
+    flops = 14.0 * w.D * len(heads) * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 numpy oracle fwd+bwd, kv head 0 ({len(heads)} q heads), query rows "
+                      f"[0,{len(sel)}) of {w.L}, all {dm.S} keys; {pairs} allowed pairs; {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="query rows of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU "
+              "path: each context-parallel rank's local attention is one GPU's work", file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only (WORLD_SIZE > 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from sliding_window_attention_fold_amd import _lib
+    from sliding_window_attention_fold_amd import workloads as wl
+
+    lib = _lib.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = wl.get(args.config)
+    dm = wl.make_doc_map(w)
+    q, k, v, do = wl.make_tensors(w, dm.S, "bf16")
+    B, Hq, Hkv, L, S, D, W = w.B, w.Hq, w.Hkv, w.L, dm.S, w.D, w.window
+    scale = D ** -0.5
+
+    ids_d = torch.from_numpy(dm.doc_ids).to(dev)
+    pad_d = None if dm.pad_mask is None else torch.from_numpy(dm.pad_mask).to(dev)
+    qd, kd, vd, dod = (t.to(dev).contiguous() for t in (q, k, v, do))
+    folded = torch.empty((B, S), dtype=torch.int32, device=dev)
+    nseg = lib.nb_segment_buffer_elems(B, L, S)
+    segbuf = torch.empty((nseg,), dtype=torch.int32, device=dev)
+    out = torch.empty_like(qd)
+    resid = torch.empty_like(qd)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+    dq = torch.empty_like(qd)
+    dk = torch.empty_like(kd)
+    dv = torch.empty_like(vd)
+    ws_bytes = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, _lib.NB_BF16)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    n_owner = len(dm.owner_off) - 1
+    attended = torch.empty((n_owner,), dtype=torch.uint8, device=dev)
+    off_c = (ctypes.c_int32 * len(dm.owner_off))(*dm.owner_off)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    bf = _lib.NB_BF16
+
+    calls = {
+        "segment_build": lambda: lib.nb_segment_build(P(ids_d), P(pad_d), B, S, L, W, P(folded), P(segbuf), nseg,
+                                                      sp),
+        "attn_fwd": lambda: lib.nb_attn_fwd(P(qd), P(kd), P(vd), P(out), P(resid), P(lse), P(segbuf), B, Hq, Hkv, L,
+                                            S, D, scale, W, 0.0, bf, None, 0, sp),
+        "bwd_dq": lambda: lib.nb_attn_bwd_dq(P(dod), P(qd), P(kd), P(vd), P(out), P(resid), P(lse), P(segbuf), B,
+                                             Hq, Hkv, L, S, D, scale, W, bf, P(dq), P(ws), ws_bytes, sp),
+        "bwd_dkdv": lambda: lib.nb_attn_bwd_dkdv(P(dod), P(qd), P(kd), P(vd), P(lse), P(segbuf), B, Hq, Hkv, L, S,
+                                                 D, scale, W, bf, P(dk), P(dv), P(ws), ws_bytes, sp),
+        "owner_flags": lambda: lib.nb_owner_attended(P(segbuf), P(folded), B, L, S, ctypes.cast(off_c,
+                                                     ctypes.c_void_p), n_owner, P(attended), sp),
+    }
+    names = list(calls)
+
+    def step(events=None):
+        for i, n in enumerate(names):
+            if events is not None:
+                events[i].record(stream)
+            st = calls[n]()
+            if st != 0:
+                raise _lib.NbError(st, n)
+        if events is not None:
+            events[len(names)].record(stream)
+
+    # exact useful pairs from the device segment buffer (accounting, outside the timed region)
+    step()
+    torch.cuda.synchronize()
+    off_klo = lib.nb_segment_offset_row_klo(B, L)
+    klo = segbuf[off_klo:off_klo + B * L].view(B, L).long()
+    pos = (S - L + torch.arange(L, device=dev)).view(1, L)
+    band_lo = klo if W < 0 else torch.maximum(klo, pos - W)
+    pairs = int(torch.clamp(pos - band_lo + 1, min=0).sum().item())
+    useful = 14.0 * D * Hq * pairs
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.steps):
+        step(evs[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    per = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+           for i, n in enumerate(names)}
+
+    if args.copy_mib > 0:
+        a = torch.empty((args.copy_mib << 20,), dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    tflops = useful / (ms_step * 1e-3) / 1e12
+    dom = max(("attn_fwd", "bwd_dq", "bwd_dkdv"), key=lambda n: per[n])
+    dom_flops = KERNELS[dom][2] * D * Hq * pairs
+    achieved = dom_flops / (per[dom] * 1e-3) / 1e12
+    traffic = read_traffic(dom, f"config{args.config}")
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"config{args.config}: {w.name}", "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "L": L, "S": S,
+            "window": W, "doc_lengths": list(w.doc_len), "pad_tail": w.pad_tail, "seed": w.seed,
+            "pairs_per_head": pairs, "useful_flop_per_step": useful,
+        },
+        "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "ms_per_kernel": {n: round(per[n], 5) for n in names},
+        "fwd_bwd_ms": round(per["attn_fwd"] + per["bwd_dq"] + per["bwd_dkdv"], 5),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "kernel": dom, "bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+            "algorithmic_flop_per_launch": dom_flops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, dm, (q, k, v, do), args.cpu_rows)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

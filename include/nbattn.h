@@ -176,6 +176,27 @@ int nb_attn_bwd(const void* dout, const void* q, const void* k, const void* v, c
                 void* dq, void* dk, void* dv, const int32_t* owner_off, int n_owner,
                 uint8_t* owner_attended, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * The passes nb_attn_bwd runs, for callers that schedule them separately (for
+ * instance to hand dK/dV to the owner exchange while other work runs) and for
+ * per-kernel timing.  Same arguments and conventions as nb_attn_bwd.
+ *   nb_attn_bwd_dq:   Delta = dO . (o + o_resid) into ws, then dq.
+ *   nb_attn_bwd_dkdv: dk, dv; needs the Delta an earlier nb_attn_bwd_dq call on
+ *                     the same stream left in the same ws.
+ *   nb_owner_attended: owner_attended[o] = 1 iff some real query attended a key
+ *                     of chunk o (cp_local_ring page, _owner_grad_dict).
+ */
+int nb_attn_bwd_dq(const void* dout, const void* q, const void* k, const void* v, const void* o,
+                   const void* o_resid, const float* lse, const int32_t* seg_buf, int B, int Hq,
+                   int Hkv, int L, int S, int D, float scale, int window_left, int dtype, void* dq,
+                   void* ws, size_t ws_bytes, void* stream);
+int nb_attn_bwd_dkdv(const void* dout, const void* q, const void* k, const void* v,
+                     const float* lse, const int32_t* seg_buf, int B, int Hq, int Hkv, int L, int S,
+                     int D, float scale, int window_left, int dtype, void* dk, void* dv,
+                     const void* ws, size_t ws_bytes, void* stream);
+int nb_owner_attended(const int32_t* seg_buf, const int32_t* folded_ids, int B, int L, int S,
+                      const int32_t* owner_off, int n_owner, uint8_t* owner_attended, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

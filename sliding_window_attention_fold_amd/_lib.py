@@ -36,6 +36,9 @@ SIGNATURES = {
     "nb_attn_bwd_workspace_bytes": (_Z, [_I] * 7),
     "nb_attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I,
                          _P, _P, _P, _P, _I, _P, _P, _Z, _P]),
+    "nb_attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _Z, _P]),
+    "nb_attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _Z, _P]),
+    "nb_owner_attended": (_I, [_P, _P, _I, _I, _I, _P, _I, _P, _P]),
 }
 
 _LIB = None

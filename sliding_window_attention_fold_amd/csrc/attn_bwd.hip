@@ -10,14 +10,16 @@
 // Two passes keep every output owned by exactly one workgroup (no atomics, the
 // result is bitwise reproducible):
 //   1. dQ:     one workgroup per (128 query rows, q head, batch row); Q and dO in
-//      registers, K/V staged row-major and K transposed per key tile.  Its
-//      prologue forms Delta = dO . O (O = stored value + saved rounding residual)
-//      and publishes it for pass 2;
+//      registers, K/V tiles copied into LDS asynchronously (double-buffered);
+//      K^T is read transposed from the same row-major tile.  Its prologue
+//      forms Delta = dO . O (O = stored value + saved rounding residual) and
+//      publishes it for pass 2;
 //   2. dK/dV:  one workgroup per (128 keys, kv head, batch row), four waves of
 //      32 keys; K and V stay in registers, the loop runs over the group's q
-//      heads and the 32-row query tiles whose bands reach the keys, with Q and dO
-//      staged in LDS both row-major (A operands of S and dP) and transposed (A
-//      operands of dV^T and dK^T).  Keys no query attends come out as exact 0.
+//      heads and the 32-row query tiles whose bands reach the keys.  Q and dO
+//      tiles (plus their rows' LSE, Delta, band start) are copied into LDS
+//      asynchronously and read row-wise (A operands of S and dP) and transposed
+//      (A operands of dV^T and dK^T).  Keys no query attends come out as exact 0.
 #include <math.h>
 
 #include "nb_device.h"
@@ -31,22 +33,22 @@ template <typename T, int D>
 struct DkvCfg {
   static constexpr int NW = 4;
   static constexpr int NT = 64 * NW;
-  static constexpr int BK = 32 * NW;               // keys per workgroup
-  static constexpr int BQ = 32;                    // query rows per step
-  static constexpr int RP = D + Pad<T>::elems;      // row-major pitch
-  static constexpr int TP = BQ + Pad<T>::elems;     // transposed pitch
+  static constexpr int BK = 32 * NW;   // keys per workgroup
+  static constexpr int BQ = 32;        // query rows per step
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   typedef DkvCfg<T, D> C;
+  typedef Tile<T, C::BQ, D> TL;
   typedef typename Frag<T>::type F;
-  __shared__ __attribute__((aligned(16))) T Qs[C::BQ * C::RP];
-  __shared__ __attribute__((aligned(16))) T dOs[C::BQ * C::RP];
-  __shared__ __attribute__((aligned(16))) T Qt[D * C::TP];
-  __shared__ __attribute__((aligned(16))) T dOt[D * C::TP];
-  __shared__ float lse_s[C::BQ], delta_s[C::BQ];
-  __shared__ int bs_s[C::BQ];
+  // two (Q, dO, row metadata) buffers: one is filled by DMA while the other is read
+  __shared__ __attribute__((aligned(1024))) T Q0[TL::ELEMS];
+  __shared__ __attribute__((aligned(1024))) T G0[TL::ELEMS];
+  __shared__ __attribute__((aligned(1024))) T Q1[TL::ELEMS];
+  __shared__ __attribute__((aligned(1024))) T G1[TL::ELEMS];
+  __shared__ __attribute__((aligned(256))) float lse0[64], lse1[64], dl0[64], dl1[64];
+  __shared__ __attribute__((aligned(256))) int klo0[64], klo1[64];
   __shared__ int n_tiles_s;
 
   const int kt = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -81,96 +83,102 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     __syncthreads();
   }
   __syncthreads();
-  const int t_end = t_first + n_tiles_s;
+  const int n_t = n_tiles_s;
+  const int n_iter = grp * n_t;      // (q head of the group, query tile) steps
 
-  const T* __restrict__ kp = reinterpret_cast<const T*>(p.k) + (((size_t)b * p.Hkv + kvh) * p.S + j) * D;
-  const T* __restrict__ vp = reinterpret_cast<const T*>(p.v) + (((size_t)b * p.Hkv + kvh) * p.S + j) * D;
-  const bool key_ok = j < p.S;
+  const T* kvq = reinterpret_cast<const T*>(p.q);
+  const T* kvd = reinterpret_cast<const T*>(p.dout);
+  auto load = [&](T* Qs, T* Gs, float* ls, float* ds, int* ks, int it) {
+    const int hh = it / n_t, t = t_first + it % n_t;
+    const int i0 = t * C::BQ;
+    const int nr = min(C::BQ, p.L - i0);
+    const size_t rb = ((size_t)b * p.Hq + kvh * grp + hh) * p.L + i0;
+    dma_tile<T, C::BQ, D, C::NW>(Qs, kvq + rb * D, nr);
+    dma_tile<T, C::BQ, D, C::NW>(Gs, kvd + rb * D, nr);
+    if (w == 0) dma_words(ls, p.lse + rb, nr);
+    if (w == 1) dma_words(ds, p.delta + rb, nr);
+    if (w == 2) dma_words(ks, p.row_klo + (size_t)b * p.L + i0, nr);
+  };
+  if (n_iter > 0) load(Q0, G0, lse0, dl0, klo0, 0);
+
+  // this lane's key row of K and V: the B operands of S = Q K^T and dP = dO V^T
   F kf[D / 16], vf[D / 16];
+  {
+    const size_t kr = ((size_t)b * p.Hkv + kvh) * p.S + min(j, p.S - 1);
+    const T* kp = reinterpret_cast<const T*>(p.k) + kr * D;
+    const T* vp = reinterpret_cast<const T*>(p.v) + kr * D;
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    kf[kk] = key_ok ? load_frag<T>(kp + 16 * kk + 8 * g) : zero_frag<T>();
-    vf[kk] = key_ok ? load_frag<T>(vp + 16 * kk + 8 * g) : zero_frag<T>();
+    for (int kk = 0; kk < D / 16; ++kk) {
+      kf[kk] = load_frag<T>(kp + 16 * kk + 8 * g);
+      vf[kk] = load_frag<T>(vp + 16 * kk + 8 * g);
+    }
   }
+  const TileAccess<T, TL> acc(ln, lane);
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
   for (int d = 0; d < D / 32; ++d) { dkacc[d] = f32x16{}; dvacc[d] = f32x16{}; }
 
-  for (int hh = 0; hh < grp; ++hh) {
-    const int h = kvh * grp + hh;
-    const size_t rowbase = ((size_t)b * p.Hq + h) * p.L;
-    for (int t = t_first; t < t_end; ++t) {
-      const int i0 = t * C::BQ;
-      const int nrows = min(C::BQ, p.L - i0);
-      __syncthreads();
-      const T* qsrc = reinterpret_cast<const T*>(p.q) + (rowbase + i0) * D;
-      const T* dsrc = reinterpret_cast<const T*>(p.dout) + (rowbase + i0) * D;
-      stage_rows<T, C::BQ, D, C::RP, C::NT>(Qs, qsrc, nrows);
-      stage_rows<T, C::BQ, D, C::RP, C::NT>(dOs, dsrc, nrows);
-      stage_rows_transposed<T, C::BQ, D, C::TP, C::NT>(Qt, qsrc, nrows);
-      stage_rows_transposed<T, C::BQ, D, C::TP, C::NT>(dOt, dsrc, nrows);
-      if (tid < C::BQ) {
-        const int i = i0 + tid;
-        int bsi = off + i + 1;  // empty band
-        float lse2 = 0.f, dl = 0.f;
-        if (i < p.L) {
-          const int pos = off + i;
-          bsi = max(0, p.row_klo[(size_t)b * p.L + i]);
-          if (p.window >= 0) bsi = max(bsi, pos - p.window);
-          if (bsi <= pos) {
-            lse2 = p.lse[rowbase + i] * kLog2e;
-            dl = p.delta[rowbase + i];
-          }
-        }
-        bs_s[tid] = bsi;
-        lse_s[tid] = lse2;
-        delta_s[tid] = dl;
-      }
-      __syncthreads();
+  auto compute = [&](const T* Qs, const T* Gs, const float* ls, const float* ds, const int* ks, int it) {
+    const int t = t_first + it % n_t;
+    const int i0 = t * C::BQ;
+    const int nrows = min(C::BQ, p.L - i0);
+    // rows of this tile: positions off+i0 .. off+i0+nrows-1; band starts are nondecreasing
+    const int p_min = off + i0, p_max = off + i0 + nrows - 1;
+    auto band = [&](int qi) {
+      const int bq = max(0, ks[qi]);
+      return p.window >= 0 ? max(bq, off + i0 + qi - p.window) : bq;
+    };
+    const int bs_min = band(0), bs_max = band(nrows - 1);
+    if (jw > p_max || jw + 31 < bs_min) return;
+    // every (row, key) pair of the wave inside the band: no element mask
+    const bool full = (nrows == C::BQ) && jw >= bs_max && jw + 31 <= p_min;
 
-      // rows of this tile: positions off+i0 .. off+i0+nrows-1
-      const int p_min = off + i0, p_max = off + i0 + nrows - 1;
-      const int bs_min = bs_s[0], bs_max = bs_s[nrows - 1];
-      if (jw > p_max || jw + 31 < bs_min) continue;
-      // every (row, key) pair of the wave inside the band: no element mask
-      const bool full = (nrows == C::BQ) && jw >= bs_max && jw + 31 <= p_min;
-
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const F a = load_frag<T>(Qs + ln * C::RP + 16 * kk + 8 * g);
-        sacc = mma(a, kf[kk], sacc);
-        const F c = load_frag<T>(dOs + ln * C::RP + 16 * kk + 8 * g);
-        dpacc = mma(c, vf[kk], dpacc);
+    for (int kk = 0; kk < D / 16; ++kk) {
+      sacc = mma(acc.row(Qs, 0, kk), kf[kk], sacc);
+      dpacc = mma(acc.row(Gs, 0, kk), vf[kk], dpacc);
+    }
+    if constexpr (sizeof(T) == 2) interleave_lds_mfma<D / 8, 1>();
+    // accumulator r: query row acc_row(r, g) of the tile, key j
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qi = acc_row(r, g);
+      float pr = fast_exp2(sacc[r] * p.scale_log2 - ls[qi] * kLog2e);
+      if (!full) {
+        if (qi >= nrows || j < band(qi) || j > off + i0 + qi) pr = 0.f;
       }
-      // accumulator r: query row acc_row(r, g) of the tile, key j
+      sacc[r] = pr;
+      dpacc[r] = pr * (dpacc[r] - ds[qi]);
+    }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = acc_row(r, g);
-        const int pos = off + i0 + qi;
-        float pr = exp2f(sacc[r] * p.scale_log2 - lse_s[qi]);
-        if (!full) {
-          if (qi >= nrows || j < bs_s[qi] || j > pos) pr = 0.f;
-        }
-        sacc[r] = pr;
-        dpacc[r] = pr * (dpacc[r] - delta_s[qi]);
-      }
+    for (int m = 0; m < 2; ++m) {
+      const F pf = acc_to_frag<T>(sacc, m);
+      const F sf = acc_to_frag<T>(dpacc, m);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const F pf = acc_to_frag<T>(sacc, m);
-        const F sf = acc_to_frag<T>(dpacc, m);
-#pragma unroll
-        for (int d = 0; d < D / 32; ++d) {
-          const F a = load_frag<T>(dOt + (32 * d + ln) * C::TP + 16 * m + 8 * g);
-          dvacc[d] = mma(a, pf, dvacc[d]);
-          const F c = load_frag<T>(Qt + (32 * d + ln) * C::TP + 16 * m + 8 * g);
-          dkacc[d] = mma(c, sf, dkacc[d]);
-        }
+      for (int d = 0; d < D / 32; ++d) {
+        dvacc[d] = mma(acc.col(Gs, d, m), pf, dvacc[d]);
+        dkacc[d] = mma(acc.col(Qs, d, m), sf, dkacc[d]);
       }
     }
+    if constexpr (sizeof(T) == 2) interleave_lds_mfma<D / 8, 2>();
+  };
+
+  for (int it = 0; it < n_iter; it += 2) {
+    wait_global();
+    __syncthreads();
+    if (it + 1 < n_iter) load(Q1, G1, lse1, dl1, klo1, it + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(Q0, G0, lse0, dl0, klo0, it);
+    if (it + 1 >= n_iter) break;
+    wait_global();
+    __syncthreads();
+    if (it + 2 < n_iter) load(Q0, G0, lse0, dl0, klo0, it + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(Q1, G1, lse1, dl1, klo1, it + 1);
   }
 
-  if (!key_ok) return;
+  if (j >= p.S) return;
   T* dkp = reinterpret_cast<T*>(p.dk) + (((size_t)b * p.Hkv + kvh) * p.S + j) * D;
   T* dvp = reinterpret_cast<T*>(p.dv) + (((size_t)b * p.Hkv + kvh) * p.S + j) * D;
 #pragma unroll
@@ -193,18 +201,18 @@ struct DqCfg {
   static constexpr int NW = 4;
   static constexpr int NT = 64 * NW;
   static constexpr int BM = 32 * NW;
-  static constexpr int BN = (sizeof(T) == 4 && D == 256) ? 32 : 64;
-  static constexpr int RP = D + Pad<T>::elems;
-  static constexpr int TP = BN + Pad<T>::elems;
+  static constexpr int BN = (D * sizeof(T) > 512) ? 32 : 64;
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   typedef DqCfg<T, D> C;
+  typedef Tile<T, C::BN, D> TL;
   typedef typename Frag<T>::type F;
-  __shared__ __attribute__((aligned(16))) T Ks[C::BN * C::RP];
-  __shared__ __attribute__((aligned(16))) T Vs[C::BN * C::RP];
-  __shared__ __attribute__((aligned(16))) T Kt[D * C::TP];
+  __shared__ __attribute__((aligned(1024))) T K0[TL::ELEMS];
+  __shared__ __attribute__((aligned(1024))) T V0[TL::ELEMS];
+  __shared__ __attribute__((aligned(1024))) T K1[TL::ELEMS];
+  __shared__ __attribute__((aligned(1024))) T V1[TL::ELEMS];
   __shared__ int red[4][2];
 
   const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -231,55 +239,51 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int x = 0; x < C::NW; ++x) { kstart = min(kstart, red[x][0]); kend = max(kend, red[x][1]); }
 
+  const T* __restrict__ kbase = reinterpret_cast<const T*>(p.k) + ((size_t)b * p.Hkv + kvh) * p.S * D;
+  const T* __restrict__ vbase = reinterpret_cast<const T*>(p.v) + ((size_t)b * p.Hkv + kvh) * p.S * D;
+  auto load = [&](T* Ks, T* Vs, int j0) {
+    const int nv = min(C::BN, p.S - j0);
+    dma_tile<T, C::BN, D, C::NW>(Ks, kbase + (size_t)j0 * D, nv);
+    dma_tile<T, C::BN, D, C::NW>(Vs, vbase + (size_t)j0 * D, nv);
+  };
+  if (kstart < kend) load(K0, V0, kstart);
+
   const size_t qrow = ((size_t)b * p.Hq + h) * p.L + i;
+  const size_t qrow_c = ((size_t)b * p.Hq + h) * p.L + min(i, p.L - 1);  // rows past L read row L-1
   F qf[D / 16], df[D / 16];
+  float dl;
   {
-    const T* qp = reinterpret_cast<const T*>(p.q) + qrow * D;
-    const T* dp = reinterpret_cast<const T*>(p.dout) + qrow * D;
+    const T* qp = reinterpret_cast<const T*>(p.q) + qrow_c * D;
+    const T* dp = reinterpret_cast<const T*>(p.dout) + qrow_c * D;
+    const T* op = reinterpret_cast<const T*>(p.o) + qrow_c * D;
+    const T* olp = p.o_lo ? reinterpret_cast<const T*>(p.o_lo) + qrow_c * D : nullptr;
+    // Delta_i = dO_i . O_i with O the stored value plus its saved rounding
+    // residual; published for the dK/dV pass, which runs after this one.
+    float part = 0.f;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      qf[kk] = in_range ? load_frag<T>(qp + 16 * kk + 8 * g) : zero_frag<T>();
-      df[kk] = in_range ? load_frag<T>(dp + 16 * kk + 8 * g) : zero_frag<T>();
-    }
-  }
-  const float lse2 = real ? p.lse[qrow] * kLog2e : 0.f;
-  // Delta_i = dO_i . O_i with O taken as the stored value plus its saved
-  // rounding residual; published for the dK/dV pass, which runs after this one.
-  float dl = 0.f;
-  {
-    float part = 0.f;
-    if (in_range) {
-      const T* op = reinterpret_cast<const T*>(p.o) + qrow * D;
-      const T* olp = p.o_lo ? reinterpret_cast<const T*>(p.o_lo) + qrow * D : nullptr;
+      qf[kk] = load_frag<T>(qp + 16 * kk + 8 * g);
+      df[kk] = load_frag<T>(dp + 16 * kk + 8 * g);
+      const F ov = load_frag<T>(op + 16 * kk + 8 * g);
+      const F ol = olp ? load_frag<T>(olp + 16 * kk + 8 * g) : zero_frag<T>();
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const F ov = load_frag<T>(op + 16 * kk + 8 * g);
-        const F ol = olp ? load_frag<T>(olp + 16 * kk + 8 * g) : zero_frag<T>();
-#pragma unroll
-        for (int t = 0; t < 8; ++t) part += to_f32(df[kk][t]) * (to_f32(ov[t]) + to_f32(ol[t]));
-      }
+      for (int t = 0; t < 8; ++t) part += to_f32(df[kk][t]) * (to_f32(ov[t]) + to_f32(ol[t]));
+      if (!in_range) { qf[kk] = zero_frag<T>(); df[kk] = zero_frag<T>(); }
     }
     dl = part + __shfl_xor(part, 32);
     if (!real) dl = 0.f;
     if (in_range && g == 0) p.delta[qrow] = dl;
   }
-  const T* __restrict__ kbase = reinterpret_cast<const T*>(p.k) + ((size_t)b * p.Hkv + kvh) * p.S * D;
-  const T* __restrict__ vbase = reinterpret_cast<const T*>(p.v) + ((size_t)b * p.Hkv + kvh) * p.S * D;
+  const float lse2 = real ? p.lse[qrow_c] * kLog2e : 0.f;
 
+  const TileAccess<T, TL> acc(ln, lane);
   f32x16 dqacc[D / 32];
 #pragma unroll
   for (int d = 0; d < D / 32; ++d) dqacc[d] = f32x16{};
 
-  for (int j0 = kstart; j0 < kend; j0 += C::BN) {
-    const int nvalid = min(C::BN, p.S - j0);
-    __syncthreads();
-    stage_rows<T, C::BN, D, C::RP, C::NT>(Ks, kbase + (size_t)j0 * D, nvalid);
-    stage_rows<T, C::BN, D, C::RP, C::NT>(Vs, vbase + (size_t)j0 * D, nvalid);
-    stage_rows_transposed<T, C::BN, D, C::TP, C::NT>(Kt, kbase + (size_t)j0 * D, nvalid);
-    __syncthreads();
-    if (j0 >= w_hi || j0 + C::BN <= w_lo) continue;
+  auto compute = [&](const T* Ks, const T* Vs, int j0) {
+    if (j0 >= w_hi || j0 + C::BN <= w_lo) return;
     const bool full = w_all_real && j0 >= w_bs_max && j0 + C::BN - 1 <= w_p_min;
-
     f32x16 sacc[C::BN / 32], dpacc[C::BN / 32];
 #pragma unroll
     for (int sb = 0; sb < C::BN / 32; ++sb) {
@@ -287,17 +291,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       dpacc[sb] = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const F a = load_frag<T>(Ks + (32 * sb + ln) * C::RP + 16 * kk + 8 * g);
-        sacc[sb] = mma(a, qf[kk], sacc[sb]);
-        const F c = load_frag<T>(Vs + (32 * sb + ln) * C::RP + 16 * kk + 8 * g);
-        dpacc[sb] = mma(c, df[kk], dpacc[sb]);
+        sacc[sb] = mma(acc.row(Ks, sb, kk), qf[kk], sacc[sb]);
+        dpacc[sb] = mma(acc.row(Vs, sb, kk), df[kk], dpacc[sb]);
       }
     }
+    if constexpr (sizeof(T) == 2) interleave_lds_mfma<C::BN / 32 * D / 8, 1>();
 #pragma unroll
     for (int sb = 0; sb < C::BN / 32; ++sb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = exp2f(sacc[sb][r] * p.scale_log2 - lse2);
+        float pr = fast_exp2(sacc[sb][r] * p.scale_log2 - lse2);
         if (!full) {
           const int jj = j0 + 32 * sb + acc_row(r, g);
           if (!real || jj < bs || jj > pos) pr = 0.f;
@@ -309,11 +312,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     for (int m = 0; m < C::BN / 16; ++m) {
       const F sf = acc_to_frag<T>(dpacc[m >> 1], m & 1);
 #pragma unroll
-      for (int d = 0; d < D / 32; ++d) {
-        const F a = load_frag<T>(Kt + (32 * d + ln) * C::TP + 16 * m + 8 * g);
-        dqacc[d] = mma(a, sf, dqacc[d]);
-      }
+      for (int d = 0; d < D / 32; ++d) dqacc[d] = mma(acc.col(Ks, d, m), sf, dqacc[d]);
     }
+    if constexpr (sizeof(T) == 2) interleave_lds_mfma<C::BN / 16 * D / 32, 2>();
+  };
+
+  for (int j0 = kstart; j0 < kend; j0 += 2 * C::BN) {
+    wait_global();
+    __syncthreads();
+    if (j0 + C::BN < kend) load(K1, V1, j0 + C::BN);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(K0, V0, j0);
+    if (j0 + C::BN >= kend) break;
+    wait_global();
+    __syncthreads();
+    if (j0 + 2 * C::BN < kend) load(K0, V0, j0 + 2 * C::BN);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(K1, V1, j0 + C::BN);
   }
 
   if (!in_range) return;
@@ -332,34 +347,37 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------- launch
 
 template <typename T, int D>
-static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
-  {  // dQ first: it also publishes Delta for the dK/dV pass
-    typedef DqCfg<T, D> C;
-    dim3 grid((p.L + C::BM - 1) / C::BM, p.Hq, p.B);
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D>), grid, dim3(C::NT), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  {
-    typedef DkvCfg<T, D> C;
-    dim3 grid((p.S + C::BK - 1) / C::BK, p.Hkv, p.B);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), grid, dim3(C::NT), 0, s, p);
-    return hipGetLastError();
-  }
+static hipError_t launch_dq_t(const BwdParams& p, hipStream_t s) {
+  typedef DqCfg<T, D> C;
+  dim3 grid((p.L + C::BM - 1) / C::BM, p.Hq, p.B);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D>), grid, dim3(C::NT), 0, s, p);
+  return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd(const BwdParams& p, int D, bool f32, hipStream_t s) {
-  if (f32) {
-    if (D == 64) return launch_bwd_t<float, 64>(p, s);
-    if (D == 128) return launch_bwd_t<float, 128>(p, s);
-    if (D == 256) return launch_bwd_t<float, 256>(p, s);
-  } else {
-    if (D == 64) return launch_bwd_t<bf16, 64>(p, s);
-    if (D == 128) return launch_bwd_t<bf16, 128>(p, s);
-    if (D == 256) return launch_bwd_t<bf16, 256>(p, s);
-  }
-  return hipErrorInvalidValue;
+template <typename T, int D>
+static hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t s) {
+  typedef DkvCfg<T, D> C;
+  dim3 grid((p.S + C::BK - 1) / C::BK, p.Hkv, p.B);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), grid, dim3(C::NT), 0, s, p);
+  return hipGetLastError();
 }
+
+#define NB_DISPATCH(fn)                                      \
+  if (f32) {                                                 \
+    if (D == 64) return fn<float, 64>(p, s);                 \
+    if (D == 128) return fn<float, 128>(p, s);               \
+    if (D == 256) return fn<float, 256>(p, s);               \
+  } else {                                                   \
+    if (D == 64) return fn<bf16, 64>(p, s);                  \
+    if (D == 128) return fn<bf16, 128>(p, s);                \
+    if (D == 256) return fn<bf16, 256>(p, s);                \
+  }                                                          \
+  return hipErrorInvalidValue;
+
+hipError_t launch_bwd_dq(const BwdParams& p, int D, bool f32, hipStream_t s) { NB_DISPATCH(launch_dq_t) }
+hipError_t launch_bwd_dkdv(const BwdParams& p, int D, bool f32, hipStream_t s) { NB_DISPATCH(launch_dkdv_t) }
+
+#undef NB_DISPATCH
 
 // ---------------------------------------------------------------- owner flags
 

@@ -13,11 +13,12 @@
 // Work decomposition: one workgroup per (128 query rows, q head, batch row);
 // four waves of 32 rows each.  Q stays in registers as the B operand of
 // S^T = K Q^T, so every lane owns one query row: its softmax statistics are
-// lane-local up to one exchange with the lane 32 away.  K tiles are staged in
-// LDS row-major (A operand of S^T), V tiles transposed with the accumulator row
-// permutation (A operand of O^T = V^T P^T), P^T is fed from the S^T
-// accumulators directly.  Key tiles outside the union of the rows' bands are
-// never visited; tiles inside every band of a wave skip the element mask.
+// lane-local up to one exchange with the lane 32 away.  K and V tiles are
+// copied global -> LDS asynchronously (double-buffered) and stay row-major: K
+// rows are the A operand of S^T, V is read transposed (ds_read_b64_tr_b16) as
+// the A operand of O^T = V^T P^T, and P^T is fed from the S^T accumulators
+// directly.  Key tiles outside the union of the rows' bands are never visited;
+// tiles inside every band of a wave skip the element mask.
 #include <math.h>
 
 #include "nb_device.h"
@@ -30,17 +31,19 @@ struct FwdCfg {
   static constexpr int NW = 4;
   static constexpr int NT = 64 * NW;
   static constexpr int BM = 32 * NW;
-  static constexpr int BN = 64;
-  static constexpr int KP = D + Pad<T>::elems;    // K tile pitch (elements)
-  static constexpr int VP = BN + Pad<T>::elems;   // V^T tile pitch (elements)
+  static constexpr int BN = (D * sizeof(T) > 512) ? 32 : 64;  // keys per tile (4 tiles fit in LDS)
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
   typedef FwdCfg<T, D> C;
+  typedef Tile<T, C::BN, D> TL;
   typedef typename Frag<T>::type F;
-  __shared__ __attribute__((aligned(16))) T Ks[C::BN * C::KP];
-  __shared__ __attribute__((aligned(16))) T Vt[D * C::VP];
+  // two K/V tile pairs: one is being filled by DMA while the other is read
+  __shared__ __attribute__((aligned(1024))) T K0[TL::ELEMS];
+  __shared__ __attribute__((aligned(1024))) T V0[TL::ELEMS];
+  __shared__ __attribute__((aligned(1024))) T K1[TL::ELEMS];
+  __shared__ __attribute__((aligned(1024))) T V1[TL::ELEMS];
   __shared__ int red[4][2];
 
   const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -73,37 +76,44 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
   const T* __restrict__ kbase = reinterpret_cast<const T*>(p.k) + ((size_t)b * p.Hkv + kvh) * p.S * D;
   const T* __restrict__ vbase = reinterpret_cast<const T*>(p.v) + ((size_t)b * p.Hkv + kvh) * p.S * D;
 
+  auto load = [&](T* Ks, T* Vs, int j0) {
+    const int nv = min(C::BN, p.S - j0);
+    dma_tile<T, C::BN, D, C::NW>(Ks, kbase + (size_t)j0 * D, nv);
+    dma_tile<T, C::BN, D, C::NW>(Vs, vbase + (size_t)j0 * D, nv);
+  };
+  if (kstart < kend) load(K0, V0, kstart);
+
   F qf[D / 16];
   {
-    const T* qp = reinterpret_cast<const T*>(p.q) + qrow * D;
+    // rows past L read row L-1 (in bounds) and are zeroed
+    const T* qp = reinterpret_cast<const T*>(p.q) + (((size_t)b * p.Hq + h) * p.L + min(i, p.L - 1)) * D;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = in_range ? load_frag<T>(qp + 16 * kk + 8 * g) : zero_frag<T>();
+    for (int kk = 0; kk < D / 16; ++kk) {
+      qf[kk] = load_frag<T>(qp + 16 * kk + 8 * g);
+      if (!in_range) qf[kk] = zero_frag<T>();
+    }
   }
+
+  const TileAccess<T, TL> acc(ln, lane);  // K rows: this lane reads key row 32*sb + ln
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int d = 0; d < D / 32; ++d) oacc[d] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  // m_ref: exponent reference of the row (log2 units, scaled scores); l_run: the
+  // row's sum of 2^(s - m_ref) over this lane's keys (the other half is in lane^32).
+  float m_ref = -INFINITY, l_run = 0.f;
 
-  for (int j0 = kstart; j0 < kend; j0 += C::BN) {
-    const int nvalid = min(C::BN, p.S - j0);
-    __syncthreads();
-    stage_rows<T, C::BN, D, C::KP, C::NT>(Ks, kbase + (size_t)j0 * D, nvalid);
-    stage_rows_transposed<T, C::BN, D, C::VP, C::NT>(Vt, vbase + (size_t)j0 * D, nvalid);
-    __syncthreads();
-    if (j0 >= w_hi || j0 + C::BN <= w_lo) continue;
+  auto compute = [&](const T* Ks, const T* Vs, int j0) {
+    if (j0 >= w_hi || j0 + C::BN <= w_lo) return;
     const bool full = w_all_real && j0 >= w_bs_max && j0 + C::BN - 1 <= w_p_min;
-
     f32x16 sacc[C::BN / 32];
 #pragma unroll
     for (int sb = 0; sb < C::BN / 32; ++sb) {
       sacc[sb] = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const F a = load_frag<T>(Ks + (32 * sb + ln) * C::KP + 16 * kk + 8 * g);
-        sacc[sb] = mma(a, qf[kk], sacc[sb]);
-      }
+      for (int kk = 0; kk < D / 16; ++kk) sacc[sb] = mma(acc.row(Ks, sb, kk), qf[kk], sacc[sb]);
     }
+    if constexpr (sizeof(T) == 2) interleave_lds_mfma<C::BN / 32 * D / 16, 1>();
     float tmax = -INFINITY;
 #pragma unroll
     for (int sb = 0; sb < C::BN / 32; ++sb) {
@@ -119,31 +129,49 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
       }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_ref);
-    l_run *= alpha;
+    // Move the reference (and rescale O) only when some row's maximum passed it
+    // by more than kRefLag; the wave decides together so the branch is uniform.
+    if (__any(tmax > m_ref + kRefLag)) {
+      const float m_new = fmaxf(m_ref, tmax);
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int d = 0; d < D / 32; ++d) oacc[d] *= alpha;
+      for (int d = 0; d < D / 32; ++d) oacc[d] *= alpha;
+      m_ref = m_new;
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
 #pragma unroll
     for (int sb = 0; sb < C::BN / 32; ++sb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = exp2f(sacc[sb][r] - m_ref);
+        const float e = fast_exp2(sacc[sb][r] - m_use);
         sacc[sb][r] = e;
         l_run += e;
       }
     }
-    m_run = m_new;
 #pragma unroll
     for (int m = 0; m < C::BN / 16; ++m) {
       const F pf = acc_to_frag<T>(sacc[m >> 1], m & 1);
 #pragma unroll
-      for (int d = 0; d < D / 32; ++d) {
-        const F a = load_frag<T>(Vt + (32 * d + ln) * C::VP + 16 * m + 8 * g);
-        oacc[d] = mma(a, pf, oacc[d]);
-      }
+      for (int d = 0; d < D / 32; ++d) oacc[d] = mma(acc.col(Vs, d, m), pf, oacc[d]);
     }
+    if constexpr (sizeof(T) == 2) interleave_lds_mfma<C::BN / 16 * D / 32, 2>();
+  };
+
+  // Double-buffered key loop: the DMA of the next tile is issued right after
+  // the barrier that frees its buffer, then the current tile is computed.
+  for (int j0 = kstart; j0 < kend; j0 += 2 * C::BN) {
+    wait_global();
+    __syncthreads();
+    if (j0 + C::BN < kend) load(K1, V1, j0 + C::BN);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(K0, V0, j0);
+    if (j0 + C::BN >= kend) break;
+    wait_global();
+    __syncthreads();
+    if (j0 + 2 * C::BN < kend) load(K0, V0, j0 + 2 * C::BN);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(K1, V1, j0 + C::BN);
   }
 
   const float l = l_run + __shfl_xor(l_run, 32);
@@ -160,7 +188,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
                           oacc[d][4 * rq + 2] * inv, oacc[d][4 * rq + 3] * inv);
     }
   }
-  if (g == 0) p.lse[qrow] = real ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+  if (g == 0) p.lse[qrow] = real ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
 }
 
 template <typename T, int D>

@@ -34,6 +34,13 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Softmax reference lag (log2 units): the running exponent reference only moves
+// when a row maximum exceeds it by more than this, so unnormalised
+// probabilities stay <= 2^kRefLag (exact math, far from fp32 / bf16 overflow).
+constexpr float kRefLag = 8.0f;
+
+// 2^x with the hardware instruction (inputs are <= kRefLag or -inf here).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr float kLn2 = 0.6931471805599453f;
 
 template <typename T> struct Frag;
@@ -143,51 +150,185 @@ constexpr int kLdsPadBytes = 16;
 
 template <typename T> struct Pad { static constexpr int elems = kLdsPadBytes / sizeof(T); };
 
-// Copy ROWS x D elements of a row-major global matrix (rows row0.., row
-// stride D) into LDS rows of pitch PITCH.  Rows at or beyond nrows are zero.
-template <typename T, int ROWS, int D, int PITCH, int NT>
-__device__ __forceinline__ void stage_rows(T* __restrict__ lds, const T* __restrict__ src, int nrows) {
-  constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
-  constexpr int CPR = D / EPC;                 // chunks per row
-  constexpr int TOTAL = ROWS * CPR;
-  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// ---------------------------------------------------------------------------
+// LDS tiles.  A tile holds ROWS rows of a row-major [*, D] matrix, row-major in
+// LDS with no padding; the 16-byte chunks of each row are XOR-swizzled by a
+// function of the row so that the 32 rows an MFMA operand read touches, and
+// the 4 rows a transpose read touches, fall on different banks.
+// ---------------------------------------------------------------------------
+template <typename T, int ROWS, int D>
+struct Tile {
+  static constexpr int EPC = 16 / sizeof(T);     // elements per 16-byte chunk
+  static constexpr int CPR = D / EPC;            // chunks per row (>= 8)
+  static constexpr int ELEMS = ROWS * D;
+  static constexpr int BLOCKS = ROWS * CPR / 64; // 1 KB blocks (one DMA instruction each)
+  static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0, "row must be >= 8 power-of-two chunks");
+  static_assert(ROWS * CPR % 64 == 0, "tile must be whole 1 KB blocks");
+  __device__ static __forceinline__ int swz(int r) { return ((2 * (r & 7)) | ((r >> 3) & 1)) & (CPR - 1); }
+  // element offset of logical chunk lc of row r
+  __device__ static __forceinline__ int off(int r, int lc) { return r * D + ((lc ^ swz(r)) * EPC); }
+};
+
+#define NB_GLOBAL(p) ((const __attribute__((address_space(1))) void*)(p))
+#define NB_LOCAL(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Asynchronous copy of rows [0, ROWS) of src (row stride D) into a tile with
+// global_load_lds (no registers involved).  Rows at or beyond nrows repeat row
+// nrows-1: finite values the kernels always mask out.  Each wave moves whole
+// 1 KB blocks: lane l of block blk fills physical chunk blk*64 + l.
+template <typename T, int ROWS, int D, int NW>
+__device__ __forceinline__ void dma_tile(T* lds, const T* __restrict__ src, int nrows) {
+  typedef Tile<T, ROWS, D> TL;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-  for (int c = threadIdx.x; c < TOTAL; c += NT) {
-    const int r = c / CPR, col = (c % CPR) * EPC;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r < nrows) v = *reinterpret_cast<const u32x4*>(src + (size_t)r * D + col);
-    *reinterpret_cast<u32x4*>(lds + r * PITCH + col) = v;
+  for (int x = 0; x < (TL::BLOCKS + NW - 1) / NW; ++x) {
+    const int blk = w + x * NW;
+    if (TL::BLOCKS % NW != 0 && blk >= TL::BLOCKS) break;
+    const int P = blk * 64 + l;
+    const int r = P / TL::CPR, pc = P % TL::CPR;
+    const int lc = pc ^ TL::swz(r);
+    const T* g = src + (size_t)min(r, nrows - 1) * D + lc * TL::EPC;
+    __builtin_amdgcn_global_load_lds(NB_GLOBAL(g), NB_LOCAL(lds + blk * 64 * TL::EPC), 16, 0, 0);
   }
 }
 
-// Copy ROWS x D elements of a row-major global matrix into LDS transposed:
-// element (r, d) goes to lds[d * TPITCH + perm16(r)], so that 16-byte reads at
-// column 16*m + 8*g return the rows a probability accumulator holds for step m
-// and lane group g.  Rows at or beyond nrows are zero.  ROWS % 16 == 0.
-template <typename T, int ROWS, int D, int TPITCH, int NT>
-__device__ __forceinline__ void stage_rows_transposed(T* __restrict__ lds, const T* __restrict__ src,
-                                                      int nrows) {
-  typedef typename Frag<T>::type F;
-  typedef typename Quad<T>::type Q4;
-  constexpr int RG = ROWS / 4;                 // groups of 4 rows
-  constexpr int CG = D / 8;                    // groups of 8 columns
-  constexpr int TOTAL = RG * CG;
+// Asynchronous copy of n <= 64 consecutive 4-byte words (one wave; lanes >= n
+// repeat word n-1).  The destination must hold 64 words.
+__device__ __forceinline__ void dma_words(void* lds, const void* __restrict__ src, int n) {
+  const int l = threadIdx.x & 63;
+  const char* g = reinterpret_cast<const char*>(src) + 4 * min(l, n - 1);
+  __builtin_amdgcn_global_load_lds(NB_GLOBAL(g), NB_LOCAL(lds), 4, 0, 0);
+}
+
+// Scheduling hints: interleave N MFMAs each preceded by R LDS reads, so that
+// only a couple of operand fragments are live at a time (with one wave per
+// SIMD the scheduler otherwise hoists every read and runs out of registers).
+template <int N, int R>
+__device__ __forceinline__ void interleave_lds_mfma() {
 #pragma unroll
-  for (int gi = threadIdx.x; gi < TOTAL; gi += NT) {
-    const int rg = gi % RG, cg = gi / RG;
-    const int r0 = 4 * rg, c0 = 8 * cg;
-    F x[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      x[e] = (r0 + e < nrows) ? load_frag<T>(src + (size_t)(r0 + e) * D + c0) : zero_frag<T>();
-    const int col = perm16(r0);
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      Q4 v;
-      v[0] = x[0][d]; v[1] = x[1][d]; v[2] = x[2][d]; v[3] = x[3][d];
-      *reinterpret_cast<Q4*>(lds + (c0 + d) * TPITCH + col) = v;
-    }
+  for (int x = 0; x < N; ++x) {
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
   }
 }
+
+// Wait until this wave's global reads (including copies into LDS) have landed.
+__device__ __forceinline__ void wait_global() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Precomputed readers for bf16 tiles.  The XOR swizzle only touches the low 4
+// chunk bits, so every operand address is one of a few per-lane bases plus a
+// compile-time offset; keeping just those bases live (instead of letting the
+// compiler hoist one address per fragment) saves ~100 registers per kernel.
+//
+// RowReader: fragments (r0 + 32*sb, 16*kk + 8*g .. +7) for the lane's row r0.
+template <typename TL>
+struct RowReader {
+  static constexpr int NB = (TL::CPR / 2 < 8) ? TL::CPR / 2 : 8;
+  static constexpr int RB = TL::CPR * 16;  // row bytes
+  int base[NB];
+  __device__ __forceinline__ RowReader(int r0, int g) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) base[j] = 2 * TL::off(r0, 2 * j + g);
+  }
+  __device__ __forceinline__ bf16x8 read(const bf16* lds, int sb, int kk) const {
+    const int byte = base[kk % NB] + (kk / NB) * (2 * NB * 16) + sb * 32 * RB;
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(lds) + byte);
+  }
+};
+
+// ColReader: the transposed fragments frag_col(dblk, m) of a bf16 tile.
+template <typename TL>
+struct ColReader {
+  static constexpr int NB = (TL::CPR / 4 < 4) ? TL::CPR / 4 : 4;
+  static constexpr int RB = TL::CPR * 16;
+  int lo[NB], hi[NB];
+  __device__ __forceinline__ ColReader(int lane) {
+    const int g = lane >> 5, s = lane & 15, half = (lane >> 4) & 1;
+    const int r = 4 * g + (s >> 2);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int d = 32 * j + 16 * half + 4 * (s & 3);
+      lo[j] = 2 * (TL::off(r, d >> 3) + (d & 7));
+      hi[j] = 2 * (TL::off(r + 8, d >> 3) + (d & 7));
+    }
+  }
+  __device__ __forceinline__ bf16x8 read(const bf16* lds, int dblk, int m) const {
+    typedef __attribute__((address_space(3))) bf16x4 lds_b4;
+    const int extra = (dblk / NB) * (NB * 4 * 16) + m * 16 * RB;
+    const char* c = reinterpret_cast<const char*>(lds);
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4*)(c + lo[dblk % NB] + extra));
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4*)(c + hi[dblk % NB] + extra));
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+};
+
+// Operand fragment along a tile row: elements (r, 16*kk + 8*g .. +7).
+template <typename T, typename TL>
+__device__ __forceinline__ typename Frag<T>::type frag_row(const T* lds, int r, int kk, int g) {
+  if constexpr (sizeof(T) == 2) {
+    return *reinterpret_cast<const typename Frag<T>::type*>(lds + TL::off(r, 2 * kk + g));
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(lds + TL::off(r, 4 * kk + 2 * g));
+    const f32x4 b = *reinterpret_cast<const f32x4*>(lds + TL::off(r, 4 * kk + 2 * g + 1));
+    return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+}
+
+// Operand fragment across tile rows, for a product whose other operand comes
+// from accumulator rows: the lane's operand row is column d = 32*dblk + lane%32
+// of the tile, and slot t of step m holds tile row kappa(m, g, t) (see the top
+// of this file).  bf16: two ds_read_b64_tr_b16 per fragment -- within each
+// 16-lane group, lane i receives element i%4 of the 8-byte pieces the lanes
+// i/4 + 4u (u = 0..3) address, as slot u.  float: eight scalar LDS reads.
+template <typename T, typename TL>
+__device__ __forceinline__ typename Frag<T>::type frag_col(const T* lds, int dblk, int m, int lane) {
+  const int g = lane >> 5;
+  if constexpr (sizeof(T) == 2) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_b4;
+    const int s = lane & 15, half = (lane >> 4) & 1;
+    const int r = 16 * m + 4 * g + (s >> 2);
+    const int d = 32 * dblk + 16 * half + 4 * (s & 3);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4*)(lds + TL::off(r, d >> 3) + (d & 7)));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4*)(lds + TL::off(r + 8, d >> 3) + (d & 7)));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    const int d = 32 * dblk + (lane & 31);
+    f32x8 f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int r = 16 * m + 8 * (t >> 2) + 4 * g + (t & 3);
+      f[t] = lds[TL::off(r, d / TL::EPC) + d % TL::EPC];
+    }
+    return f;
+  }
+}
+
+// Operand access to a tile for one lane: rows r0 + 32*sb along D, and the
+// transposed fragments; bf16 through the precomputed readers, float (debug
+// path) through the generic element reads.
+template <typename T, typename TL> struct TileAccess;
+
+template <typename TL>
+struct TileAccess<bf16, TL> {
+  RowReader<TL> rr;
+  ColReader<TL> cr;
+  __device__ __forceinline__ TileAccess(int r0, int lane) : rr(r0, lane >> 5), cr(lane) {}
+  __device__ __forceinline__ bf16x8 row(const bf16* lds, int sb, int kk) const { return rr.read(lds, sb, kk); }
+  __device__ __forceinline__ bf16x8 col(const bf16* lds, int dblk, int m) const { return cr.read(lds, dblk, m); }
+};
+
+template <typename TL>
+struct TileAccess<float, TL> {
+  int r0, lane;
+  __device__ __forceinline__ TileAccess(int r0_, int lane_) : r0(r0_), lane(lane_) {}
+  __device__ __forceinline__ f32x8 row(const float* lds, int sb, int kk) const {
+    return frag_row<float, TL>(lds, r0 + 32 * sb, kk, lane >> 5);
+  }
+  __device__ __forceinline__ f32x8 col(const float* lds, int dblk, int m) const {
+    return frag_col<float, TL>(lds, dblk, m, lane);
+  }
+};
 
 }  // namespace nb

@@ -65,7 +65,8 @@ struct OwnerParams {
 
 hipError_t launch_segment_build(const SegParams& p, hipStream_t s);
 hipError_t launch_attn_fwd(const FwdParams& p, int D, bool f32, hipStream_t s);
-hipError_t launch_attn_bwd(const BwdParams& p, int D, bool f32, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdParams& p, int D, bool f32, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdParams& p, int D, bool f32, hipStream_t s);
 hipError_t launch_owner_flags(const OwnerParams& p, hipStream_t s);
 
 }  // namespace nb

@@ -146,32 +146,13 @@ size_t nb_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, 
   return (delta + 255) & ~(size_t)255;
 }
 
-int nb_attn_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o, const void* o_resid,
-                const float* lse,
-                const int32_t* seg_buf, const int32_t* folded_ids, int B, int Hq, int Hkv, int L, int S, int D,
-                float scale, int window_left, int dtype, void* dq, void* dk, void* dv, const int32_t* owner_off,
-                int n_owner, uint8_t* owner_attended, void* ws, size_t ws_bytes, void* stream) {
-  const void* ptrs[] = {dout, q, k, v, o, lse, seg_buf, dq, dk, dv, ws};
-  int st = attn_common_checks(ptrs, 11, B, Hq, Hkv, L, S, D, scale, dtype);
-  if (st != NB_OK) return st;
-  if (o_resid != nullptr && !aligned16(o_resid)) return NB_ERR_INVALID_ARG;
-  if (ws_bytes < nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype)) return NB_ERR_WORKSPACE;
-  if (n_owner < 0 || n_owner > nb::kMaxOwners) return NB_ERR_INVALID_ARG;
-  nb::OwnerParams op;
-  if (n_owner > 0) {
-    if (owner_off == nullptr || owner_attended == nullptr || folded_ids == nullptr) return NB_ERR_INVALID_ARG;
-    if (owner_off[0] != 0 || owner_off[n_owner] != S) return NB_ERR_INVALID_ARG;
-    for (int x = 0; x < n_owner; ++x)
-      if (owner_off[x + 1] < owner_off[x]) return NB_ERR_INVALID_ARG;
-    std::memset(&op, 0, sizeof(op));
-    op.folded = folded_ids;
-    op.kcov_lo = seg_buf + nb::seg_layout(B, L, S).kcov_lo;
-    op.attended = owner_attended;
-    op.B = B;
-    op.S = S;
-    op.n_owner = n_owner;
-    for (int x = 0; x <= n_owner; ++x) op.off[x] = owner_off[x];
-  }
+}  // extern "C"
+
+namespace {
+
+nb::BwdParams bwd_params(const void* dout, const void* q, const void* k, const void* v, const void* o,
+                         const void* o_resid, const float* lse, const int32_t* seg_buf, int B, int Hq, int Hkv,
+                         int L, int S, float scale, int window_left, void* dq, void* dk, void* dv, void* ws) {
   nb::BwdParams p;
   p.q = q;
   p.k = k;
@@ -193,10 +174,94 @@ int nb_attn_bwd(const void* dout, const void* q, const void* k, const void* v, c
   p.window = window_left < 0 ? -1 : window_left;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
-  hipStream_t s = (hipStream_t)stream;
-  st = map_hip(nb::launch_attn_bwd(p, D, dtype == NB_F32, s));
-  if (st != NB_OK || n_owner == 0) return st;
+  return p;
+}
+
+int owner_checks(const int32_t* folded_ids, int S, const int32_t* owner_off, int n_owner,
+                 const uint8_t* owner_attended) {
+  if (n_owner < 0 || n_owner > nb::kMaxOwners) return NB_ERR_INVALID_ARG;
+  if (n_owner == 0) return NB_OK;
+  if (owner_off == nullptr || owner_attended == nullptr || folded_ids == nullptr) return NB_ERR_INVALID_ARG;
+  if (owner_off[0] != 0 || owner_off[n_owner] != S) return NB_ERR_INVALID_ARG;
+  for (int x = 0; x < n_owner; ++x)
+    if (owner_off[x + 1] < owner_off[x]) return NB_ERR_INVALID_ARG;
+  return NB_OK;
+}
+
+int launch_owner(const int32_t* seg_buf, const int32_t* folded_ids, int B, int L, int S, const int32_t* owner_off,
+                 int n_owner, uint8_t* owner_attended, hipStream_t s) {
+  if (n_owner == 0) return NB_OK;
+  nb::OwnerParams op;
+  std::memset(&op, 0, sizeof(op));
+  op.folded = folded_ids;
+  op.kcov_lo = seg_buf + nb::seg_layout(B, L, S).kcov_lo;
+  op.attended = owner_attended;
+  op.B = B;
+  op.S = S;
+  op.n_owner = n_owner;
+  for (int x = 0; x <= n_owner; ++x) op.off[x] = owner_off[x];
   return map_hip(nb::launch_owner_flags(op, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int nb_attn_bwd_dq(const void* dout, const void* q, const void* k, const void* v, const void* o,
+                   const void* o_resid, const float* lse, const int32_t* seg_buf, int B, int Hq, int Hkv, int L,
+                   int S, int D, float scale, int window_left, int dtype, void* dq, void* ws, size_t ws_bytes,
+                   void* stream) {
+  const void* ptrs[] = {dout, q, k, v, o, lse, seg_buf, dq, ws};
+  int st = attn_common_checks(ptrs, 9, B, Hq, Hkv, L, S, D, scale, dtype);
+  if (st != NB_OK) return st;
+  if (o_resid != nullptr && !aligned16(o_resid)) return NB_ERR_INVALID_ARG;
+  if (ws_bytes < nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype)) return NB_ERR_WORKSPACE;
+  const nb::BwdParams p = bwd_params(dout, q, k, v, o, o_resid, lse, seg_buf, B, Hq, Hkv, L, S, scale,
+                                     window_left, dq, nullptr, nullptr, ws);
+  return map_hip(nb::launch_bwd_dq(p, D, dtype == NB_F32, (hipStream_t)stream));
+}
+
+int nb_attn_bwd_dkdv(const void* dout, const void* q, const void* k, const void* v, const float* lse,
+                     const int32_t* seg_buf, int B, int Hq, int Hkv, int L, int S, int D, float scale,
+                     int window_left, int dtype, void* dk, void* dv, const void* ws, size_t ws_bytes,
+                     void* stream) {
+  const void* ptrs[] = {dout, q, k, v, lse, seg_buf, dk, dv, ws};
+  int st = attn_common_checks(ptrs, 9, B, Hq, Hkv, L, S, D, scale, dtype);
+  if (st != NB_OK) return st;
+  if (ws_bytes < nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype)) return NB_ERR_WORKSPACE;
+  const nb::BwdParams p = bwd_params(dout, q, k, v, nullptr, nullptr, lse, seg_buf, B, Hq, Hkv, L, S, scale,
+                                     window_left, nullptr, dk, dv, const_cast<void*>(ws));
+  return map_hip(nb::launch_bwd_dkdv(p, D, dtype == NB_F32, (hipStream_t)stream));
+}
+
+int nb_owner_attended(const int32_t* seg_buf, const int32_t* folded_ids, int B, int L, int S,
+                      const int32_t* owner_off, int n_owner, uint8_t* owner_attended, void* stream) {
+  if (seg_buf == nullptr || !dims_ok(B, L, S)) return NB_ERR_INVALID_ARG;
+  int st = owner_checks(folded_ids, S, owner_off, n_owner, owner_attended);
+  if (st != NB_OK) return st;
+  return launch_owner(seg_buf, folded_ids, B, L, S, owner_off, n_owner, owner_attended, (hipStream_t)stream);
+}
+
+int nb_attn_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o, const void* o_resid,
+                const float* lse, const int32_t* seg_buf, const int32_t* folded_ids, int B, int Hq, int Hkv, int L,
+                int S, int D, float scale, int window_left, int dtype, void* dq, void* dk, void* dv,
+                const int32_t* owner_off, int n_owner, uint8_t* owner_attended, void* ws, size_t ws_bytes,
+                void* stream) {
+  const void* ptrs[] = {dout, q, k, v, o, lse, seg_buf, dq, dk, dv, ws};
+  int st = attn_common_checks(ptrs, 11, B, Hq, Hkv, L, S, D, scale, dtype);
+  if (st != NB_OK) return st;
+  if (o_resid != nullptr && !aligned16(o_resid)) return NB_ERR_INVALID_ARG;
+  if (ws_bytes < nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype)) return NB_ERR_WORKSPACE;
+  st = owner_checks(folded_ids, S, owner_off, n_owner, owner_attended);
+  if (st != NB_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const nb::BwdParams p = bwd_params(dout, q, k, v, o, o_resid, lse, seg_buf, B, Hq, Hkv, L, S, scale,
+                                     window_left, dq, dk, dv, ws);
+  st = map_hip(nb::launch_bwd_dq(p, D, dtype == NB_F32, s));
+  if (st != NB_OK) return st;
+  st = map_hip(nb::launch_bwd_dkdv(p, D, dtype == NB_F32, s));
+  if (st != NB_OK) return st;
+  return launch_owner(seg_buf, folded_ids, B, L, S, owner_off, n_owner, owner_attended, s);
 }
 
 }  // extern "C"
