@@ -51,8 +51,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) int klo0[64], klo1[64];
   __shared__ int n_tiles_s;
 
-  const int kt = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // Work order: the kv group (batch row, kv head) varies fastest (one XCD per
+  // group with 8 XCDs, so the Q/dO rows neighbouring key tiles share stay in its
+  // L2); key tiles run from the end of the neighbourhood backwards, so the
+  // cheap tiles no query reaches (the beginning) are dispatched last and fill
+  // the tail.
   const int grp = p.Hq / p.Hkv;
+  const int ngroups = p.B * p.Hkv;
+  const int n_kt = (p.S + C::BK - 1) / C::BK;
+  const int gid = blockIdx.x % ngroups;
+  const int b = gid / p.Hkv, kvh = gid % p.Hkv;
+  const int kt = n_kt - 1 - (int)(blockIdx.x / ngroups);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, ln = lane & 31;
   const int off = p.S - p.L;
   const int j0 = kt * C::BK;                      // first key of the workgroup
@@ -215,8 +224,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) T V1[TL::ELEMS];
   __shared__ int red[4][2];
 
-  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int kvh = h / (p.Hq / p.Hkv);
+  // same work order as the forward: kv group fastest, then q head, then query tile
+  const int grp = p.Hq / p.Hkv;
+  const int ngroups = p.B * p.Hkv;
+  const int gid = blockIdx.x % ngroups, rest = blockIdx.x / ngroups;
+  const int b = gid / p.Hkv, kvh = gid % p.Hkv;
+  const int h = kvh * grp + rest % grp, qt = rest / grp;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, ln = lane & 31;
   const int off = p.S - p.L;
   const int i = qt * C::BM + 32 * w + ln;
@@ -349,7 +362,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
 template <typename T, int D>
 static hipError_t launch_dq_t(const BwdParams& p, hipStream_t s) {
   typedef DqCfg<T, D> C;
-  dim3 grid((p.L + C::BM - 1) / C::BM, p.Hq, p.B);
+  dim3 grid((unsigned)((p.L + C::BM - 1) / C::BM) * p.Hq * p.B);
   hipLaunchKernelGGL((bwd_dq_kernel<T, D>), grid, dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
@@ -357,7 +370,7 @@ static hipError_t launch_dq_t(const BwdParams& p, hipStream_t s) {
 template <typename T, int D>
 static hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t s) {
   typedef DkvCfg<T, D> C;
-  dim3 grid((p.S + C::BK - 1) / C::BK, p.Hkv, p.B);
+  dim3 grid((unsigned)((p.S + C::BK - 1) / C::BK) * p.Hkv * p.B);
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), grid, dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }

@@ -46,8 +46,15 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) T V1[TL::ELEMS];
   __shared__ int red[4][2];
 
-  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int kvh = h / (p.Hq / p.Hkv);
+  // Work order: the kv group (batch row, kv head) varies fastest, so with the
+  // round-robin dispatch over 8 XCDs every group stays on one XCD and the K/V
+  // window its query tiles share stays in that XCD's L2; the group's q heads
+  // come next, then the query tiles in order.
+  const int grp = p.Hq / p.Hkv;
+  const int ngroups = p.B * p.Hkv;
+  const int gid = blockIdx.x % ngroups, rest = blockIdx.x / ngroups;
+  const int b = gid / p.Hkv, kvh = gid % p.Hkv;
+  const int h = kvh * grp + rest % grp, qt = rest / grp;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, ln = lane & 31;
   const int off = p.S - p.L;
   const int i = qt * C::BM + 32 * w + ln;
@@ -194,7 +201,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
 template <typename T, int D>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   typedef FwdCfg<T, D> C;
-  dim3 grid((p.L + C::BM - 1) / C::BM, p.Hq, p.B);
+  dim3 grid((unsigned)((p.L + C::BM - 1) / C::BM) * p.Hq * p.B);
   hipLaunchKernelGGL((attn_fwd_kernel<T, D>), grid, dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
