@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int gid = blockIdx.x % ngroups;
   const int b = gid / p.Hkv, kvh = gid % p.Hkv;
   const int kt = n_kt - 1 - (int)(blockIdx.x / ngroups);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, ln = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
   const int off = p.S - p.L;
   const int j0 = kt * C::BK;                      // first key of the workgroup
   const int jw = j0 + 32 * w;                     // first key of the wave
@@ -97,13 +97,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   const T* kvq = reinterpret_cast<const T*>(p.q);
   const T* kvd = reinterpret_cast<const T*>(p.dout);
+  const DmaPlan<T, C::BQ, D, C::NW> plan;
   auto load = [&](T* Qs, T* Gs, float* ls, float* ds, int* ks, int it) {
     const int hh = it / n_t, t = t_first + it % n_t;
     const int i0 = t * C::BQ;
     const int nr = min(C::BQ, p.L - i0);
     const size_t rb = ((size_t)b * p.Hq + kvh * grp + hh) * p.L + i0;
-    dma_tile<T, C::BQ, D, C::NW>(Qs, kvq + rb * D, nr);
-    dma_tile<T, C::BQ, D, C::NW>(Gs, kvd + rb * D, nr);
+    plan.issue(Qs, kvq + rb * D, nr);
+    plan.issue(Gs, kvd + rb * D, nr);
     if (w == 0) dma_words(ls, p.lse + rb, nr);
     if (w == 1) dma_words(ds, p.delta + rb, nr);
     if (w == 2) dma_words(ks, p.row_klo + (size_t)b * p.L + i0, nr);
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qi = acc_row(r, g);
-      float pr = fast_exp2(sacc[r] * p.scale_log2 - ls[qi] * kLog2e);
+      float pr = fast_exp2(fmaf(sacc[r], p.scale_log2, -ls[qi] * kLog2e));
       if (!full) {
         if (qi >= nrows || j < band(qi) || j > off + i0 + qi) pr = 0.f;
       }
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   const int gid = blockIdx.x % ngroups, rest = blockIdx.x / ngroups;
   const int b = gid / p.Hkv, kvh = gid % p.Hkv;
   const int h = kvh * grp + rest % grp, qt = rest / grp;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, ln = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
   const int off = p.S - p.L;
   const int i = qt * C::BM + 32 * w + ln;
   const bool in_range = i < p.L;
@@ -254,10 +255,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
 
   const T* __restrict__ kbase = reinterpret_cast<const T*>(p.k) + ((size_t)b * p.Hkv + kvh) * p.S * D;
   const T* __restrict__ vbase = reinterpret_cast<const T*>(p.v) + ((size_t)b * p.Hkv + kvh) * p.S * D;
+  const DmaPlan<T, C::BN, D, C::NW> plan;
   auto load = [&](T* Ks, T* Vs, int j0) {
     const int nv = min(C::BN, p.S - j0);
-    dma_tile<T, C::BN, D, C::NW>(Ks, kbase + (size_t)j0 * D, nv);
-    dma_tile<T, C::BN, D, C::NW>(Vs, vbase + (size_t)j0 * D, nv);
+    plan.issue(Ks, kbase + (size_t)j0 * D, nv);
+    plan.issue(Vs, vbase + (size_t)j0 * D, nv);
   };
   if (kstart < kend) load(K0, V0, kstart);
 
@@ -313,7 +315,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     for (int sb = 0; sb < C::BN / 32; ++sb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = fast_exp2(sacc[sb][r] * p.scale_log2 - lse2);
+        float pr = fast_exp2(fmaf(sacc[sb][r], p.scale_log2, -lse2));
         if (!full) {
           const int jj = j0 + 32 * sb + acc_row(r, g);
           if (!real || jj < bs || jj > pos) pr = 0.f;

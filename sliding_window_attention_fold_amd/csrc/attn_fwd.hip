@@ -26,16 +26,22 @@
 
 namespace nb {
 
+// Two workgroups share a CU (bf16): while one runs its softmax on the vector
+// units, the other keeps the matrix cores busy, which a single wave per SIMD
+// cannot do on its own.  That needs <= 256 registers per wave and <= 80 KB of
+// LDS per workgroup, hence 32-key tiles at D = 256.  The float32 debug path
+// keeps one workgroup per CU.
 template <typename T, int D>
 struct FwdCfg {
   static constexpr int NW = 4;
   static constexpr int NT = 64 * NW;
   static constexpr int BM = 32 * NW;
-  static constexpr int BN = (D * sizeof(T) > 512) ? 32 : 64;  // keys per tile (4 tiles fit in LDS)
+  static constexpr int BN = (D <= 128) ? 64 : 32;  // keys per tile
+  static constexpr int OCC = (sizeof(T) == 2) ? 2 : 1;  // workgroups per CU
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdParams p) {
   typedef FwdCfg<T, D> C;
   typedef Tile<T, C::BN, D> TL;
   typedef typename Frag<T>::type F;
@@ -55,7 +61,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdParams p) {
   const int gid = blockIdx.x % ngroups, rest = blockIdx.x / ngroups;
   const int b = gid / p.Hkv, kvh = gid % p.Hkv;
   const int h = kvh * grp + rest % grp, qt = rest / grp;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, ln = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
   const int off = p.S - p.L;
   const int i = qt * C::BM + 32 * w + ln;
   const bool in_range = i < p.L;

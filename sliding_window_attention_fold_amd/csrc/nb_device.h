@@ -39,6 +39,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 // probabilities stay <= 2^kRefLag (exact math, far from fp32 / bf16 overflow).
 constexpr float kRefLag = 8.0f;
 
+// Wave index within the workgroup, as a wave-uniform (scalar) value: LDS
+// destinations of the async copies must be uniform, and without the hint the
+// compiler wraps every copy in a waterfall loop.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // 2^x with the hardware instruction (inputs are <= kRefLag or -inf here).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr float kLn2 = 0.6931471805599453f;
@@ -181,7 +186,7 @@ struct Tile {
 template <typename T, int ROWS, int D, int NW>
 __device__ __forceinline__ void dma_tile(T* lds, const T* __restrict__ src, int nrows) {
   typedef Tile<T, ROWS, D> TL;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int w = wave_id(), l = threadIdx.x & 63;
 #pragma unroll
   for (int x = 0; x < (TL::BLOCKS + NW - 1) / NW; ++x) {
     const int blk = w + x * NW;
@@ -193,6 +198,42 @@ __device__ __forceinline__ void dma_tile(T* lds, const T* __restrict__ src, int 
     __builtin_amdgcn_global_load_lds(NB_GLOBAL(g), NB_LOCAL(lds + blk * 64 * TL::EPC), 16, 0, 0);
   }
 }
+
+// The same copy with this lane's per-block offsets computed once: issuing a
+// tile then costs one uniform base (SGPRs) plus a precomputed 32-bit offset
+// per block.  Rows at or beyond nrows repeat row nrows-1 (uniform slow path).
+template <typename T, int ROWS, int D, int NW>
+struct DmaPlan {
+  typedef Tile<T, ROWS, D> TL;
+  static_assert(TL::BLOCKS % NW == 0, "tile blocks must split evenly over the waves");
+  static constexpr int PER = TL::BLOCKS / NW;
+  int goff[PER];  // element offset of this lane's chunk within a full tile
+  __device__ __forceinline__ DmaPlan() {
+    const int w = wave_id(), l = threadIdx.x & 63;
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      const int P = (w + x * NW) * 64 + l;
+      const int r = P / TL::CPR, pc = P % TL::CPR;
+      goff[x] = r * D + (pc ^ TL::swz(r)) * TL::EPC;
+    }
+  }
+  __device__ __forceinline__ void issue(T* lds, const T* __restrict__ src, int nrows) const {
+    const int w = wave_id(), l = threadIdx.x & 63;
+    if (nrows >= ROWS) {
+#pragma unroll
+      for (int x = 0; x < PER; ++x)
+        __builtin_amdgcn_global_load_lds(NB_GLOBAL(src + goff[x]), NB_LOCAL(lds + (w + x * NW) * 64 * TL::EPC),
+                                         16, 0, 0);
+    } else {
+#pragma unroll
+      for (int x = 0; x < PER; ++x) {
+        const int r = ((w + x * NW) * 64 + l) / TL::CPR;
+        const int o = goff[x] + (min(r, nrows - 1) - r) * D;
+        __builtin_amdgcn_global_load_lds(NB_GLOBAL(src + o), NB_LOCAL(lds + (w + x * NW) * 64 * TL::EPC), 16, 0, 0);
+      }
+    }
+  }
+};
 
 // Asynchronous copy of n <= 64 consecutive 4-byte words (one wave; lanes >= n
 // repeat word n-1).  The destination must hold 64 words.
@@ -228,9 +269,9 @@ struct RowReader {
   static constexpr int NB = (TL::CPR / 2 < 8) ? TL::CPR / 2 : 8;
   static constexpr int RB = TL::CPR * 16;  // row bytes
   int base[NB];
-  __device__ __forceinline__ RowReader(int r0, int g) {
+  __device__ __forceinline__ RowReader(int r0, int g, int byte0 = 0) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) base[j] = 2 * TL::off(r0, 2 * j + g);
+    for (int j = 0; j < NB; ++j) base[j] = byte0 + 2 * TL::off(r0, 2 * j + g);
   }
   __device__ __forceinline__ bf16x8 read(const bf16* lds, int sb, int kk) const {
     const int byte = base[kk % NB] + (kk / NB) * (2 * NB * 16) + sb * 32 * RB;
@@ -244,14 +285,14 @@ struct ColReader {
   static constexpr int NB = (TL::CPR / 4 < 4) ? TL::CPR / 4 : 4;
   static constexpr int RB = TL::CPR * 16;
   int lo[NB], hi[NB];
-  __device__ __forceinline__ ColReader(int lane) {
+  __device__ __forceinline__ ColReader(int lane, int byte0 = 0) {
     const int g = lane >> 5, s = lane & 15, half = (lane >> 4) & 1;
     const int r = 4 * g + (s >> 2);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int d = 32 * j + 16 * half + 4 * (s & 3);
-      lo[j] = 2 * (TL::off(r, d >> 3) + (d & 7));
-      hi[j] = 2 * (TL::off(r + 8, d >> 3) + (d & 7));
+      lo[j] = byte0 + 2 * (TL::off(r, d >> 3) + (d & 7));
+      hi[j] = byte0 + 2 * (TL::off(r + 8, d >> 3) + (d & 7));
     }
   }
   __device__ __forceinline__ bf16x8 read(const bf16* lds, int dblk, int m) const {
@@ -314,20 +355,24 @@ template <typename TL>
 struct TileAccess<bf16, TL> {
   RowReader<TL> rr;
   ColReader<TL> cr;
-  __device__ __forceinline__ TileAccess(int r0, int lane) : rr(r0, lane >> 5), cr(lane) {}
+  // row_byte0 / col_byte0: constant byte offsets (from the pointer later passed
+  // to row() / col()) folded into the per-lane bases
+  __device__ __forceinline__ TileAccess(int r0, int lane, int row_byte0 = 0, int col_byte0 = 0)
+      : rr(r0, lane >> 5, row_byte0), cr(lane, col_byte0) {}
   __device__ __forceinline__ bf16x8 row(const bf16* lds, int sb, int kk) const { return rr.read(lds, sb, kk); }
   __device__ __forceinline__ bf16x8 col(const bf16* lds, int dblk, int m) const { return cr.read(lds, dblk, m); }
 };
 
 template <typename TL>
 struct TileAccess<float, TL> {
-  int r0, lane;
-  __device__ __forceinline__ TileAccess(int r0_, int lane_) : r0(r0_), lane(lane_) {}
+  int r0, lane, rb0, cb0;
+  __device__ __forceinline__ TileAccess(int r0_, int lane_, int row_byte0 = 0, int col_byte0 = 0)
+      : r0(r0_), lane(lane_), rb0(row_byte0 / 4), cb0(col_byte0 / 4) {}
   __device__ __forceinline__ f32x8 row(const float* lds, int sb, int kk) const {
-    return frag_row<float, TL>(lds, r0 + 32 * sb, kk, lane >> 5);
+    return frag_row<float, TL>(lds + rb0, r0 + 32 * sb, kk, lane >> 5);
   }
   __device__ __forceinline__ f32x8 col(const float* lds, int dblk, int m) const {
-    return frag_col<float, TL>(lds, dblk, m, lane);
+    return frag_col<float, TL>(lds + cb0, dblk, m, lane);
   }
 };
 
