@@ -14,8 +14,9 @@
 //      K^T is read transposed from the same row-major tile.  Its prologue
 //      forms Delta = dO . O (O = stored value + saved rounding residual) and
 //      publishes it for pass 2;
-//   2. dK/dV:  one workgroup per (128 keys, kv head, batch row), four waves of
-//      32 keys; K and V stay in registers, the loop runs over the group's q
+//   2. dK/dV:  one workgroup per (128 keys, kv head, batch row): four key groups
+//      of 32 keys, each served by a pair of waves (K side: S, P, dV; V side:
+//      dP, dS, dK; P crosses through LDS).  The loop runs over the group's q
 //      heads and the 32-row query tiles whose bands reach the keys.  Q and dO
 //      tiles (plus their rows' LSE, Delta, band start) are copied into LDS
 //      asynchronously and read row-wise (A operands of S and dP) and transposed
@@ -29,16 +30,23 @@ namespace nb {
 
 // ---------------------------------------------------------------- dK / dV
 
+// Eight waves: four key groups of 32 keys, two roles per group.  Role A holds
+// the group's K rows, forms S = Q K^T and P, hands P to its partner through LDS
+// and accumulates dV^T = dO^T P; role B holds the V rows, forms dP = dO V^T,
+// takes P, forms dS = P (dP - Delta) and accumulates dK^T = Q^T dS.  Splitting
+// the roles keeps each wave under 256 registers at D = 256 (K or V rows plus
+// one accumulator), so two waves share each SIMD and hide each other's
+// latency; the matrix-core work is the same as one wave doing both.
 template <typename T, int D>
 struct DkvCfg {
-  static constexpr int NW = 4;
+  static constexpr int NW = 8;
   static constexpr int NT = 64 * NW;
-  static constexpr int BK = 32 * NW;   // keys per workgroup
+  static constexpr int BK = 128;       // keys per workgroup
   static constexpr int BQ = 32;        // query rows per step
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   typedef DkvCfg<T, D> C;
   typedef Tile<T, C::BQ, D> TL;
   typedef typename Frag<T>::type F;
@@ -49,6 +57,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) T G1[TL::ELEMS];
   __shared__ __attribute__((aligned(256))) float lse0[64], lse1[64], dl0[64], dl1[64];
   __shared__ __attribute__((aligned(256))) int klo0[64], klo1[64];
+  // P handed from role A to role B: [key group][value quad][lane][4]
+  __shared__ __attribute__((aligned(256))) f32x4 pex[4][4][64];
   __shared__ int n_tiles_s;
 
   // Work order: the kv group (batch row, kv head) varies fastest (one XCD per
@@ -63,9 +73,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int b = gid / p.Hkv, kvh = gid % p.Hkv;
   const int kt = n_kt - 1 - (int)(blockIdx.x / ngroups);
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
+  const int kg = w & 3;                           // key group
+  const bool role_a = w < 4;                      // A: S, P, dV   B: dP, dS, dK
   const int off = p.S - p.L;
   const int j0 = kt * C::BK;                      // first key of the workgroup
-  const int jw = j0 + 32 * w;                     // first key of the wave
+  const int jw = j0 + 32 * kg;                    // first key of the group
   const int j = jw + ln;                          // this lane's key (C column / B operand)
   const int jmax = min(j0 + C::BK, p.S) - 1;      // last key of the workgroup
 
@@ -97,38 +109,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   const T* kvq = reinterpret_cast<const T*>(p.q);
   const T* kvd = reinterpret_cast<const T*>(p.dout);
-  const DmaPlan<T, C::BQ, D, C::NW> plan;
   auto load = [&](T* Qs, T* Gs, float* ls, float* ds, int* ks, int it) {
     const int hh = it / n_t, t = t_first + it % n_t;
     const int i0 = t * C::BQ;
     const int nr = min(C::BQ, p.L - i0);
     const size_t rb = ((size_t)b * p.Hq + kvh * grp + hh) * p.L + i0;
-    plan.issue(Qs, kvq + rb * D, nr);
-    plan.issue(Gs, kvd + rb * D, nr);
+    dma_tile<T, C::BQ, D, C::NW>(Qs, kvq + rb * D, nr);
+    dma_tile<T, C::BQ, D, C::NW>(Gs, kvd + rb * D, nr);
     if (w == 0) dma_words(ls, p.lse + rb, nr);
     if (w == 1) dma_words(ds, p.delta + rb, nr);
     if (w == 2) dma_words(ks, p.row_klo + (size_t)b * p.L + i0, nr);
   };
   if (n_iter > 0) load(Q0, G0, lse0, dl0, klo0, 0);
 
-  // this lane's key row of K and V: the B operands of S = Q K^T and dP = dO V^T
-  F kf[D / 16], vf[D / 16];
+  // this lane's key row of K (role A) or V (role B): the B operand of S = Q K^T
+  // or dP = dO V^T
+  F kv[D / 16];
   {
     const size_t kr = ((size_t)b * p.Hkv + kvh) * p.S + min(j, p.S - 1);
-    const T* kp = reinterpret_cast<const T*>(p.k) + kr * D;
-    const T* vp = reinterpret_cast<const T*>(p.v) + kr * D;
+    const T* src = reinterpret_cast<const T*>(role_a ? p.k : p.v) + kr * D;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      kf[kk] = load_frag<T>(kp + 16 * kk + 8 * g);
-      vf[kk] = load_frag<T>(vp + 16 * kk + 8 * g);
-    }
+    for (int kk = 0; kk < D / 16; ++kk) kv[kk] = load_frag<T>(src + 16 * kk + 8 * g);
   }
   const TileAccess<T, TL> acc(ln, lane);
-  f32x16 dkacc[D / 32], dvacc[D / 32];
+  f32x16 gacc[D / 32];   // dV^T (role A) or dK^T (role B) of the group's keys
 #pragma unroll
-  for (int d = 0; d < D / 32; ++d) { dkacc[d] = f32x16{}; dvacc[d] = f32x16{}; }
+  for (int d = 0; d < D / 32; ++d) gacc[d] = f32x16{};
 
-  auto compute = [&](const T* Qs, const T* Gs, const float* ls, const float* ds, const int* ks, int it) {
+  auto step = [&](const T* Qs, const T* Gs, const float* ls, const float* ds, const int* ks, int it) {
     const int t = t_first + it % n_t;
     const int i0 = t * C::BQ;
     const int nrows = min(C::BQ, p.L - i0);
@@ -139,39 +147,53 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       return p.window >= 0 ? max(bq, off + i0 + qi - p.window) : bq;
     };
     const int bs_min = band(0), bs_max = band(nrows - 1);
-    if (jw > p_max || jw + 31 < bs_min) return;
-    // every (row, key) pair of the wave inside the band: no element mask
+    const bool active = !(jw > p_max || jw + 31 < bs_min);
+    // every (row, key) pair of the group inside the band: no element mask
     const bool full = (nrows == C::BQ) && jw >= bs_max && jw + 31 <= p_min;
 
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    // first half: role A forms P and publishes it, role B forms dP
+    f32x16 sacc = f32x16{};
+    if (active) {
+      const T* src = role_a ? Qs : Gs;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      sacc = mma(acc.row(Qs, 0, kk), kf[kk], sacc);
-      dpacc = mma(acc.row(Gs, 0, kk), vf[kk], dpacc);
-    }
-    if constexpr (sizeof(T) == 2) interleave_lds_mfma<D / 8, 1>();
-    // accumulator r: query row acc_row(r, g) of the tile, key j
+      for (int kk = 0; kk < D / 16; ++kk) sacc = mma(acc.row(src, 0, kk), kv[kk], sacc);
+      if (role_a) {
+        // accumulator r: query row acc_row(r, g) of the tile, key j
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qi = acc_row(r, g);
-      float pr = fast_exp2(fmaf(sacc[r], p.scale_log2, -ls[qi] * kLog2e));
-      if (!full) {
-        if (qi >= nrows || j < band(qi) || j > off + i0 + qi) pr = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          const int qi = acc_row(r, g);
+          float pr = fast_exp2(fmaf(sacc[r], p.scale_log2, -ls[qi] * kLog2e));
+          if (!full) {
+            if (qi >= nrows || j < band(qi) || j > off + i0 + qi) pr = 0.f;
+          }
+          sacc[r] = pr;
+        }
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          pex[kg][qd][lane] = f32x4{sacc[4 * qd], sacc[4 * qd + 1], sacc[4 * qd + 2], sacc[4 * qd + 3]};
       }
-      sacc[r] = pr;
-      dpacc[r] = pr * (dpacc[r] - ds[qi]);
     }
+    __syncthreads();
+    if (!active) return;
+    // second half: role A accumulates dV^T = dO^T P, role B dK^T = Q^T dS
+    if (!role_a) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const f32x4 pq = pex[kg][qd][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * qd + e;
+          sacc[r] = pq[e] * (sacc[r] - ds[acc_row(r, g)]);
+        }
+      }
+    }
+    const T* src = role_a ? Gs : Qs;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const F pf = acc_to_frag<T>(sacc, m);
-      const F sf = acc_to_frag<T>(dpacc, m);
+      const F sf = acc_to_frag<T>(sacc, m);
 #pragma unroll
-      for (int d = 0; d < D / 32; ++d) {
-        dvacc[d] = mma(acc.col(Gs, d, m), pf, dvacc[d]);
-        dkacc[d] = mma(acc.col(Qs, d, m), sf, dkacc[d]);
-      }
+      for (int d = 0; d < D / 32; ++d) gacc[d] = mma(acc.col(src, d, m), sf, gacc[d]);
     }
-    if constexpr (sizeof(T) == 2) interleave_lds_mfma<D / 8, 2>();
   };
 
   for (int it = 0; it < n_iter; it += 2) {
@@ -179,27 +201,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     __syncthreads();
     if (it + 1 < n_iter) load(Q1, G1, lse1, dl1, klo1, it + 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(Q0, G0, lse0, dl0, klo0, it);
+    step(Q0, G0, lse0, dl0, klo0, it);
     if (it + 1 >= n_iter) break;
     wait_global();
     __syncthreads();
     if (it + 2 < n_iter) load(Q0, G0, lse0, dl0, klo0, it + 2);
     __builtin_amdgcn_sched_barrier(0);
-    compute(Q1, G1, lse1, dl1, klo1, it + 1);
+    step(Q1, G1, lse1, dl1, klo1, it + 1);
   }
 
   if (j >= p.S) return;
-  T* dkp = reinterpret_cast<T*>(p.dk) + (((size_t)b * p.Hkv + kvh) * p.S + j) * D;
-  T* dvp = reinterpret_cast<T*>(p.dv) + (((size_t)b * p.Hkv + kvh) * p.S + j) * D;
+  T* dst = reinterpret_cast<T*>(role_a ? p.dv : p.dk) + (((size_t)b * p.Hkv + kvh) * p.S + j) * D;
+  const float f = role_a ? 1.f : p.scale;
 #pragma unroll
   for (int d = 0; d < D / 32; ++d) {
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      const int dd = 32 * d + 8 * rq + 4 * g;
-      store_quad<T>(dkp + dd, dkacc[d][4 * rq] * p.scale, dkacc[d][4 * rq + 1] * p.scale,
-                    dkacc[d][4 * rq + 2] * p.scale, dkacc[d][4 * rq + 3] * p.scale);
-      store_quad<T>(dvp + dd, dvacc[d][4 * rq], dvacc[d][4 * rq + 1], dvacc[d][4 * rq + 2],
-                    dvacc[d][4 * rq + 3]);
+      store_quad<T>(dst + 32 * d + 8 * rq + 4 * g, gacc[d][4 * rq] * f, gacc[d][4 * rq + 1] * f,
+                    gacc[d][4 * rq + 2] * f, gacc[d][4 * rq + 3] * f);
     }
   }
 }
