@@ -9,10 +9,12 @@
 //   dQ = scale * dS K.
 // Two passes keep every output owned by exactly one workgroup (no atomics, the
 // result is bitwise reproducible):
-//   1. dQ:     one workgroup per (128 query rows, q head, batch row); Q and dO in
-//      registers, K/V tiles copied into LDS asynchronously (double-buffered);
-//      K^T is read transposed from the same row-major tile.  Its prologue
-//      forms Delta = dO . O (O = stored value + saved rounding residual) and
+//   1. dQ:     one workgroup per (128 query rows, q head, batch row): four query
+//      groups of 32 rows, each served by a pair of waves (Q side: S, P; dO
+//      side: dP; they swap P and dP through LDS and each accumulates half of
+//      dQ).  K/V tiles are copied into LDS asynchronously (double-buffered); K^T
+//      is read transposed from the same row-major tile.  Its prologue forms
+//      Delta = dO . O (O = stored value + saved rounding residual) and
 //      publishes it for pass 2;
 //   2. dK/dV:  one workgroup per (128 keys, kv head, batch row): four key groups
 //      of 32 keys, each served by a pair of waves (K side: S, P, dV; V side:
@@ -225,24 +227,39 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- dQ
 
+// Eight waves: four query groups of 32 rows, two roles per group.  Role A holds
+// the rows' Q and forms S^T = K Q^T and P; role B holds dO and forms
+// dP^T = V dO^T.  They swap P and dP through LDS, both form dS, and each
+// accumulates half of dQ's columns (A the first D/2, B the rest).  Each wave
+// then needs one operand block plus half an accumulator, so two waves share
+// each SIMD at D = 256; the matrix-core work is the same as one wave doing all.
 template <typename T, int D>
 struct DqCfg {
-  static constexpr int NW = 4;
+  static constexpr int NW = 8;
   static constexpr int NT = 64 * NW;
-  static constexpr int BM = 32 * NW;
-  static constexpr int BN = (D * sizeof(T) > 512) ? 32 : 64;
+  static constexpr int BM = 128;                    // query rows per workgroup
+  static constexpr int BN = (D * sizeof(T) <= 256) ? 64 : 32;   // keys per tile
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   typedef DqCfg<T, D> C;
   typedef Tile<T, C::BN, D> TL;
   typedef typename Frag<T>::type F;
+  constexpr int NSB = C::BN / 32;
+  constexpr int NM = C::BN / 16;
+  constexpr int DH = D / 64;   // 32-wide d blocks of dQ per role
   __shared__ __attribute__((aligned(1024))) T K0[TL::ELEMS];
   __shared__ __attribute__((aligned(1024))) T V0[TL::ELEMS];
   __shared__ __attribute__((aligned(1024))) T K1[TL::ELEMS];
   __shared__ __attribute__((aligned(1024))) T V1[TL::ELEMS];
-  __shared__ int red[4][2];
+  // P (from A) and dP (from B) per query group: [group][block][value quad][lane][4]
+  __shared__ __attribute__((aligned(256))) f32x4 xch[2][4][NSB][4][64];
+  f32x4 (*xp)[NSB][4][64] = xch[0];
+  f32x4 (*xdp)[NSB][4][64] = xch[1];
+  // prologue scratch, dead before the first exchange (a barrier separates them)
+  float (*dls)[64] = reinterpret_cast<float (*)[64]>(&xch[1][0][0][0][0]);
+  int (*red)[2] = reinterpret_cast<int (*)[2]>(&xch[0][0][0][0][0]);
 
   // same work order as the forward: kv group fastest, then q head, then query tile
   const int grp = p.Hq / p.Hkv;
@@ -251,8 +268,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   const int b = gid / p.Hkv, kvh = gid % p.Hkv;
   const int h = kvh * grp + rest % grp, qt = rest / grp;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
+  const int qg = w & 3;                 // query group
+  const bool role_a = w < 4;            // A: Q, S, P   B: dO, dP, Delta
   const int off = p.S - p.L;
-  const int i = qt * C::BM + 32 * w + ln;
+  const int i = qt * C::BM + 32 * qg + ln;
   const bool in_range = i < p.L;
   const int pos = off + i;
   int bs = pos + 1;
@@ -267,88 +286,117 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   const int w_p_min = wave_min_i(real ? pos : INT_MAX);
   const bool w_all_real = wave_min_i(real ? 1 : 0) != 0;
   if (lane == 0) { red[w][0] = w_lo; red[w][1] = w_hi; }
+
+  const size_t qrow = ((size_t)b * p.Hq + h) * p.L + i;
+  const size_t qrow_c = ((size_t)b * p.Hq + h) * p.L + min(i, p.L - 1);  // rows past L read row L-1
+  // this lane's row of Q (role A) or dO (role B): the B operand of S^T or dP^T
+  F rf[D / 16];
+  {
+    const T* src = reinterpret_cast<const T*>(role_a ? p.q : p.dout) + qrow_c * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      rf[kk] = load_frag<T>(src + 16 * kk + 8 * g);
+      if (!in_range) rf[kk] = zero_frag<T>();
+    }
+  }
+  // Delta_i = dO_i . O_i with O the stored value plus its saved rounding
+  // residual (role B); published for the dK/dV pass, which runs after this one.
+  if (!role_a) {
+    const T* op = reinterpret_cast<const T*>(p.o) + qrow_c * D;
+    const T* olp = p.o_lo ? reinterpret_cast<const T*>(p.o_lo) + qrow_c * D : nullptr;
+    float part = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const F ov = load_frag<T>(op + 16 * kk + 8 * g);
+      const F ol = olp ? load_frag<T>(olp + 16 * kk + 8 * g) : zero_frag<T>();
+#pragma unroll
+      for (int t = 0; t < 8; ++t) part += to_f32(rf[kk][t]) * (to_f32(ov[t]) + to_f32(ol[t]));
+    }
+    float dl = part + __shfl_xor(part, 32);
+    if (!real) dl = 0.f;
+    if (in_range && g == 0) p.delta[qrow] = dl;
+    if (g == 0) dls[qg][ln] = dl;
+  }
+  const float lse2 = real ? p.lse[qrow_c] * kLog2e : 0.f;
   __syncthreads();
+  const float dl = dls[qg][ln];
   int kstart = INT_MAX, kend = INT_MIN;
 #pragma unroll
   for (int x = 0; x < C::NW; ++x) { kstart = min(kstart, red[x][0]); kend = max(kend, red[x][1]); }
 
   const T* __restrict__ kbase = reinterpret_cast<const T*>(p.k) + ((size_t)b * p.Hkv + kvh) * p.S * D;
   const T* __restrict__ vbase = reinterpret_cast<const T*>(p.v) + ((size_t)b * p.Hkv + kvh) * p.S * D;
-  const DmaPlan<T, C::BN, D, C::NW> plan;
   auto load = [&](T* Ks, T* Vs, int j0) {
     const int nv = min(C::BN, p.S - j0);
-    plan.issue(Ks, kbase + (size_t)j0 * D, nv);
-    plan.issue(Vs, vbase + (size_t)j0 * D, nv);
+    dma_tile<T, C::BN, D, C::NW>(Ks, kbase + (size_t)j0 * D, nv);
+    dma_tile<T, C::BN, D, C::NW>(Vs, vbase + (size_t)j0 * D, nv);
   };
   if (kstart < kend) load(K0, V0, kstart);
 
-  const size_t qrow = ((size_t)b * p.Hq + h) * p.L + i;
-  const size_t qrow_c = ((size_t)b * p.Hq + h) * p.L + min(i, p.L - 1);  // rows past L read row L-1
-  F qf[D / 16], df[D / 16];
-  float dl;
-  {
-    const T* qp = reinterpret_cast<const T*>(p.q) + qrow_c * D;
-    const T* dp = reinterpret_cast<const T*>(p.dout) + qrow_c * D;
-    const T* op = reinterpret_cast<const T*>(p.o) + qrow_c * D;
-    const T* olp = p.o_lo ? reinterpret_cast<const T*>(p.o_lo) + qrow_c * D : nullptr;
-    // Delta_i = dO_i . O_i with O the stored value plus its saved rounding
-    // residual; published for the dK/dV pass, which runs after this one.
-    float part = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      qf[kk] = load_frag<T>(qp + 16 * kk + 8 * g);
-      df[kk] = load_frag<T>(dp + 16 * kk + 8 * g);
-      const F ov = load_frag<T>(op + 16 * kk + 8 * g);
-      const F ol = olp ? load_frag<T>(olp + 16 * kk + 8 * g) : zero_frag<T>();
-#pragma unroll
-      for (int t = 0; t < 8; ++t) part += to_f32(df[kk][t]) * (to_f32(ov[t]) + to_f32(ol[t]));
-      if (!in_range) { qf[kk] = zero_frag<T>(); df[kk] = zero_frag<T>(); }
-    }
-    dl = part + __shfl_xor(part, 32);
-    if (!real) dl = 0.f;
-    if (in_range && g == 0) p.delta[qrow] = dl;
-  }
-  const float lse2 = real ? p.lse[qrow_c] * kLog2e : 0.f;
-
   const TileAccess<T, TL> acc(ln, lane);
-  f32x16 dqacc[D / 32];
+  const int dh0 = role_a ? 0 : DH;      // first 32-wide d block of this wave's dQ half
+  f32x16 dqacc[DH];
 #pragma unroll
-  for (int d = 0; d < D / 32; ++d) dqacc[d] = f32x16{};
+  for (int d = 0; d < DH; ++d) dqacc[d] = f32x16{};
 
-  auto compute = [&](const T* Ks, const T* Vs, int j0) {
-    if (j0 >= w_hi || j0 + C::BN <= w_lo) return;
+  auto step = [&](const T* Ks, const T* Vs, int j0) {
+    const bool active = !(j0 >= w_hi || j0 + C::BN <= w_lo);   // same for both roles of the group
     const bool full = w_all_real && j0 >= w_bs_max && j0 + C::BN - 1 <= w_p_min;
-    f32x16 sacc[C::BN / 32], dpacc[C::BN / 32];
+    f32x16 sacc[NSB];
+    if (active) {
+      const T* src = role_a ? Ks : Vs;
 #pragma unroll
-    for (int sb = 0; sb < C::BN / 32; ++sb) {
-      sacc[sb] = f32x16{};
-      dpacc[sb] = f32x16{};
+      for (int sb = 0; sb < NSB; ++sb) {
+        sacc[sb] = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        sacc[sb] = mma(acc.row(Ks, sb, kk), qf[kk], sacc[sb]);
-        dpacc[sb] = mma(acc.row(Vs, sb, kk), df[kk], dpacc[sb]);
+        for (int kk = 0; kk < D / 16; ++kk) sacc[sb] = mma(acc.row(src, sb, kk), rf[kk], sacc[sb]);
       }
-    }
-    if constexpr (sizeof(T) == 2) interleave_lds_mfma<C::BN / 32 * D / 8, 1>();
+      if (role_a) {
+        // accumulator r of block sb: key j0 + 32*sb + acc_row(r, g), query row i (this lane)
 #pragma unroll
-    for (int sb = 0; sb < C::BN / 32; ++sb) {
+        for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = fast_exp2(fmaf(sacc[sb][r], p.scale_log2, -lse2));
-        if (!full) {
-          const int jj = j0 + 32 * sb + acc_row(r, g);
-          if (!real || jj < bs || jj > pos) pr = 0.f;
+          for (int r = 0; r < 16; ++r) {
+            float pr = fast_exp2(fmaf(sacc[sb][r], p.scale_log2, -lse2));
+            if (!full) {
+              const int jj = j0 + 32 * sb + acc_row(r, g);
+              if (!real || jj < bs || jj > pos) pr = 0.f;
+            }
+            sacc[sb][r] = pr;
+          }
         }
-        dpacc[sb][r] = pr * (dpacc[sb][r] - dl);
+      }
+      f32x4 (*mine)[4][64] = role_a ? xp[qg] : xdp[qg];
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          mine[sb][qd][lane] = f32x4{sacc[sb][4 * qd], sacc[sb][4 * qd + 1], sacc[sb][4 * qd + 2], sacc[sb][4 * qd + 3]};
+    }
+    __syncthreads();
+    if (!active) return;
+    // dS = P (dP - Delta), with the partner's half taken from LDS
+    f32x4 (*theirs)[4][64] = role_a ? xdp[qg] : xp[qg];
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const f32x4 o = theirs[sb][qd][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * qd + e;
+          const float pr = role_a ? sacc[sb][r] : o[e];
+          const float dp = role_a ? o[e] : sacc[sb][r];
+          sacc[sb][r] = pr * (dp - dl);
+        }
       }
     }
 #pragma unroll
-    for (int m = 0; m < C::BN / 16; ++m) {
-      const F sf = acc_to_frag<T>(dpacc[m >> 1], m & 1);
+    for (int m = 0; m < NM; ++m) {
+      const F sf = acc_to_frag<T>(sacc[m >> 1], m & 1);
 #pragma unroll
-      for (int d = 0; d < D / 32; ++d) dqacc[d] = mma(acc.col(Ks, d, m), sf, dqacc[d]);
+      for (int d = 0; d < DH; ++d) dqacc[d] = mma(acc.col(Ks, dh0 + d, m), sf, dqacc[d]);
     }
-    if constexpr (sizeof(T) == 2) interleave_lds_mfma<C::BN / 16 * D / 32, 2>();
   };
 
   for (int j0 = kstart; j0 < kend; j0 += 2 * C::BN) {
@@ -356,22 +404,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     __syncthreads();
     if (j0 + C::BN < kend) load(K1, V1, j0 + C::BN);
     __builtin_amdgcn_sched_barrier(0);
-    compute(K0, V0, j0);
+    step(K0, V0, j0);
     if (j0 + C::BN >= kend) break;
     wait_global();
     __syncthreads();
     if (j0 + 2 * C::BN < kend) load(K0, V0, j0 + 2 * C::BN);
     __builtin_amdgcn_sched_barrier(0);
-    compute(K1, V1, j0 + C::BN);
+    step(K1, V1, j0 + C::BN);
   }
 
   if (!in_range) return;
   T* dqp = reinterpret_cast<T*>(p.dq) + qrow * D;
 #pragma unroll
-  for (int d = 0; d < D / 32; ++d) {
+  for (int d = 0; d < DH; ++d) {
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      store_quad<T>(dqp + 32 * d + 8 * rq + 4 * g, dqacc[d][4 * rq] * p.scale,
+      store_quad<T>(dqp + 32 * (dh0 + d) + 8 * rq + 4 * g, dqacc[d][4 * rq] * p.scale,
                     dqacc[d][4 * rq + 1] * p.scale, dqacc[d][4 * rq + 2] * p.scale,
                     dqacc[d][4 * rq + 3] * p.scale);
     }
