@@ -68,8 +68,9 @@ def read_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(w, dm, tensors, rows: int):
-    """The fp64 oracle (as it stands) on a bounded sample: one kv-head group, the first `rows` query rows."""
+def cpu_baseline(w, dm, tensors, rows: int, kv_heads: int):
+    """The fp64 oracle (as it stands) on a bounded sample: the first `kv_heads` kv heads with their q heads,
+    the first `rows` query rows, every key of the neighbourhood."""
     import numpy as np
     from oracle import nbattn_oracle as orc
 
@@ -80,20 +81,22 @@ def cpu_baseline(w, dm, tensors, rows: int):
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
     q, k, v, do = tensors
+    nkv = max(1, min(kv_heads, w.Hkv))
+    nq = nkv * w.g
     folded = orc.fold_pad(dm.doc_ids, dm.pad_mask)
     sel = np.arange(min(rows, w.L))
-    heads = list(range(w.g))                    # q heads of kv head 0
     t0 = time.perf_counter()
-    orc.attention_forward(q[:, :w.g], k[:, :1], v[:, :1], folded, w.window, w.D ** -0.5, rows=sel)
-    orc.attention_backward(q[:, :w.g], k[:, :1], v[:, :1], do[:, :w.g], folded, w.window, w.D ** -0.5,
+    orc.attention_forward(q[:, :nq], k[:, :nkv], v[:, :nkv], folded, w.window, w.D ** -0.5, rows=sel)
+    orc.attention_backward(q[:, :nq], k[:, :nkv], v[:, :nkv], do[:, :nq], folded, w.window, w.D ** -0.5,
                            rows=sel)
     dt = time.perf_counter() - t0
     M = orc.allow_mask(folded, w.L, w.window, rows=sel)[:, 0] & orc.real_rows(folded, w.L)[:, sel][:, :, None]
     pairs = int(M.sum())
-    flops = 14.0 * w.D * len(heads) * pairs
+    flops = 14.0 * w.D * nq * pairs
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 numpy oracle fwd+bwd, kv head 0 ({len(heads)} q heads), query rows "
-                      f"[0,{len(sel)}) of {w.L}, all {dm.S} keys; {pairs} allowed pairs; {dt:.1f} s"}
+            "sample": f"fp64 numpy oracle fwd+bwd, kv heads [0,{nkv}) of {w.Hkv} ({nq} of {w.Hq} q heads), "
+                      f"query rows [0,{len(sel)}) of {w.L}, all {dm.S} keys; {pairs} allowed pairs per head; "
+                      f"{dt:.1f} s"}
 
 
 def main() -> int:
@@ -102,7 +105,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
-    ap.add_argument("--cpu-rows", type=int, default=1024, help="query rows of the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows of the oracle sample")
+    ap.add_argument("--cpu-kv-heads", type=int, default=4, help="kv heads (with their q heads) of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
@@ -244,10 +248,11 @@ def main() -> int:
             "kernel": dom, "bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
             "algorithmic_flop_per_launch": dom_flops,
+            "traffic_gbs": None if traffic is None else round(traffic / (per[dom] * 1e-3) / 1e9, 1),
         },
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, dm, (q, k, v, do), args.cpu_rows)
+        rec["cpu_baseline"] = cpu_baseline(w, dm, (q, k, v, do), args.cpu_rows, args.cpu_kv_heads)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
