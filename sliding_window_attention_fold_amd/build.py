@@ -55,6 +55,11 @@ def build(jobs: int = 4) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # every kernel launch stub must resolve inside the library
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "_ZN2nb" in ln]
+    if nm.returncode != 0 or missing:
+        raise RuntimeError(f"link left library symbols undefined: {missing or nm.stderr}")
     os.replace(tmp, LIB)
     return LIB
 

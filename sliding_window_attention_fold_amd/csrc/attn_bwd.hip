@@ -111,13 +111,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   const T* kvq = reinterpret_cast<const T*>(p.q);
   const T* kvd = reinterpret_cast<const T*>(p.dout);
+  const TileDma<T, C::BQ, D, C::NW> dma;   // Q and dO tiles share one layout
   auto load = [&](T* Qs, T* Gs, float* ls, float* ds, int* ks, int it) {
     const int hh = it / n_t, t = t_first + it % n_t;
     const int i0 = t * C::BQ;
     const int nr = min(C::BQ, p.L - i0);
     const size_t rb = ((size_t)b * p.Hq + kvh * grp + hh) * p.L + i0;
-    dma_tile<T, C::BQ, D, C::NW>(Qs, kvq + rb * D, nr);
-    dma_tile<T, C::BQ, D, C::NW>(Gs, kvd + rb * D, nr);
+    dma.issue(Qs, kvq + rb * D, nr);
+    dma.issue(Gs, kvd + rb * D, nr);
     if (w == 0) dma_words(ls, p.lse + rb, nr);
     if (w == 1) dma_words(ds, p.delta + rb, nr);
     if (w == 2) dma_words(ks, p.row_klo + (size_t)b * p.L + i0, nr);
@@ -326,10 +327,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
 
   const T* __restrict__ kbase = reinterpret_cast<const T*>(p.k) + ((size_t)b * p.Hkv + kvh) * p.S * D;
   const T* __restrict__ vbase = reinterpret_cast<const T*>(p.v) + ((size_t)b * p.Hkv + kvh) * p.S * D;
+  const TileDma<T, C::BN, D, C::NW> dma;   // K and V tiles share one layout
   auto load = [&](T* Ks, T* Vs, int j0) {
     const int nv = min(C::BN, p.S - j0);
-    dma_tile<T, C::BN, D, C::NW>(Ks, kbase + (size_t)j0 * D, nv);
-    dma_tile<T, C::BN, D, C::NW>(Vs, vbase + (size_t)j0 * D, nv);
+    dma.issue(Ks, kbase + (size_t)j0 * D, nv);
+    dma.issue(Vs, vbase + (size_t)j0 * D, nv);
   };
   if (kstart < kend) load(K0, V0, kstart);
 

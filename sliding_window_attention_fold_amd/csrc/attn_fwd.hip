@@ -89,10 +89,11 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdP
   const T* __restrict__ kbase = reinterpret_cast<const T*>(p.k) + ((size_t)b * p.Hkv + kvh) * p.S * D;
   const T* __restrict__ vbase = reinterpret_cast<const T*>(p.v) + ((size_t)b * p.Hkv + kvh) * p.S * D;
 
+  const TileDma<T, C::BN, D, C::NW> dma;   // K and V tiles share one layout
   auto load = [&](T* Ks, T* Vs, int j0) {
     const int nv = min(C::BN, p.S - j0);
-    dma_tile<T, C::BN, D, C::NW>(Ks, kbase + (size_t)j0 * D, nv);
-    dma_tile<T, C::BN, D, C::NW>(Vs, vbase + (size_t)j0 * D, nv);
+    dma.issue(Ks, kbase + (size_t)j0 * D, nv);
+    dma.issue(Vs, vbase + (size_t)j0 * D, nv);
   };
   if (kstart < kend) load(K0, V0, kstart);
 

@@ -160,8 +160,8 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 // ---------------------------------------------------------------------------
 // LDS tiles.  A tile holds ROWS rows of a row-major [*, D] matrix, row-major in
 // LDS with no padding; the 16-byte chunks of each row are XOR-swizzled by a
-// function of the row so that the 32 rows an MFMA operand read touches, and
-// the 4 rows a transpose read touches, fall on different banks.
+// function of the row (period 16 rows) so that both the row reads of an MFMA
+// operand and the transpose reads are free of bank conflicts.
 // ---------------------------------------------------------------------------
 template <typename T, int ROWS, int D>
 struct Tile {
@@ -171,7 +171,15 @@ struct Tile {
   static constexpr int BLOCKS = ROWS * CPR / 64; // 1 KB blocks (one DMA instruction each)
   static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0, "row must be >= 8 power-of-two chunks");
   static_assert(ROWS * CPR % 64 == 0, "tile must be whole 1 KB blocks");
-  __device__ static __forceinline__ int swz(int r) { return ((2 * (r & 7)) | ((r >> 3) & 1)) & (CPR - 1); }
+  // LDS has 64 banks of 4 bytes.  A 16-byte row read serves 16 lanes per
+  // cycle (rows r..r+15 at one chunk): swz must be a bijection on 16
+  // consecutive rows.  A transpose read serves 32 lanes per cycle (4
+  // consecutive rows x one aligned 64-byte group of 4 chunks): the 4 rows must
+  // land on different 4-chunk groups.  Rows of 8 chunks (128 bytes) pair up
+  // per 256-byte bank line, hence the separate form.
+  __device__ static __forceinline__ constexpr int swz(int r) {
+    return CPR >= 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
   // element offset of logical chunk lc of row r
   __device__ static __forceinline__ int off(int r, int lc) { return r * D + ((lc ^ swz(r)) * EPC); }
 };
@@ -199,39 +207,56 @@ __device__ __forceinline__ void dma_tile(T* lds, const T* __restrict__ src, int 
   }
 }
 
-// The same copy with this lane's per-block offsets computed once: issuing a
-// tile then costs one uniform base (SGPRs) plus a precomputed 32-bit offset
-// per block.  Rows at or beyond nrows repeat row nrows-1 (uniform slow path).
+// The same copy through a buffer resource: the tile's base lives in scalar
+// registers and each lane keeps the byte offsets of its chunks (loop
+// invariant), so issuing a full tile costs one instruction per 1 KB block and
+// no vector arithmetic.  Rows at or beyond nrows repeat row nrows-1 (uniform
+// slow path for the last, partial tile).
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
 template <typename T, int ROWS, int D, int NW>
-struct DmaPlan {
+struct TileDma {
   typedef Tile<T, ROWS, D> TL;
-  static_assert(TL::BLOCKS % NW == 0, "tile blocks must split evenly over the waves");
-  static constexpr int PER = TL::BLOCKS / NW;
-  int goff[PER];  // element offset of this lane's chunk within a full tile
-  __device__ __forceinline__ DmaPlan() {
+  static constexpr int PER = (TL::BLOCKS + NW - 1) / NW;
+  static constexpr int RB = D * (int)sizeof(T);  // row bytes
+  uint32_t voff[PER];
+  __device__ __forceinline__ TileDma() {
     const int w = wave_id(), l = threadIdx.x & 63;
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
       const int P = (w + x * NW) * 64 + l;
       const int r = P / TL::CPR, pc = P % TL::CPR;
-      goff[x] = r * D + (pc ^ TL::swz(r)) * TL::EPC;
+      voff[x] = (uint32_t)(r * RB + ((pc ^ TL::swz(r)) * 16));
     }
   }
   __device__ __forceinline__ void issue(T* lds, const T* __restrict__ src, int nrows) const {
+    // The buffer-resource type exists only for the device target; the host
+    // pass (which only needs the kernels' launch stubs) sees an empty body.
+#if defined(__HIP_DEVICE_COMPILE__)
     const int w = wave_id(), l = threadIdx.x & 63;
+    typedef __attribute__((address_space(3))) void lds_void;
     if (nrows >= ROWS) {
-#pragma unroll
-      for (int x = 0; x < PER; ++x)
-        __builtin_amdgcn_global_load_lds(NB_GLOBAL(src + goff[x]), NB_LOCAL(lds + (w + x * NW) * 64 * TL::EPC),
-                                         16, 0, 0);
-    } else {
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, ROWS * RB, kBufferWord3);
 #pragma unroll
       for (int x = 0; x < PER; ++x) {
-        const int r = ((w + x * NW) * 64 + l) / TL::CPR;
-        const int o = goff[x] + (min(r, nrows - 1) - r) * D;
-        __builtin_amdgcn_global_load_lds(NB_GLOBAL(src + o), NB_LOCAL(lds + (w + x * NW) * 64 * TL::EPC), 16, 0, 0);
+        const int blk = w + x * NW;
+        if (TL::BLOCKS % NW == 0 || blk < TL::BLOCKS)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + blk * 64 * TL::EPC), 16, voff[x], 0, 0, 0);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nrows * RB, kBufferWord3);
+#pragma unroll
+      for (int x = 0; x < PER; ++x) {
+        const int blk = w + x * NW;
+        const int r = (blk * 64 + l) / TL::CPR;
+        const uint32_t o = voff[x] - (uint32_t)((r - min(r, nrows - 1)) * RB);
+        if (TL::BLOCKS % NW == 0 || blk < TL::BLOCKS)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + blk * 64 * TL::EPC), 16, o, 0, 0, 0);
       }
     }
+#endif
   }
 };
 
