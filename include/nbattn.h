@@ -151,7 +151,9 @@ int nb_attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_re
                 int window_left, float dropout_p, int dtype, void* ws, size_t ws_bytes,
                 void* stream);
 
-/* Bytes of workspace nb_attn_bwd needs (Delta rows: B * Hq * L floats, aligned). */
+/* Bytes of workspace nb_attn_bwd needs: the Delta rows (B * Hq * L floats)
+ * and the dK/dV work order (B * ceil(S / 32) ints), each 256-byte aligned.
+ * Returns 0 for non-positive sizes. */
 size_t nb_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, int dtype);
 
 /*

@@ -18,12 +18,15 @@
 //      publishes it for pass 2;
 //   2. dK/dV:  one workgroup per (128 keys, kv head, batch row): four key groups
 //      of 32 keys, each served by a pair of waves (K side: S, P, dV; V side:
-//      dP, dS, dK; P crosses through LDS).  The loop runs over the group's q
+//      dP, dS, dK; P crosses through LDS).  A one-workgroup pre-pass orders
+//      the key tiles by decreasing work so the longest start first.  The loop runs over the group's q
 //      heads and the 32-row query tiles whose bands reach the keys.  Q and dO
 //      tiles (plus their rows' LSE, Delta, band start) are copied into LDS
 //      asynchronously and read row-wise (A operands of S and dP) and transposed
 //      (A operands of dV^T and dK^T).  Keys no query attends come out as exact 0.
 #include <math.h>
+
+#include <algorithm>
 
 #include "nb_device.h"
 #include "nb_kernels.h"
@@ -32,7 +35,7 @@ namespace nb {
 
 // ---------------------------------------------------------------- dK / dV
 
-// Eight waves: four key groups of 32 keys, two roles per group.  Role A holds
+// NKG key groups of 32 keys, two waves (roles) per group.  Role A holds
 // the group's K rows, forms S = Q K^T and P, hands P to its partner through LDS
 // and accumulates dV^T = dO^T P; role B holds the V rows, forms dP = dO V^T,
 // takes P, forms dS = P (dP - Delta) and accumulates dK^T = Q^T dS.  Splitting
@@ -41,14 +44,19 @@ namespace nb {
 // latency; the matrix-core work is the same as one wave doing both.
 template <typename T, int D>
 struct DkvCfg {
-  static constexpr int NW = 8;
+  static constexpr int NKG = 4;        // key groups of 32 keys
+  static constexpr int NW = 2 * NKG;
   static constexpr int NT = 64 * NW;
-  static constexpr int BK = 128;       // keys per workgroup
+  static constexpr int BK = 32 * NKG;  // keys per workgroup
   static constexpr int BQ = 32;        // query rows per step
+  static constexpr int OCC = 1;        // workgroups per CU
+  // operand fragments read ahead of their MFMA; 0 = plain loop (D = 256 and the
+  // float path have no registers to spare)
+  static constexpr int AHEAD = (D <= 128 && sizeof(T) == 2) ? 4 : 0;
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__((DkvCfg<T, D>::NT), (DkvCfg<T, D>::OCC)) void bwd_dkdv_kernel(BwdParams p) {
   typedef DkvCfg<T, D> C;
   typedef Tile<T, C::BQ, D> TL;
   typedef typename Frag<T>::type F;
@@ -60,24 +68,38 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) float lse0[64], lse1[64], dl0[64], dl1[64];
   __shared__ __attribute__((aligned(256))) int klo0[64], klo1[64];
   // P handed from role A to role B: [key group][value quad][lane][4]
-  __shared__ __attribute__((aligned(256))) f32x4 pex[4][4][64];
-  __shared__ int n_tiles_s;
+  __shared__ __attribute__((aligned(256))) f32x4 pex[C::NKG][4][64];
+  __shared__ int n_tiles_s, item_s;
 
-  // Work order: the kv group (batch row, kv head) varies fastest (one XCD per
-  // group with 8 XCDs, so the Q/dO rows neighbouring key tiles share stay in its
-  // L2); key tiles run from the end of the neighbourhood backwards, so the
-  // cheap tiles no query reaches (the beginning) are dispatched last and fill
-  // the tail.
+  // Work distribution: a persistent grid (one workgroup per CU slot) pulls
+  // items (kv head, batch row, key tile) from NQ queues; workgroup w serves
+  // queue w % NQ, which holds the flat items f = q, q + NQ, ...  Flat items
+  // list the kv head fastest over the (batch row, key tile) pairs in the order
+  // of decreasing work computed by dkdv_order_kernel, so with 8 queues (one
+  // per XCD, as consecutive workgroups land on consecutive XCDs) each kv head
+  // stays on one XCD, whose L2 then holds the Q/dO rows its key tiles share,
+  // and each XCD runs its longest tiles first.  Which workgroup computes an
+  // item never changes the result.
   const int grp = p.Hq / p.Hkv;
-  const int ngroups = p.B * p.Hkv;
   const int n_kt = (p.S + C::BK - 1) / C::BK;
-  const int gid = blockIdx.x % ngroups;
-  const int b = gid / p.Hkv, kvh = gid % p.Hkv;
-  const int kt = n_kt - 1 - (int)(blockIdx.x / ngroups);
+  const int total = p.B * n_kt * p.Hkv;
+  const int nq = min(kNumQueues, (int)gridDim.x);
+  const int qcls = blockIdx.x % nq;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
-  const int kg = w & 3;                           // key group
-  const bool role_a = w < 4;                      // A: S, P, dV   B: dP, dS, dK
+  const int kg = w % C::NKG;                      // key group
+  const bool role_a = w < C::NKG;                 // A: S, P, dV   B: dP, dS, dK
   const int off = p.S - p.L;
+  const TileAccess<T, TL> acc(ln, lane);
+  const TileDma<T, C::BQ, D, C::NW> dma;   // Q and dO tiles share one layout
+
+  for (;;) {
+  if (tid == 0) item_s = qcls + nq * atomicAdd(&p.counters[qcls], 1);
+  __syncthreads();
+  const int f = item_s;
+  if (f >= total) break;
+  const int kvh = f % p.Hkv;
+  const int code = p.order[f / p.Hkv];
+  const int b = code / n_kt, kt = code % n_kt;
   const int j0 = kt * C::BK;                      // first key of the workgroup
   const int jw = j0 + 32 * kg;                    // first key of the group
   const int j = jw + ln;                          // this lane's key (C column / B operand)
@@ -111,7 +133,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   const T* kvq = reinterpret_cast<const T*>(p.q);
   const T* kvd = reinterpret_cast<const T*>(p.dout);
-  const TileDma<T, C::BQ, D, C::NW> dma;   // Q and dO tiles share one layout
   auto load = [&](T* Qs, T* Gs, float* ls, float* ds, int* ks, int it) {
     const int hh = it / n_t, t = t_first + it % n_t;
     const int i0 = t * C::BQ;
@@ -134,7 +155,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) kv[kk] = load_frag<T>(src + 16 * kk + 8 * g);
   }
-  const TileAccess<T, TL> acc(ln, lane);
   f32x16 gacc[D / 32];   // dV^T (role A) or dK^T (role B) of the group's keys
 #pragma unroll
   for (int d = 0; d < D / 32; ++d) gacc[d] = f32x16{};
@@ -149,7 +169,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
       const int bq = max(0, ks[qi]);
       return p.window >= 0 ? max(bq, off + i0 + qi - p.window) : bq;
     };
-    const int bs_min = band(0), bs_max = band(nrows - 1);
+    // (uniform values; readfirstlane lets the compiler branch on the scalar unit)
+    const int bs_min = __builtin_amdgcn_readfirstlane(band(0));
+    const int bs_max = __builtin_amdgcn_readfirstlane(band(nrows - 1));
     const bool active = !(jw > p_max || jw + 31 < bs_min);
     // every (row, key) pair of the group inside the band: no element mask
     const bool full = (nrows == C::BQ) && jw >= bs_max && jw + 31 <= p_min;
@@ -158,18 +180,32 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
     f32x16 sacc = f32x16{};
     if (active) {
       const T* src = role_a ? Qs : Gs;
+      if constexpr (C::AHEAD > 0) {
+        lds_mfma_pipeline<D / 16, C::AHEAD, F>([&](int kk) { return acc.row(src, 0, kk); },
+                                               [&](int kk, const F& a) { sacc = mma(a, kv[kk], sacc); });
+      } else {
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) sacc = mma(acc.row(src, 0, kk), kv[kk], sacc);
+        for (int kk = 0; kk < D / 16; ++kk) sacc = mma(acc.row(src, 0, kk), kv[kk], sacc);
+      }
       if (role_a) {
         // accumulator r: query row acc_row(r, g) of the tile, key j
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = acc_row(r, g);
-          float pr = fast_exp2(fmaf(sacc[r], p.scale_log2, -ls[qi] * kLog2e));
+        for (int rq = 0; rq < 4; ++rq) {
+          // rows 8*rq + 4*g + e: their LSE (and band starts) as one 16-byte read
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + 8 * rq + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sacc[4 * rq + e] = fast_exp2(fmaf(sacc[4 * rq + e], p.scale_log2, -l4[e] * kLog2e));
           if (!full) {
-            if (qi >= nrows || j < band(qi) || j > off + i0 + qi) pr = 0.f;
+            const int4 k4 = *reinterpret_cast<const int4*>(ks + 8 * rq + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int qi = 8 * rq + 4 * g + e;
+              int bq = max(0, k4[e]);
+              if (p.window >= 0) bq = max(bq, off + i0 + qi - p.window);
+              const bool in = (qi < nrows) & (j >= bq) & (j <= off + i0 + qi);
+              sacc[4 * rq + e] = in ? sacc[4 * rq + e] : 0.f;
+            }
           }
-          sacc[r] = pr;
         }
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd)
@@ -183,19 +219,25 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         const f32x4 pq = pex[kg][qd][lane];
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds + 8 * qd + 4 * g);  // rows acc_row(4*qd + e, g)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * qd + e;
-          sacc[r] = pq[e] * (sacc[r] - ds[acc_row(r, g)]);
-        }
+        for (int e = 0; e < 4; ++e) sacc[4 * qd + e] = pq[e] * (sacc[4 * qd + e] - d4[e]);
       }
     }
     const T* src = role_a ? Gs : Qs;
+    if constexpr (C::AHEAD > 0) {
+      const F sf[2] = {acc_to_frag<T>(sacc, 0), acc_to_frag<T>(sacc, 1)};
+      constexpr int ND = D / 32;
+      lds_mfma_pipeline<2 * ND, C::AHEAD, F>(
+          [&](int x) { return acc.col(src, x % ND, x / ND); },
+          [&](int x, const F& a) { gacc[x % ND] = mma(a, sf[x / ND], gacc[x % ND]); });
+    } else {
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const F sf = acc_to_frag<T>(sacc, m);
+      for (int m = 0; m < 2; ++m) {
+        const F sf = acc_to_frag<T>(sacc, m);
 #pragma unroll
-      for (int d = 0; d < D / 32; ++d) gacc[d] = mma(acc.col(src, d, m), sf, gacc[d]);
+        for (int d = 0; d < D / 32; ++d) gacc[d] = mma(acc.col(src, d, m), sf, gacc[d]);
+      }
     }
   };
 
@@ -213,16 +255,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
     step(Q1, G1, lse1, dl1, klo1, it + 1);
   }
 
-  if (j >= p.S) return;
-  T* dst = reinterpret_cast<T*>(role_a ? p.dv : p.dk) + (((size_t)b * p.Hkv + kvh) * p.S + j) * D;
-  const float f = role_a ? 1.f : p.scale;
+  if (j < p.S) {
+    T* dst = reinterpret_cast<T*>(role_a ? p.dv : p.dk) + (((size_t)b * p.Hkv + kvh) * p.S + j) * D;
+    const float sc = role_a ? 1.f : p.scale;
 #pragma unroll
-  for (int d = 0; d < D / 32; ++d) {
+    for (int d = 0; d < D / 32; ++d) {
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      store_quad<T>(dst + 32 * d + 8 * rq + 4 * g, gacc[d][4 * rq] * f, gacc[d][4 * rq + 1] * f,
-                    gacc[d][4 * rq + 2] * f, gacc[d][4 * rq + 3] * f);
+      for (int rq = 0; rq < 4; ++rq) {
+        store_quad<T>(dst + 32 * d + 8 * rq + 4 * g, gacc[d][4 * rq] * sc, gacc[d][4 * rq + 1] * sc,
+                      gacc[d][4 * rq + 2] * sc, gacc[d][4 * rq + 3] * sc);
+      }
     }
+  }
+  // every wave is done with this item's LDS buffers and item_s before the next fetch
+  __syncthreads();
   }
 }
 
@@ -281,11 +327,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     if (p.window >= 0) bs = max(bs, pos - p.window);
   }
   const bool real = in_range && bs <= pos;
-  const int w_lo = wave_min_i(real ? bs : INT_MAX);
-  const int w_hi = wave_max_i(real ? pos + 1 : INT_MIN);
-  const int w_bs_max = wave_max_i(real ? bs : INT_MIN);
-  const int w_p_min = wave_min_i(real ? pos : INT_MAX);
-  const bool w_all_real = wave_min_i(real ? 1 : 0) != 0;
+  // (uniform; readfirstlane makes the tile decisions scalar branches)
+  const int w_lo = __builtin_amdgcn_readfirstlane(wave_min_i(real ? bs : INT_MAX));
+  const int w_hi = __builtin_amdgcn_readfirstlane(wave_max_i(real ? pos + 1 : INT_MIN));
+  const int w_bs_max = __builtin_amdgcn_readfirstlane(wave_max_i(real ? bs : INT_MIN));
+  const int w_p_min = __builtin_amdgcn_readfirstlane(wave_min_i(real ? pos : INT_MAX));
+  const bool w_all_real = __builtin_amdgcn_readfirstlane(wave_min_i(real ? 1 : 0)) != 0;
   if (lane == 0) { red[w][0] = w_lo; red[w][1] = w_hi; }
 
   const size_t qrow = ((size_t)b * p.Hq + h) * p.L + i;
@@ -362,7 +409,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
             float pr = fast_exp2(fmaf(sacc[sb][r], p.scale_log2, -lse2));
             if (!full) {
               const int jj = j0 + 32 * sb + acc_row(r, g);
-              if (!real || jj < bs || jj > pos) pr = 0.f;
+              if ((!real) | (jj < bs) | (jj > pos)) pr = 0.f;
             }
             sacc[sb][r] = pr;
           }
@@ -430,6 +477,75 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- launch
 
+// ---------------------------------------------------------------- dK/dV work order
+
+// Items (batch row, key tile) sorted by decreasing work -- the number of
+// 32-row query tiles whose bands reach the tile, counted exactly as the dK/dV
+// kernel counts them -- with ties in decreasing tile order.  One workgroup:
+// exact counts by binary search over the nondecreasing band starts, then a
+// bitonic sort of (work, index) keys in LDS.  More than kOrderMax items keep
+// the natural order.
+constexpr int kOrderNT = 1024;
+constexpr int kOrderMax = 8192;
+
+template <int BK, int BQ>
+__global__ __launch_bounds__(kOrderNT) void dkdv_order_kernel(BwdParams p) {
+  __shared__ unsigned long long keys[kOrderMax];
+  const int tid = threadIdx.x;
+  const int n_kt = (p.S + BK - 1) / BK;
+  const int n = p.B * n_kt;
+  if (tid < kNumQueues) p.counters[tid] = 0;  // the dK/dV pass's work queues start empty
+  if (n > kOrderMax) {
+    for (int i = tid; i < n; i += kOrderNT) p.order[i] = i;
+    return;
+  }
+  const int off = p.S - p.L;
+  const int n_q_tiles = (p.L + BQ - 1) / BQ;
+  int N = 1;
+  while (N < n) N <<= 1;
+  for (int i = tid; i < N; i += kOrderNT) {
+    unsigned long long key = ~0ull;  // padding sorts last
+    if (i < n) {
+      const int b = i / n_kt, kt = i % n_kt;
+      const int jmax = min(kt * BK + BK, p.S) - 1;
+      const int t_first = max(0, kt * BK - off) / BQ;
+      auto band_start = [&](int t) {
+        const int r = t * BQ;
+        const int bq = max(0, p.row_klo[(size_t)b * p.L + r]);
+        return p.window >= 0 ? max(bq, off + r - p.window) : bq;
+      };
+      int lo = t_first, hi = n_q_tiles;  // first tile in [lo, hi) whose band starts after jmax
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (band_start(mid) <= jmax) lo = mid + 1;
+        else hi = mid;
+      }
+      const unsigned work = (unsigned)(lo - t_first);
+      key = ((unsigned long long)(0xFFFFFFFFu - work) << 32) | (unsigned)(n - 1 - i);
+    }
+    keys[i] = key;
+  }
+  __syncthreads();
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < N; i += kOrderNT) {
+        const int l = i ^ j;
+        if (l > i) {
+          const unsigned long long a = keys[i], c = keys[l];
+          if ((a > c) == ((i & k) == 0)) {
+            keys[i] = c;
+            keys[l] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < n; i += kOrderNT) p.order[i] = n - 1 - (int)(unsigned)(keys[i] & 0xFFFFFFFFu);
+}
+
+size_t dkdv_order_elems(int B, int S) { return (size_t)B * ((S + 31) / 32); }
+
 template <typename T, int D>
 static hipError_t launch_dq_t(const BwdParams& p, hipStream_t s) {
   typedef DqCfg<T, D> C;
@@ -441,7 +557,17 @@ static hipError_t launch_dq_t(const BwdParams& p, hipStream_t s) {
 template <typename T, int D>
 static hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t s) {
   typedef DkvCfg<T, D> C;
-  dim3 grid((unsigned)((p.S + C::BK - 1) / C::BK) * p.Hkv * p.B);
+  static_assert(C::BK >= 32, "the work-order array is sized for tiles of at least 32 keys");
+  hipLaunchKernelGGL((dkdv_order_kernel<C::BK, C::BQ>), dim3(1), dim3(kOrderNT), 0, s, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // persistent grid: one workgroup per CU slot, at most one per item
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+    n_cu = 256;
+  const long long items = (long long)((p.S + C::BK - 1) / C::BK) * p.Hkv * p.B;
+  dim3 grid((unsigned)std::min<long long>(items, (long long)n_cu * C::OCC));
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), grid, dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }

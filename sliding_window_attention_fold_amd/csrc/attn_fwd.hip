@@ -38,6 +38,10 @@ struct FwdCfg {
   static constexpr int BM = 32 * NW;
   static constexpr int BN = (D <= 128) ? 64 : 32;  // keys per tile
   static constexpr int OCC = (sizeof(T) == 2) ? 2 : 1;  // workgroups per CU
+  // operand fragments read ahead of their MFMA (fewer at D = 256, where the
+  // Q fragments and O accumulators leave little room)
+  static constexpr int AHEAD_S = (D <= 128) ? 4 : 2;
+  static constexpr int AHEAD_PV = (D <= 128) ? 3 : 2;
 };
 
 template <typename T, int D>
@@ -74,11 +78,13 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdP
   const bool real = in_range && bs <= pos;
 
   // Key range of the wave and of the workgroup (union of the rows' bands).
-  const int w_lo = wave_min_i(real ? bs : INT_MAX);
-  const int w_hi = wave_max_i(real ? pos + 1 : INT_MIN);
-  const int w_bs_max = wave_max_i(real ? bs : INT_MIN);
-  const int w_p_min = wave_min_i(real ? pos : INT_MAX);
-  const bool w_all_real = wave_min_i(real ? 1 : 0) != 0;
+  // (wave reductions are uniform; readfirstlane lets the compiler see it, so
+  // the tile decisions below are scalar branches)
+  const int w_lo = __builtin_amdgcn_readfirstlane(wave_min_i(real ? bs : INT_MAX));
+  const int w_hi = __builtin_amdgcn_readfirstlane(wave_max_i(real ? pos + 1 : INT_MIN));
+  const int w_bs_max = __builtin_amdgcn_readfirstlane(wave_max_i(real ? bs : INT_MIN));
+  const int w_p_min = __builtin_amdgcn_readfirstlane(wave_min_i(real ? pos : INT_MAX));
+  const bool w_all_real = __builtin_amdgcn_readfirstlane(wave_min_i(real ? 1 : 0)) != 0;
   if (lane == 0) { red[w][0] = w_lo; red[w][1] = w_hi; }
   __syncthreads();
   int kstart = INT_MAX, kend = INT_MIN;
@@ -121,13 +127,12 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdP
     if (j0 >= w_hi || j0 + C::BN <= w_lo) return;
     const bool full = w_all_real && j0 >= w_bs_max && j0 + C::BN - 1 <= w_p_min;
     f32x16 sacc[C::BN / 32];
+    constexpr int NK = D / 16;
 #pragma unroll
-    for (int sb = 0; sb < C::BN / 32; ++sb) {
-      sacc[sb] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) sacc[sb] = mma(acc.row(Ks, sb, kk), qf[kk], sacc[sb]);
-    }
-    if constexpr (sizeof(T) == 2) interleave_lds_mfma<C::BN / 32 * D / 16, 1>();
+    for (int sb = 0; sb < C::BN / 32; ++sb) sacc[sb] = f32x16{};
+    lds_mfma_pipeline<C::BN / 32 * NK, C::AHEAD_S, F>(
+        [&](int x) { return acc.row(Ks, x / NK, x % NK); },
+        [&](int x, const F& a) { sacc[x / NK] = mma(a, qf[x % NK], sacc[x / NK]); });
     float tmax = -INFINITY;
 #pragma unroll
     for (int sb = 0; sb < C::BN / 32; ++sb) {
@@ -136,7 +141,7 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdP
         float x = sacc[sb][r] * p.scale_log2;
         if (!full) {
           const int j = j0 + 32 * sb + acc_row(r, g);
-          if (j < bs || j > pos) x = -INFINITY;
+          if ((j < bs) | (j > pos)) x = -INFINITY;
         }
         sacc[sb][r] = x;
         tmax = fmaxf(tmax, x);
@@ -163,13 +168,13 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdP
         l_run += e;
       }
     }
+    F pf[C::BN / 16];
 #pragma unroll
-    for (int m = 0; m < C::BN / 16; ++m) {
-      const F pf = acc_to_frag<T>(sacc[m >> 1], m & 1);
-#pragma unroll
-      for (int d = 0; d < D / 32; ++d) oacc[d] = mma(acc.col(Vs, d, m), pf, oacc[d]);
-    }
-    if constexpr (sizeof(T) == 2) interleave_lds_mfma<C::BN / 16 * D / 32, 2>();
+    for (int m = 0; m < C::BN / 16; ++m) pf[m] = acc_to_frag<T>(sacc[m >> 1], m & 1);
+    constexpr int ND = D / 32;
+    lds_mfma_pipeline<C::BN / 16 * ND, C::AHEAD_PV, F>(
+        [&](int x) { return acc.col(Vs, x % ND, x / ND); },
+        [&](int x, const F& a) { oacc[x % ND] = mma(a, pf[x / ND], oacc[x % ND]); });
   };
 
   // Double-buffered key loop: the DMA of the next tile is issued right after

@@ -280,6 +280,42 @@ __device__ __forceinline__ void interleave_lds_mfma() {
   }
 }
 
+// Software-pipelined form: the first AHEAD groups of R reads are issued up
+// front, then each MFMA is followed by the reads AHEAD MFMAs ahead of it, so
+// the LDS latency of an operand is covered by the MFMAs issued in between.
+template <int N, int R, int AHEAD>
+__device__ __forceinline__ void pipeline_lds_mfma() {
+  static_assert(AHEAD >= 1 && AHEAD <= N, "read-ahead must be within the product");
+  __builtin_amdgcn_sched_group_barrier(0x100, R * AHEAD, 0);
+#pragma unroll
+  for (int x = 0; x < N - AHEAD; ++x) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
+// Explicit software pipeline of N (operand read, MFMA) pairs: the reads of
+// the first A operands are issued up front and each MFMA k is issued together
+// with the read of operand k + A.  Scheduling barriers pin that order, so an
+// operand's LDS latency is covered by the A MFMAs issued before its use; A + 1
+// fragments are live at a time.
+template <int N, int A, typename F, typename ReadFn, typename MmaFn>
+__device__ __forceinline__ void lds_mfma_pipeline(ReadFn&& rd, MmaFn&& mm) {
+  static_assert(A >= 1 && A <= N, "read-ahead must be within the product");
+  F buf[A];
+#pragma unroll
+  for (int x = 0; x < A; ++x) buf[x] = rd(x);
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    __builtin_amdgcn_sched_barrier(0);
+    const F cur = buf[k % A];
+    if (k + A < N) buf[k % A] = rd(k + A);
+    mm(k, cur);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Wait until this wave's global reads (including copies into LDS) have landed.
 __device__ __forceinline__ void wait_global() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 

@@ -45,6 +45,8 @@ struct BwdParams {
   const void* dout;
   const float* lse;
   float* delta;
+  int* order;        // workspace: dK/dV key tiles (b * n_tiles + tile) by decreasing work
+  int* counters;     // workspace: kNumQueues work-queue counters of the dK/dV pass
   const int32_t* row_klo;
   void* dq;
   void* dk;
@@ -67,6 +69,10 @@ hipError_t launch_segment_build(const SegParams& p, hipStream_t s);
 hipError_t launch_attn_fwd(const FwdParams& p, int D, bool f32, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdParams& p, int D, bool f32, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int D, bool f32, hipStream_t s);
+// Elements of the dK/dV work-order array for (B, S) (enough for the smallest
+// key tile), followed in the workspace by kNumQueues queue counters.
+size_t dkdv_order_elems(int B, int S);
+constexpr int kNumQueues = 8;
 hipError_t launch_owner_flags(const OwnerParams& p, hipStream_t s);
 
 }  // namespace nb

@@ -136,14 +136,17 @@ int nb_attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_re
   return map_hip(nb::launch_attn_fwd(p, D, dtype == NB_F32, (hipStream_t)stream));
 }
 
+namespace {
+size_t delta_bytes(int B, int Hq, int L) { return (((size_t)B * Hq * L * sizeof(float)) + 255) & ~(size_t)255; }
+}  // namespace
+
 size_t nb_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, int dtype) {
   (void)Hkv;
-  (void)S;
   (void)D;
   (void)dtype;
-  if (B < 1 || Hq < 1 || L < 1) return 0;
-  const size_t delta = (size_t)B * Hq * L * sizeof(float);
-  return (delta + 255) & ~(size_t)255;
+  if (B < 1 || Hq < 1 || L < 1 || S < 1) return 0;
+  const size_t order = ((nb::dkdv_order_elems(B, S) + nb::kNumQueues) * sizeof(int) + 255) & ~(size_t)255;
+  return delta_bytes(B, Hq, L) + order;
 }
 
 }  // extern "C"
@@ -162,6 +165,8 @@ nb::BwdParams bwd_params(const void* dout, const void* q, const void* k, const v
   p.dout = dout;
   p.lse = lse;
   p.delta = reinterpret_cast<float*>(ws);
+  p.order = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + delta_bytes(B, Hq, L));
+  p.counters = p.order + nb::dkdv_order_elems(B, S);
   p.row_klo = seg_buf + nb::seg_layout(B, L, S).row_klo;
   p.dq = dq;
   p.dk = dk;
