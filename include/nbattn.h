@@ -79,7 +79,7 @@ int nb_version(void);
  *   row_klo[N]         first key of that row's segment (neighbourhood position);
  *                      p + 1 for padding rows (an empty key range)
  *   kcov_lo[B]         first covered key of batch row b (S if none)
- *   scratch            builder-private (duplicate-id detection)
+ *   scratch            builder-private (per-tile records, duplicate-id set)
  * Entries past n_seg (past n_seg + 1 for cu_q / cu_k) are unspecified.
  * ------------------------------------------------------------------------ */
 #define NB_SEG_HEADER 16
@@ -117,7 +117,8 @@ size_t nb_segment_buffer_elems(int B, int L, int S);
  *   doc_ids    [B,S] int32 device, neighbourhood doc map
  *   pad_mask   [B,S] uint8 device, nonzero = padding, or NULL
  *   folded_ids [B,S] int32 device, out: doc_ids with padding set to 0
- *   seg_buf    device, out, seg_buf_elems >= nb_segment_buffer_elems(B, L, S)
+ *   seg_buf    device, out, 16-byte aligned,
+ *              seg_buf_elems >= nb_segment_buffer_elems(B, L, S)
  * Requires 1 <= L <= S, B >= 1.  Segments are valid by construction.
  */
 int nb_segment_build(const int32_t* doc_ids, const uint8_t* pad_mask, int B, int S, int L,

@@ -286,6 +286,8 @@ struct DqCfg {
   static constexpr int NT = 64 * NW;
   static constexpr int BM = 128;                    // query rows per workgroup
   static constexpr int BN = (D * sizeof(T) <= 256) ? 64 : 32;   // keys per tile
+  // operand fragments read ahead of their MFMA; 0 = plain loop (float path)
+  static constexpr int AHEAD = (sizeof(T) != 2) ? 0 : (D <= 128) ? 4 : 2;
 };
 
 template <typename T, int D>
@@ -394,11 +396,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     f32x16 sacc[NSB];
     if (active) {
       const T* src = role_a ? Ks : Vs;
+      constexpr int NK = D / 16;
 #pragma unroll
-      for (int sb = 0; sb < NSB; ++sb) {
-        sacc[sb] = f32x16{};
+      for (int sb = 0; sb < NSB; ++sb) sacc[sb] = f32x16{};
+      if constexpr (C::AHEAD > 0) {
+        lds_mfma_pipeline<NSB * NK, C::AHEAD, F>(
+            [&](int x) { return acc.row(src, x / NK, x % NK); },
+            [&](int x, const F& a) { sacc[x / NK] = mma(a, rf[x % NK], sacc[x / NK]); });
+      } else {
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) sacc[sb] = mma(acc.row(src, sb, kk), rf[kk], sacc[sb]);
+        for (int x = 0; x < NSB * NK; ++x) sacc[x / NK] = mma(acc.row(src, x / NK, x % NK), rf[x % NK], sacc[x / NK]);
       }
       if (role_a) {
         // accumulator r of block sb: key j0 + 32*sb + acc_row(r, g), query row i (this lane)
@@ -440,11 +447,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
         }
       }
     }
+    F sf[NM];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const F sf = acc_to_frag<T>(sacc[m >> 1], m & 1);
+    for (int m = 0; m < NM; ++m) sf[m] = acc_to_frag<T>(sacc[m >> 1], m & 1);
+    if constexpr (C::AHEAD > 0) {
+      lds_mfma_pipeline<NM * DH, C::AHEAD, F>(
+          [&](int x) { return acc.col(Ks, dh0 + x % DH, x / DH); },
+          [&](int x, const F& a) { dqacc[x % DH] = mma(a, sf[x / DH], dqacc[x % DH]); });
+    } else {
 #pragma unroll
-      for (int d = 0; d < DH; ++d) dqacc[d] = mma(acc.col(Ks, dh0 + d, m), sf, dqacc[d]);
+      for (int x = 0; x < NM * DH; ++x) dqacc[x % DH] = mma(acc.col(Ks, dh0 + x % DH, x / DH), sf[x / DH], dqacc[x % DH]);
     }
   };
 

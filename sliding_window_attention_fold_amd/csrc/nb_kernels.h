@@ -8,8 +8,10 @@
 namespace nb {
 
 struct SegLayout {
-  size_t cu_q, cu_k, q_row0, k_row0, row_seg, row_klo, kcov_lo, hash;
-  int hash_size;  // power of two >= 2 * S
+  size_t cu_q, cu_k, q_row0, k_row0, row_seg, row_klo, kcov_lo;
+  size_t tiles;   // builder scratch: per-tile records
+  size_t hash;    // builder scratch: (row, id) set, hash_size 8-byte entries
+  size_t hash_size;  // power of two >= 2 * B * S
 };
 
 SegLayout seg_layout(int B, int L, int S);

@@ -83,6 +83,7 @@ size_t nb_segment_buffer_elems(int B, int L, int S) {
 int nb_segment_build(const int32_t* doc_ids, const uint8_t* pad_mask, int B, int S, int L, int window_left,
                      int32_t* folded_ids, int32_t* seg_buf, size_t seg_buf_elems, void* stream) {
   if (doc_ids == nullptr || folded_ids == nullptr || seg_buf == nullptr) return NB_ERR_INVALID_ARG;
+  if (!aligned16(seg_buf)) return NB_ERR_INVALID_ARG;
   if (!dims_ok(B, L, S)) return NB_ERR_INVALID_ARG;
   if (seg_buf_elems < nb::seg_buffer_elems(B, L, S)) return NB_ERR_WORKSPACE;
   nb::SegParams p;

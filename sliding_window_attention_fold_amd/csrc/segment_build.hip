@@ -9,52 +9,65 @@
 // start .. last local row (bottom-right alignment), cu_seqlens_q[i] paired
 // with cu_seqlens_k[i].
 //
-// One workgroup of 1024 threads walks the batch rows in order and each row in
-// tiles of 8192 positions, carrying the running counts across tiles and rows,
-// so segment indices are global and ordered by (row, position) without any
-// host round trip.  Per position it needs the start of its run (a prefix max of
-// run starts) and, at the last position of a run reaching the query shard, the
-// running segment count, query-row count and key-length sum (prefix sums).
-// Duplicate document ids across separate runs of a row are detected with an
-// open-addressing set in the buffer's scratch area (status bit 0).
+// Three launches over tiles of 2048 positions of one batch row each:
+//   1. stats (one workgroup per tile): fold the padding, write the folded ids,
+//      clear the duplicate-id set, and reduce the tile to a few numbers -- its
+//      last run start, its segment ends (ends at or after the shard start),
+//      real query rows, and the key lengths / maxima of the segments whose run
+//      starts inside the tile; a segment end whose run began in an earlier
+//      tile (at most one per tile) is recorded by position;
+//   2. scan (one workgroup): in (row, tile) order, the run start carried into
+//      each tile (a segmented prefix max), the completed key lengths of the
+//      carried-in segments, and exclusive prefix sums of segment ends, query
+//      rows and key lengths; writes the header;
+//   3. emit (one workgroup per tile): per-position outputs and per-segment
+//      cu_seqlens / row offsets, from the tile's prefixes plus in-tile scans.
+//      Run starts are inserted into an open-addressing set keyed by (row, id)
+//      to detect an id that occurs in two separate runs (status bit 0).
+// Segment indices are global and ordered by (row, position).
+#include "../../include/nbattn.h"
 #include "nb_device.h"
 #include "nb_kernels.h"
 
 namespace nb {
 
 namespace {
-constexpr int SB_NT = 1024;
+constexpr int SB_NT = 256;
 constexpr int SB_ITEMS = 8;
 constexpr int SB_TILE = SB_NT * SB_ITEMS;
 constexpr int SB_WAVES = SB_NT / 64;
+constexpr int SC_NT = 1024;   // scan kernel
+constexpr int SC_WAVES = SC_NT / 64;
 
-// Exclusive block-wide scan (sum, or max when MX); `total` gets the block aggregate.
-template <bool MX>
-__device__ int block_excl_scan(int x, int* sh, int& total) {
+// Exclusive block-wide scan (sum, or max when MX) over NT threads; `total`
+// gets the block aggregate.  `sh` holds 2 * NT / 64 elements.
+template <bool MX, int NT, typename V>
+__device__ V block_excl_scan(V x, V* sh, V& total) {
+  constexpr int NWV = NT / 64;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int ident = MX ? INT_MIN : 0;
-  int v = x;
+  const V ident = MX ? (V)(sizeof(V) == 8 ? LLONG_MIN : INT_MIN) : (V)0;
+  V v = x;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(v, d);
+    const V y = __shfl_up(v, d);
     if (lane >= d) v = MX ? max(v, y) : v + y;
   }
   if (lane == 63) sh[wid] = v;
   __syncthreads();
   if (wid == 0) {
-    int t = lane < SB_WAVES ? sh[lane] : ident;
+    V t = lane < NWV ? sh[lane] : ident;
 #pragma unroll
-    for (int d = 1; d < SB_WAVES; d <<= 1) {
-      const int y = __shfl_up(t, d);
+    for (int d = 1; d < NWV; d <<= 1) {
+      const V y = __shfl_up(t, d);
       if (lane >= d) t = MX ? max(t, y) : t + y;
     }
-    if (lane < SB_WAVES) sh[SB_WAVES + lane] = t;
+    if (lane < NWV) sh[NWV + lane] = t;
   }
   __syncthreads();
-  const int before_wave = wid ? sh[SB_WAVES + wid - 1] : ident;
-  int before_lane = __shfl_up(v, 1);
+  const V before_wave = wid ? sh[NWV + wid - 1] : ident;
+  V before_lane = __shfl_up(v, 1);
   if (lane == 0) before_lane = ident;
-  total = sh[2 * SB_WAVES - 1];
+  total = sh[2 * NWV - 1];
   __syncthreads();
   return MX ? max(before_wave, before_lane) : before_wave + before_lane;
 }
@@ -66,23 +79,207 @@ __device__ __forceinline__ int folded_at(const SegParams& p, int b, int j) {
   return v;
 }
 
-// Insert a document id into the row's id set; returns true if it was present.
-__device__ bool id_seen_before(int* table, int mask, int id) {
-  uint32_t h = ((uint32_t)id * 2654435761u) & (uint32_t)mask;
+// Insert (row, id) into the set; returns true if it was present.  Entries are
+// (row + 1, id) pairs packed in 64 bits; 0 marks an empty slot.
+__device__ bool id_seen_before(unsigned long long* table, uint32_t mask, int row, int id) {
+  const unsigned long long key = ((unsigned long long)(unsigned)(row + 1) << 32) | (unsigned)id;
+  uint32_t h = ((uint32_t)id * 2654435761u + (uint32_t)row * 40503u) & mask;
   while (true) {
-    const int old = atomicCAS(&table[h], 0, id);
-    if (old == 0) return false;
-    if (old == id) return true;
+    const unsigned long long old = atomicCAS(&table[h], 0ull, key);
+    if (old == 0ull || old == key) return old == key;
     h = (h + 1) & (uint32_t)mask;
   }
 }
+
+// per-tile records in the scratch area (int32 each)
+enum { T_LAST_START, T_N_END, T_N_REALQ, T_KLEN_INT, T_MQ_INT, T_MK_INT, T_EXT_END, T_STAT };
+enum { P_START_BEFORE, P_SEG_BEFORE, P_Q_BEFORE, P_K_BEFORE, P_ROW_SEG0 };
+constexpr int kTileRec = 16;   // T_* in [0, 8), P_* in [8, 16)
+
+// Per-thread view of its SB_ITEMS positions: folded ids plus both neighbours.
+struct Span {
+  int f[SB_ITEMS];
+  int fprev, fnext, jb;
+};
+
+__device__ __forceinline__ void load_span(const SegParams& p, const int32_t* src, int b, int t0, Span& sp) {
+  sp.jb = t0 + threadIdx.x * SB_ITEMS;
+  const int32_t* row = src + (size_t)b * p.S;
+#pragma unroll
+  for (int u = 0; u < SB_ITEMS; ++u) sp.f[u] = (sp.jb + u < p.S) ? row[sp.jb + u] : 0;
+  sp.fprev = (sp.jb > 0 && sp.jb - 1 < p.S) ? row[sp.jb - 1] : 0;
+  sp.fnext = (sp.jb + SB_ITEMS < p.S) ? row[sp.jb + SB_ITEMS] : 0;
+}
 }  // namespace
 
-__global__ __launch_bounds__(SB_NT) void segment_build_kernel(SegParams p) {
+__global__ __launch_bounds__(SB_NT) void seg_stats_kernel(SegParams p) {
   __shared__ int sh[2 * SB_WAVES];
   const int S = p.S, L = p.L, off = S - L;
   const int lo = p.window >= 0 ? max(0, off - p.window) : 0;
-  int32_t* __restrict__ seg = p.seg;
+  const int T = (S + SB_TILE - 1) / SB_TILE;
+  const int b = blockIdx.x / T, k = blockIdx.x % T;
+  const int t0 = k * SB_TILE;
+  int32_t* rec = p.seg + p.lay.tiles + (size_t)blockIdx.x * kTileRec;
+
+  // fold the padding (doc ids -> folded ids), then work on the folded ids
+  Span sp;
+  sp.jb = t0 + threadIdx.x * SB_ITEMS;
+#pragma unroll
+  for (int u = 0; u < SB_ITEMS; ++u) sp.f[u] = (sp.jb + u < S) ? folded_at(p, b, sp.jb + u) : 0;
+  sp.fprev = (sp.jb > 0 && sp.jb - 1 < S) ? folded_at(p, b, sp.jb - 1) : 0;
+  sp.fnext = (sp.jb + SB_ITEMS < S) ? folded_at(p, b, sp.jb + SB_ITEMS) : 0;
+#pragma unroll
+  for (int u = 0; u < SB_ITEMS; ++u)
+    if (sp.jb + u < S) p.folded[(size_t)b * S + sp.jb + u] = sp.f[u];
+
+  // this workgroup's slice of the duplicate-id set
+  unsigned long long* table = reinterpret_cast<unsigned long long*>(p.seg + p.lay.hash);
+  for (size_t x = (size_t)blockIdx.x * SB_NT + threadIdx.x; x < p.lay.hash_size; x += (size_t)gridDim.x * SB_NT)
+    table[x] = 0ull;
+  if (k == 0 && threadIdx.x == 0) p.seg[p.lay.kcov_lo + b] = S;
+
+  // run starts: the tile's last, and per thread the last one before it (in-tile)
+  int my_last = -1;
+#pragma unroll
+  for (int u = 0; u < SB_ITEMS; ++u) {
+    const int pv = u ? sp.f[u - 1] : sp.fprev;
+    if (sp.f[u] > 0 && pv != sp.f[u]) my_last = sp.jb + u;
+  }
+  int tile_last;
+  const int before = block_excl_scan<true, SB_NT>(my_last, sh, tile_last);
+
+  // segment ends: those whose run starts in the tile are complete here; the
+  // one (if any) whose run began in an earlier tile is left to the scan
+  int n_end = 0, n_realq = 0, klen = 0, mq = 0, mk = 0, ext = -1;
+  int cur = before;
+#pragma unroll
+  for (int u = 0; u < SB_ITEMS; ++u) {
+    const int j = sp.jb + u;
+    const int pv = u ? sp.f[u - 1] : sp.fprev;
+    const int nx = (u + 1 < SB_ITEMS) ? sp.f[u + 1] : sp.fnext;
+    if (j >= S) break;
+    if (sp.f[u] > 0 && pv != sp.f[u]) cur = j;
+    if (sp.f[u] > 0 && j >= off) ++n_realq;
+    if (sp.f[u] > 0 && nx != sp.f[u] && j >= off) {
+      ++n_end;
+      if (cur >= 0) {
+        const int ql = j + 1 - max(cur, off), kl = j + 1 - max(cur, lo);
+        klen += kl;
+        mq = max(mq, ql);
+        mk = max(mk, kl);
+      } else {
+        ext = j;
+      }
+    }
+  }
+  int tot;
+  block_excl_scan<false, SB_NT>(n_end, sh, tot);
+  if (threadIdx.x == 0) rec[T_N_END] = tot;
+  block_excl_scan<false, SB_NT>(n_realq, sh, tot);
+  if (threadIdx.x == 0) rec[T_N_REALQ] = tot;
+  block_excl_scan<false, SB_NT>(klen, sh, tot);
+  if (threadIdx.x == 0) rec[T_KLEN_INT] = tot;
+  block_excl_scan<true, SB_NT>(mq, sh, tot);
+  if (threadIdx.x == 0) rec[T_MQ_INT] = tot;
+  block_excl_scan<true, SB_NT>(mk, sh, tot);
+  if (threadIdx.x == 0) rec[T_MK_INT] = tot;
+  block_excl_scan<true, SB_NT>(ext, sh, tot);
+  if (threadIdx.x == 0) {
+    rec[T_EXT_END] = tot;
+    rec[T_LAST_START] = tile_last;
+  }
+}
+
+__global__ __launch_bounds__(SC_NT) void seg_scan_kernel(SegParams p) {
+  __shared__ long long shl[2 * SC_WAVES];
+  __shared__ int shi[2 * SC_WAVES];
+  const int S = p.S, L = p.L, off = S - L;
+  const int lo = p.window >= 0 ? max(0, off - p.window) : 0;
+  const int T = (S + SB_TILE - 1) / SB_TILE;
+  const int n = p.B * T;
+  int32_t* tiles = p.seg + p.lay.tiles;
+  long long carry_key = LLONG_MIN, carry_rkey = LLONG_MIN;
+  int carry_seg = 0, carry_q = 0, carry_k = 0, maxq = 0, maxk = 0;
+  for (int c0 = 0; c0 < n; c0 += SC_NT) {
+    const int i = c0 + threadIdx.x;
+    const bool in = i < n;
+    const int32_t* rec = tiles + (size_t)(in ? i : 0) * kTileRec;
+    const int b = in ? i / T : 0;
+    // segmented prefix max of run starts within the row: key (row, start + 1)
+    const long long key = in ? (long long)b * ((long long)S + 1) + (rec[T_LAST_START] + 1) : LLONG_MIN;
+    long long agg;
+    const long long kb = max(carry_key, block_excl_scan<true, SC_NT>(key, shl, agg));
+    const int sb = (in && kb >= (long long)b * ((long long)S + 1)) ? (int)(kb - (long long)b * ((long long)S + 1)) - 1 : -1;
+    // complete the carried-in segment of the tile
+    int klen = 0, mq = 0, mk = 0, n_end = 0, n_realq = 0, ext = -1;
+    if (in) {
+      n_end = rec[T_N_END];
+      n_realq = rec[T_N_REALQ];
+      klen = rec[T_KLEN_INT];
+      mq = rec[T_MQ_INT];
+      mk = rec[T_MK_INT];
+      ext = rec[T_EXT_END];
+      if (ext >= 0) {
+        klen += ext + 1 - max(sb, lo);
+        mq = max(mq, ext + 1 - max(sb, off));
+        mk = max(mk, ext + 1 - max(sb, lo));
+      }
+    }
+    int tot_seg, tot_q, tot_k, cmq, cmk;
+    const int seg_before = carry_seg + block_excl_scan<false, SC_NT>(n_end, shi, tot_seg);
+    const int q_before = carry_q + block_excl_scan<false, SC_NT>(n_realq, shi, tot_q);
+    const int k_before = carry_k + block_excl_scan<false, SC_NT>(klen, shi, tot_k);
+    block_excl_scan<true, SC_NT>(mq, shi, cmq);
+    block_excl_scan<true, SC_NT>(mk, shi, cmk);
+    // segments before the row's first tile: carried by a segmented max of the
+    // (row, seg_before) pairs of first tiles
+    const long long rkey = (in && i % T == 0) ? (long long)b * (1ll << 32) + seg_before : LLONG_MIN;
+    long long ragg;
+    const long long rk = max(carry_rkey, block_excl_scan<true, SC_NT>(rkey, shl, ragg));
+    if (in) {
+      int32_t* pr = tiles + (size_t)i * kTileRec + 8;
+      pr[P_START_BEFORE] = sb;
+      pr[P_SEG_BEFORE] = seg_before;
+      pr[P_Q_BEFORE] = q_before;
+      pr[P_K_BEFORE] = k_before;
+      pr[P_ROW_SEG0] = (i % T == 0) ? seg_before : (int)(rk & 0xFFFFFFFFll);
+    }
+    carry_key = max(carry_key, agg);
+    carry_rkey = max(carry_rkey, ragg);
+    carry_seg += tot_seg;
+    carry_q += tot_q;
+    carry_k += tot_k;
+    maxq = max(maxq, cmq);
+    maxk = max(maxk, cmk);
+  }
+  if (threadIdx.x == 0) {
+    int32_t* seg = p.seg;
+    seg[0] = carry_seg;
+    seg[1] = maxq;
+    seg[2] = maxk;
+    seg[3] = 0;   // status: set by the emit pass
+    seg[4] = lo;
+    seg[5] = p.B;
+    seg[6] = L;
+    seg[7] = S;
+    seg[8] = p.window;
+    seg[9] = carry_q;
+    for (int x = 10; x < 16; ++x) seg[x] = 0;
+    seg[p.lay.cu_q] = 0;
+    seg[p.lay.cu_k] = 0;
+  }
+}
+
+__global__ __launch_bounds__(SB_NT) void seg_emit_kernel(SegParams p) {
+  __shared__ int sh[2 * SB_WAVES];
+  const int S = p.S, L = p.L, off = S - L;
+  const int lo = p.window >= 0 ? max(0, off - p.window) : 0;
+  const int T = (S + SB_TILE - 1) / SB_TILE;
+  const int b = blockIdx.x / T, k = blockIdx.x % T;
+  const int32_t* pr = p.seg + p.lay.tiles + (size_t)blockIdx.x * kTileRec + 8;
+  const int start_before = pr[P_START_BEFORE], seg_before = pr[P_SEG_BEFORE];
+  const int q_before = pr[P_Q_BEFORE], k_before = pr[P_K_BEFORE], row_seg0 = pr[P_ROW_SEG0];
+  int32_t* seg = p.seg;
   int32_t* cu_q = seg + p.lay.cu_q;
   int32_t* cu_k = seg + p.lay.cu_k;
   int32_t* q_row0 = seg + p.lay.q_row0;
@@ -90,129 +287,71 @@ __global__ __launch_bounds__(SB_NT) void segment_build_kernel(SegParams p) {
   int32_t* row_seg = seg + p.lay.row_seg;
   int32_t* row_klo = seg + p.lay.row_klo;
   int32_t* kcov_lo = seg + p.lay.kcov_lo;
-  int* table = seg + p.lay.hash;
-  const int hmask = p.lay.hash_size - 1;
+  unsigned long long* table = reinterpret_cast<unsigned long long*>(seg + p.lay.hash);
+  const uint32_t hmask = (uint32_t)(p.lay.hash_size - 1);
 
-  int n_seg = 0, cuq = 0, cuk = 0, maxq = 0, maxk = 0, dup = 0;
-  if (threadIdx.x == 0) { cu_q[0] = 0; cu_k[0] = 0; }
+  Span sp;
+  load_span(p, p.folded, b, k * SB_TILE, sp);
 
-  for (int b = 0; b < p.B; ++b) {
-    for (int x = threadIdx.x; x < p.lay.hash_size; x += SB_NT) table[x] = 0;
-    if (threadIdx.x == 0) kcov_lo[b] = S;
-    __threadfence();
-    __syncthreads();
-    int carry_start = -1, row_nseg = 0, row_realq = 0, row_klen = 0;
-
-    for (int t0 = 0; t0 < S; t0 += SB_TILE) {
-      const int jb = t0 + threadIdx.x * SB_ITEMS;
-      int f[SB_ITEMS];
+  int my_last = -1;
 #pragma unroll
-      for (int u = 0; u < SB_ITEMS; ++u) f[u] = (jb + u < S) ? folded_at(p, b, jb + u) : 0;
-      const int fprev = (jb > 0 && jb - 1 < S) ? folded_at(p, b, jb - 1) : 0;
-      const int fnext = (jb + SB_ITEMS < S) ? folded_at(p, b, jb + SB_ITEMS) : 0;
+  for (int u = 0; u < SB_ITEMS; ++u) {
+    const int pv = u ? sp.f[u - 1] : sp.fprev;
+    if (sp.f[u] > 0 && pv != sp.f[u]) my_last = sp.jb + u;
+  }
+  int tmp;
+  const int before = max(start_before, block_excl_scan<true, SB_NT>(my_last, sh, tmp));
+  int n_end = 0, n_realq = 0, klen = 0;
+  {
+    int cur = before;
 #pragma unroll
-      for (int u = 0; u < SB_ITEMS; ++u)
-        if (jb + u < S) p.folded[(size_t)b * S + jb + u] = f[u];
-
-      // pass 1: last run start among this thread's positions
-      int my_last_start = -1;
-#pragma unroll
-      for (int u = 0; u < SB_ITEMS; ++u) {
-        const int pv = u ? f[u - 1] : fprev;
-        if (f[u] > 0 && pv != f[u]) my_last_start = jb + u;
+    for (int u = 0; u < SB_ITEMS; ++u) {
+      const int j = sp.jb + u;
+      if (j >= S) break;
+      const int pv = u ? sp.f[u - 1] : sp.fprev;
+      const int nx = (u + 1 < SB_ITEMS) ? sp.f[u + 1] : sp.fnext;
+      if (sp.f[u] > 0 && pv != sp.f[u]) cur = j;
+      if (sp.f[u] > 0 && j >= off) ++n_realq;
+      if (sp.f[u] > 0 && nx != sp.f[u] && j >= off) {
+        ++n_end;
+        klen += j + 1 - max(cur, lo);
       }
-      int tile_last_start;
-      const int start_before = max(carry_start, block_excl_scan<true>(my_last_start, sh, tile_last_start));
-
-      // pass 2: per-thread counts of segment ends, real query rows, key lengths
-      int n_end = 0, n_realq = 0, klen = 0, mq = 0, mk = 0;
-      {
-        int cur = start_before;
-#pragma unroll
-        for (int u = 0; u < SB_ITEMS; ++u) {
-          const int j = jb + u;
-          const int pv = u ? f[u - 1] : fprev;
-          const int nx = (u + 1 < SB_ITEMS) ? f[u + 1] : fnext;
-          if (f[u] > 0 && pv != f[u]) cur = j;
-          if (f[u] > 0 && j >= off) ++n_realq;
-          if (f[u] > 0 && nx != f[u] && j >= off) {
-            ++n_end;
-            const int ql = j + 1 - max(cur, off), kl = j + 1 - max(cur, lo);
-            klen += kl;
-            mq = max(mq, ql);
-            mk = max(mk, kl);
-          }
-        }
-      }
-      int tot_end, tot_realq, tot_klen, tile_mq, tile_mk;
-      const int end_before = block_excl_scan<false>(n_end, sh, tot_end);
-      const int realq_before = block_excl_scan<false>(n_realq, sh, tot_realq);
-      const int klen_before = block_excl_scan<false>(klen, sh, tot_klen);
-      block_excl_scan<true>(mq, sh, tile_mq);
-      block_excl_scan<true>(mk, sh, tile_mk);
-
-      // pass 3: emit
-      {
-        int cur = start_before;
-        int e_run = row_nseg + end_before;            // segments of this row ended before j
-        int q_run = cuq + row_realq + realq_before;   // real query rows before j (all rows)
-        int k_run = cuk + row_klen + klen_before;     // key lengths of segments before j
-#pragma unroll
-        for (int u = 0; u < SB_ITEMS; ++u) {
-          const int j = jb + u;
-          if (j >= S) break;
-          const int pv = u ? f[u - 1] : fprev;
-          const int nx = (u + 1 < SB_ITEMS) ? f[u + 1] : fnext;
-          const bool doc = f[u] > 0;
-          if (doc && pv != f[u]) {
-            cur = j;
-            if (id_seen_before(table, hmask, f[u])) dup = 1;
-          }
-          if (j >= off) {
-            const int qi = (size_t)b * L + (j - off);
-            row_seg[qi] = doc ? n_seg + e_run : -1;
-            row_klo[qi] = doc ? max(cur, lo) : j + 1;
-            if (doc) ++q_run;
-          }
-          if (doc && nx != f[u] && j >= off) {
-            const int sid = n_seg + e_run;
-            const int k0 = max(cur, lo);
-            k_run += j + 1 - k0;
-            cu_q[sid + 1] = q_run;
-            cu_k[sid + 1] = k_run;
-            q_row0[sid] = b * L + (max(cur, off) - off);
-            k_row0[sid] = b * S + k0;
-            if (e_run == 0) kcov_lo[b] = k0;
-            ++e_run;
-          }
-        }
-      }
-      carry_start = max(carry_start, tile_last_start);
-      row_nseg += tot_end;
-      row_realq += tot_realq;
-      row_klen += tot_klen;
-      maxq = max(maxq, tile_mq);
-      maxk = max(maxk, tile_mk);
     }
-    n_seg += row_nseg;
-    cuq += row_realq;
-    cuk += row_klen;
-    __syncthreads();
   }
-  dup = __syncthreads_or(dup);
-  if (threadIdx.x == 0) {
-    seg[0] = n_seg;
-    seg[1] = maxq;
-    seg[2] = maxk;
-    seg[3] = dup ? 1 : 0;
-    seg[4] = lo;
-    seg[5] = p.B;
-    seg[6] = L;
-    seg[7] = S;
-    seg[8] = p.window;
-    seg[9] = cuq;
-    for (int x = 10; x < 16; ++x) seg[x] = 0;
+  int e_run = seg_before + block_excl_scan<false, SB_NT>(n_end, sh, tmp);
+  int q_run = q_before + block_excl_scan<false, SB_NT>(n_realq, sh, tmp);
+  int k_run = k_before + block_excl_scan<false, SB_NT>(klen, sh, tmp);
+  int dup = 0;
+  int cur = before;
+#pragma unroll
+  for (int u = 0; u < SB_ITEMS; ++u) {
+    const int j = sp.jb + u;
+    if (j >= S) break;
+    const int pv = u ? sp.f[u - 1] : sp.fprev;
+    const int nx = (u + 1 < SB_ITEMS) ? sp.f[u + 1] : sp.fnext;
+    const bool doc = sp.f[u] > 0;
+    if (doc && pv != sp.f[u]) {
+      cur = j;
+      if (id_seen_before(table, hmask, b, sp.f[u])) dup = 1;
+    }
+    if (j >= off) {
+      const int qi = b * L + (j - off);   // < B * L since off <= j < S
+      row_seg[qi] = doc ? e_run : -1;
+      row_klo[qi] = doc ? max(cur, lo) : j + 1;
+      if (doc) ++q_run;
+    }
+    if (doc && nx != sp.f[u] && j >= off && e_run < p.B * L) {   // (every segment owns >= 1 query row)
+      const int k0 = max(cur, lo);
+      k_run += j + 1 - k0;
+      cu_q[e_run + 1] = q_run;
+      cu_k[e_run + 1] = k_run;
+      q_row0[e_run] = b * L + (max(cur, off) - off);
+      k_row0[e_run] = b * S + k0;
+      if (e_run == row_seg0) kcov_lo[b] = k0;
+      ++e_run;
+    }
   }
+  if (__syncthreads_or(dup) && threadIdx.x == 0) atomicOr(seg + NB_HDR_STATUS, NB_SEG_STATUS_SPLIT_DOC);
 }
 
 SegLayout seg_layout(int B, int L, int S) {
@@ -225,22 +364,33 @@ SegLayout seg_layout(int B, int L, int S) {
   l.row_seg = l.k_row0 + N;
   l.row_klo = l.row_seg + N;
   l.kcov_lo = l.row_klo + N;
-  size_t h = l.kcov_lo + B;
-  h = (h + 63) & ~(size_t)63;
+  size_t t = l.kcov_lo + B;
+  t = (t + 63) & ~(size_t)63;
+  l.tiles = t;
+  const size_t n_tiles = (size_t)B * ((S + SB_TILE - 1) / SB_TILE);
+  size_t h = l.tiles + n_tiles * kTileRec;
+  h = (h + 63) & ~(size_t)63;   // 8-byte set entries, 256-byte aligned
   l.hash = h;
-  int hs = 64;
-  while (hs < 2 * S) hs <<= 1;
+  size_t hs = 64;
+  while (hs < 2 * (size_t)B * (size_t)S) hs <<= 1;
   l.hash_size = hs;
   return l;
 }
 
 size_t seg_buffer_elems(int B, int L, int S) {
   const SegLayout l = seg_layout(B, L, S);
-  return l.hash + (size_t)l.hash_size;
+  return l.hash + 2 * (size_t)l.hash_size;
 }
 
 hipError_t launch_segment_build(const SegParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(segment_build_kernel, dim3(1), dim3(SB_NT), 0, s, p);
+  const unsigned n_tiles = (unsigned)(p.B * ((p.S + SB_TILE - 1) / SB_TILE));
+  hipLaunchKernelGGL(seg_stats_kernel, dim3(n_tiles), dim3(SB_NT), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(SC_NT), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(seg_emit_kernel, dim3(n_tiles), dim3(SB_NT), 0, s, p);
   return hipGetLastError();
 }
 
