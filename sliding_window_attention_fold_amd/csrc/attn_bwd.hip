@@ -499,10 +499,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
 // the natural order.
 constexpr int kOrderNT = 1024;
 constexpr int kOrderMax = 8192;
+constexpr int kOrderBandMax = 4096;   // query-tile band starts staged in LDS
 
 template <int BK, int BQ>
 __global__ __launch_bounds__(kOrderNT) void dkdv_order_kernel(BwdParams p) {
   __shared__ unsigned long long keys[kOrderMax];
+  __shared__ int bst[kOrderBandMax];
   const int tid = threadIdx.x;
   const int n_kt = (p.S + BK - 1) / BK;
   const int n = p.B * n_kt;
@@ -513,6 +515,16 @@ __global__ __launch_bounds__(kOrderNT) void dkdv_order_kernel(BwdParams p) {
   }
   const int off = p.S - p.L;
   const int n_q_tiles = (p.L + BQ - 1) / BQ;
+  // band start of each query tile's first row (nondecreasing along a row)
+  auto band_start_g = [&](int b, int t) {
+    const int r = t * BQ;
+    const int bq = max(0, p.row_klo[(size_t)b * p.L + r]);
+    return p.window >= 0 ? max(bq, off + r - p.window) : bq;
+  };
+  const bool staged = p.B * n_q_tiles <= kOrderBandMax;
+  if (staged)
+    for (int x = tid; x < p.B * n_q_tiles; x += kOrderNT) bst[x] = band_start_g(x / n_q_tiles, x % n_q_tiles);
+  __syncthreads();
   int N = 1;
   while (N < n) N <<= 1;
   for (int i = tid; i < N; i += kOrderNT) {
@@ -521,15 +533,11 @@ __global__ __launch_bounds__(kOrderNT) void dkdv_order_kernel(BwdParams p) {
       const int b = i / n_kt, kt = i % n_kt;
       const int jmax = min(kt * BK + BK, p.S) - 1;
       const int t_first = max(0, kt * BK - off) / BQ;
-      auto band_start = [&](int t) {
-        const int r = t * BQ;
-        const int bq = max(0, p.row_klo[(size_t)b * p.L + r]);
-        return p.window >= 0 ? max(bq, off + r - p.window) : bq;
-      };
       int lo = t_first, hi = n_q_tiles;  // first tile in [lo, hi) whose band starts after jmax
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (band_start(mid) <= jmax) lo = mid + 1;
+        const int bsm = staged ? bst[b * n_q_tiles + mid] : band_start_g(b, mid);
+        if (bsm <= jmax) lo = mid + 1;
         else hi = mid;
       }
       const unsigned work = (unsigned)(lo - t_first);

@@ -9,19 +9,20 @@
 // start .. last local row (bottom-right alignment), cu_seqlens_q[i] paired
 // with cu_seqlens_k[i].
 //
-// Three launches over tiles of 2048 positions of one batch row each:
+// Two launches over tiles of 2048 positions of one batch row each:
 //   1. stats (one workgroup per tile): fold the padding, write the folded ids,
 //      clear the duplicate-id set, and reduce the tile to a few numbers -- its
 //      last run start, its segment ends (ends at or after the shard start),
 //      real query rows, and the key lengths / maxima of the segments whose run
 //      starts inside the tile; a segment end whose run began in an earlier
 //      tile (at most one per tile) is recorded by position;
-//   2. scan (one workgroup): in (row, tile) order, the run start carried into
-//      each tile (a segmented prefix max), the completed key lengths of the
-//      carried-in segments, and exclusive prefix sums of segment ends, query
-//      rows and key lengths; writes the header;
-//   3. emit (one workgroup per tile): per-position outputs and per-segment
-//      cu_seqlens / row offsets, from the tile's prefixes plus in-tile scans.
+//   2. emit (one workgroup per tile): first a scan of the tile records in
+//      (row, tile) order -- the run start carried into the tile (a segmented
+//      prefix max), the completed key lengths of the carried-in segments, and
+//      exclusive prefix sums of segment ends, query rows and key lengths (the
+//      owner of tile 0 writes the header) -- then per-position outputs and
+//      per-segment cu_seqlens / row offsets from those prefixes plus in-tile
+//      scans.
 //      Run starts are inserted into an open-addressing set keyed by (row, id)
 //      to detect an id that occurs in two separate runs (status bit 0).
 // Segment indices are global and ordered by (row, position).
@@ -36,8 +37,6 @@ constexpr int SB_NT = 256;
 constexpr int SB_ITEMS = 8;
 constexpr int SB_TILE = SB_NT * SB_ITEMS;
 constexpr int SB_WAVES = SB_NT / 64;
-constexpr int SC_NT = 1024;   // scan kernel
-constexpr int SC_WAVES = SC_NT / 64;
 
 // Exclusive block-wide scan (sum, or max when MX) over NT threads; `total`
 // gets the block aggregate.  `sh` holds 2 * NT / 64 elements.
@@ -93,8 +92,7 @@ __device__ bool id_seen_before(unsigned long long* table, uint32_t mask, int row
 
 // per-tile records in the scratch area (int32 each)
 enum { T_LAST_START, T_N_END, T_N_REALQ, T_KLEN_INT, T_MQ_INT, T_MK_INT, T_EXT_END, T_STAT };
-enum { P_START_BEFORE, P_SEG_BEFORE, P_Q_BEFORE, P_K_BEFORE, P_ROW_SEG0 };
-constexpr int kTileRec = 16;   // T_* in [0, 8), P_* in [8, 16)
+constexpr int kTileRec = 8;
 
 // Per-thread view of its SB_ITEMS positions: folded ids plus both neighbours.
 struct Span {
@@ -137,6 +135,7 @@ __global__ __launch_bounds__(SB_NT) void seg_stats_kernel(SegParams p) {
   for (size_t x = (size_t)blockIdx.x * SB_NT + threadIdx.x; x < p.lay.hash_size; x += (size_t)gridDim.x * SB_NT)
     table[x] = 0ull;
   if (k == 0 && threadIdx.x == 0) p.seg[p.lay.kcov_lo + b] = S;
+  if (blockIdx.x == 0 && threadIdx.x == 0) p.seg[NB_HDR_STATUS] = 0;
 
   // run starts: the tile's last, and per thread the last one before it (in-tile)
   int my_last = -1;
@@ -190,17 +189,28 @@ __global__ __launch_bounds__(SB_NT) void seg_stats_kernel(SegParams p) {
   }
 }
 
-__global__ __launch_bounds__(SC_NT) void seg_scan_kernel(SegParams p) {
-  __shared__ long long shl[2 * SC_WAVES];
-  __shared__ int shi[2 * SC_WAVES];
+// Prefixes of tile `mine` from the records of all tiles, in (row, tile) order:
+// the run start carried into it (segmented prefix max over its row), and the
+// segment ends, real query rows and key lengths of all earlier tiles (the
+// carried-in segment of each tile completed with its carried start).  Every
+// emit workgroup runs this over the (few) tile records; the one that owns
+// tile 0 also writes the header totals.
+struct TilePrefix {
+  int start_before, seg_before, q_before, k_before, row_seg0;
+};
+
+__device__ TilePrefix tile_prefix(const SegParams& p, int mine, bool write_header) {
+  __shared__ long long shl[2 * SB_WAVES];
+  __shared__ int shi[2 * SB_WAVES];
+  __shared__ TilePrefix out;
   const int S = p.S, L = p.L, off = S - L;
   const int lo = p.window >= 0 ? max(0, off - p.window) : 0;
   const int T = (S + SB_TILE - 1) / SB_TILE;
   const int n = p.B * T;
-  int32_t* tiles = p.seg + p.lay.tiles;
+  const int32_t* tiles = p.seg + p.lay.tiles;
   long long carry_key = LLONG_MIN, carry_rkey = LLONG_MIN;
   int carry_seg = 0, carry_q = 0, carry_k = 0, maxq = 0, maxk = 0;
-  for (int c0 = 0; c0 < n; c0 += SC_NT) {
+  for (int c0 = 0; c0 < n; c0 += SB_NT) {
     const int i = c0 + threadIdx.x;
     const bool in = i < n;
     const int32_t* rec = tiles + (size_t)(in ? i : 0) * kTileRec;
@@ -208,17 +218,17 @@ __global__ __launch_bounds__(SC_NT) void seg_scan_kernel(SegParams p) {
     // segmented prefix max of run starts within the row: key (row, start + 1)
     const long long key = in ? (long long)b * ((long long)S + 1) + (rec[T_LAST_START] + 1) : LLONG_MIN;
     long long agg;
-    const long long kb = max(carry_key, block_excl_scan<true, SC_NT>(key, shl, agg));
+    const long long kb = max(carry_key, block_excl_scan<true, SB_NT>(key, shl, agg));
     const int sb = (in && kb >= (long long)b * ((long long)S + 1)) ? (int)(kb - (long long)b * ((long long)S + 1)) - 1 : -1;
     // complete the carried-in segment of the tile
-    int klen = 0, mq = 0, mk = 0, n_end = 0, n_realq = 0, ext = -1;
+    int klen = 0, mq = 0, mk = 0, n_end = 0, n_realq = 0;
     if (in) {
       n_end = rec[T_N_END];
       n_realq = rec[T_N_REALQ];
       klen = rec[T_KLEN_INT];
       mq = rec[T_MQ_INT];
       mk = rec[T_MK_INT];
-      ext = rec[T_EXT_END];
+      const int ext = rec[T_EXT_END];
       if (ext >= 0) {
         klen += ext + 1 - max(sb, lo);
         mq = max(mq, ext + 1 - max(sb, off));
@@ -226,23 +236,22 @@ __global__ __launch_bounds__(SC_NT) void seg_scan_kernel(SegParams p) {
       }
     }
     int tot_seg, tot_q, tot_k, cmq, cmk;
-    const int seg_before = carry_seg + block_excl_scan<false, SC_NT>(n_end, shi, tot_seg);
-    const int q_before = carry_q + block_excl_scan<false, SC_NT>(n_realq, shi, tot_q);
-    const int k_before = carry_k + block_excl_scan<false, SC_NT>(klen, shi, tot_k);
-    block_excl_scan<true, SC_NT>(mq, shi, cmq);
-    block_excl_scan<true, SC_NT>(mk, shi, cmk);
-    // segments before the row's first tile: carried by a segmented max of the
-    // (row, seg_before) pairs of first tiles
+    const int seg_before = carry_seg + block_excl_scan<false, SB_NT>(n_end, shi, tot_seg);
+    const int q_before = carry_q + block_excl_scan<false, SB_NT>(n_realq, shi, tot_q);
+    const int k_before = carry_k + block_excl_scan<false, SB_NT>(klen, shi, tot_k);
+    block_excl_scan<true, SB_NT>(mq, shi, cmq);
+    block_excl_scan<true, SB_NT>(mk, shi, cmk);
+    // segments before the row's first tile: segmented max of (row, seg_before)
+    // over the rows' first tiles
     const long long rkey = (in && i % T == 0) ? (long long)b * (1ll << 32) + seg_before : LLONG_MIN;
     long long ragg;
-    const long long rk = max(carry_rkey, block_excl_scan<true, SC_NT>(rkey, shl, ragg));
-    if (in) {
-      int32_t* pr = tiles + (size_t)i * kTileRec + 8;
-      pr[P_START_BEFORE] = sb;
-      pr[P_SEG_BEFORE] = seg_before;
-      pr[P_Q_BEFORE] = q_before;
-      pr[P_K_BEFORE] = k_before;
-      pr[P_ROW_SEG0] = (i % T == 0) ? seg_before : (int)(rk & 0xFFFFFFFFll);
+    const long long rk = max(carry_rkey, block_excl_scan<true, SB_NT>(rkey, shl, ragg));
+    if (i == mine) {
+      out.start_before = sb;
+      out.seg_before = seg_before;
+      out.q_before = q_before;
+      out.k_before = k_before;
+      out.row_seg0 = (i % T == 0) ? seg_before : (int)(rk & 0xFFFFFFFFll);
     }
     carry_key = max(carry_key, agg);
     carry_rkey = max(carry_rkey, ragg);
@@ -252,22 +261,24 @@ __global__ __launch_bounds__(SC_NT) void seg_scan_kernel(SegParams p) {
     maxq = max(maxq, cmq);
     maxk = max(maxk, cmk);
   }
-  if (threadIdx.x == 0) {
+  if (write_header && threadIdx.x == 0) {
     int32_t* seg = p.seg;
-    seg[0] = carry_seg;
-    seg[1] = maxq;
-    seg[2] = maxk;
-    seg[3] = 0;   // status: set by the emit pass
-    seg[4] = lo;
-    seg[5] = p.B;
-    seg[6] = L;
-    seg[7] = S;
-    seg[8] = p.window;
-    seg[9] = carry_q;
-    for (int x = 10; x < 16; ++x) seg[x] = 0;
+    seg[NB_HDR_NSEG] = carry_seg;
+    seg[NB_HDR_MAXQ] = maxq;
+    seg[NB_HDR_MAXK] = maxk;
+    // NB_HDR_STATUS: cleared by the stats pass, set by the emit pass
+    seg[NB_HDR_LO] = lo;
+    seg[NB_HDR_B] = p.B;
+    seg[NB_HDR_L] = L;
+    seg[NB_HDR_S] = S;
+    seg[NB_HDR_WINDOW] = p.window;
+    seg[NB_HDR_NREAL] = carry_q;
+    for (int x = 10; x < NB_SEG_HEADER; ++x) seg[x] = 0;
     seg[p.lay.cu_q] = 0;
     seg[p.lay.cu_k] = 0;
   }
+  __syncthreads();
+  return out;
 }
 
 __global__ __launch_bounds__(SB_NT) void seg_emit_kernel(SegParams p) {
@@ -276,9 +287,9 @@ __global__ __launch_bounds__(SB_NT) void seg_emit_kernel(SegParams p) {
   const int lo = p.window >= 0 ? max(0, off - p.window) : 0;
   const int T = (S + SB_TILE - 1) / SB_TILE;
   const int b = blockIdx.x / T, k = blockIdx.x % T;
-  const int32_t* pr = p.seg + p.lay.tiles + (size_t)blockIdx.x * kTileRec + 8;
-  const int start_before = pr[P_START_BEFORE], seg_before = pr[P_SEG_BEFORE];
-  const int q_before = pr[P_Q_BEFORE], k_before = pr[P_K_BEFORE], row_seg0 = pr[P_ROW_SEG0];
+  const TilePrefix tp = tile_prefix(p, blockIdx.x, blockIdx.x == 0);
+  const int start_before = tp.start_before, seg_before = tp.seg_before;
+  const int q_before = tp.q_before, k_before = tp.k_before, row_seg0 = tp.row_seg0;
   int32_t* seg = p.seg;
   int32_t* cu_q = seg + p.lay.cu_q;
   int32_t* cu_k = seg + p.lay.cu_k;
@@ -386,9 +397,6 @@ hipError_t launch_segment_build(const SegParams& p, hipStream_t s) {
   const unsigned n_tiles = (unsigned)(p.B * ((p.S + SB_TILE - 1) / SB_TILE));
   hipLaunchKernelGGL(seg_stats_kernel, dim3(n_tiles), dim3(SB_NT), 0, s, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(SC_NT), 0, s, p);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(seg_emit_kernel, dim3(n_tiles), dim3(SB_NT), 0, s, p);
   return hipGetLastError();
