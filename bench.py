@@ -2,9 +2,10 @@
 """Throughput of one context-parallel rank's neighbourhood attention on one MI355X.
 
 One step is the whole hot path over one batch of synthetic input: pad fold +
-segment build, forward (O, LSE), backward (dQ pass with Delta, dK/dV pass with
-the GQA reduction) and the per-owner attended flags -- all on the device, no
-host synchronisation inside the step.  Inputs are resident in HBM before the
+segment build, forward (O, LSE), backward (Delta and work orders, then the dQ
+and dK/dV passes with the GQA reduction in one persistent grid) and the
+per-owner attended flags -- all on the device, no host synchronisation inside
+the step.  Inputs are resident in HBM before the
 timed region starts.
 
 Default workload: the Gemma-style sliding layer at rank 3 of a 4-way ring
@@ -35,8 +36,9 @@ METRIC = "fwd+bwd useful TFLOP/s per shard; % of bf16 MFMA peak (MI355X)"
 # kernel -> (symbol substring in rocprof, source file, algorithmic FLOPs per allowed pair per q head / D)
 KERNELS = {
     "attn_fwd": ("attn_fwd_kernel", "attn_fwd.hip", 4),     # S = QK^T, O = PV
-    "bwd_dq": ("bwd_dq_kernel", "attn_bwd.hip", 2),         # dQ = dS K (S, dP recomputed, not counted)
-    "bwd_dkdv": ("bwd_dkdv_kernel", "attn_bwd.hip", 8),     # S, dP, dV = P^T dO, dK = dS^T Q
+    # one persistent grid for both backward passes: S, dP, dV = P^T dO, dK = dS^T Q, dQ = dS K
+    # (the dQ pass's recompute of S and dP is not counted)
+    "bwd_main": ("bwd_kernel", "attn_bwd.hip", 10),
 }
 
 
@@ -162,10 +164,10 @@ def main() -> int:
                                                       sp),
         "attn_fwd": lambda: lib.nb_attn_fwd(P(qd), P(kd), P(vd), P(out), P(resid), P(lse), P(segbuf), B, Hq, Hkv, L,
                                             S, D, scale, W, 0.0, bf, None, 0, sp),
-        "bwd_dq": lambda: lib.nb_attn_bwd_dq(P(dod), P(qd), P(kd), P(vd), P(out), P(resid), P(lse), P(segbuf), B,
-                                             Hq, Hkv, L, S, D, scale, W, bf, P(dq), P(ws), ws_bytes, sp),
-        "bwd_dkdv": lambda: lib.nb_attn_bwd_dkdv(P(dod), P(qd), P(kd), P(vd), P(lse), P(segbuf), B, Hq, Hkv, L, S,
-                                                 D, scale, W, bf, P(dk), P(dv), P(ws), ws_bytes, sp),
+        "bwd_prep": lambda: lib.nb_attn_bwd_prep(P(dod), P(out), P(resid), P(segbuf), B, Hq, Hkv, L, S, D, W, bf,
+                                                 P(ws), ws_bytes, sp),
+        "bwd_main": lambda: lib.nb_attn_bwd_main(P(dod), P(qd), P(kd), P(vd), P(lse), P(segbuf), B, Hq, Hkv, L, S,
+                                                 D, scale, W, bf, P(dq), P(dk), P(dv), P(ws), ws_bytes, sp),
         "owner_flags": lambda: lib.nb_owner_attended(P(segbuf), P(folded), B, L, S, ctypes.cast(off_c,
                                                      ctypes.c_void_p), n_owner, P(attended), sp),
     }
@@ -218,7 +220,7 @@ def main() -> int:
         torch.cuda.synchronize()
 
     tflops = useful / (ms_step * 1e-3) / 1e12
-    dom = max(("attn_fwd", "bwd_dq", "bwd_dkdv"), key=lambda n: per[n])
+    dom = max(KERNELS, key=lambda n: per[n])
     dom_flops = KERNELS[dom][2] * D * Hq * pairs
     achieved = dom_flops / (per[dom] * 1e-3) / 1e12
     traffic = read_traffic(dom, f"config{args.config}")
@@ -242,7 +244,7 @@ def main() -> int:
         },
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "ms_per_kernel": {n: round(per[n], 5) for n in names},
-        "fwd_bwd_ms": round(per["attn_fwd"] + per["bwd_dq"] + per["bwd_dkdv"], 5),
+        "fwd_bwd_ms": round(per["attn_fwd"] + per["bwd_prep"] + per["bwd_main"], 5),
         "wall_s_timed": round(wall, 4),
         "roofline": {
             "kernel": dom, "bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,

@@ -152,9 +152,10 @@ int nb_attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_re
                 int window_left, float dropout_p, int dtype, void* ws, size_t ws_bytes,
                 void* stream);
 
-/* Bytes of workspace nb_attn_bwd needs: the Delta rows (B * Hq * L floats)
- * and the dK/dV work order (B * ceil(S / 32) ints), each 256-byte aligned.
- * Returns 0 for non-positive sizes. */
+/* Bytes of workspace nb_attn_bwd needs: the Delta rows (B * Hq * L floats),
+ * then the work orders of the two passes and the backward kernel's work-queue
+ * counters (B * ceil(S / 32) + 8 + B * ceil(L / 32) ints), each part 256-byte
+ * aligned. */
 size_t nb_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, int dtype);
 
 /*
@@ -180,15 +181,30 @@ int nb_attn_bwd(const void* dout, const void* q, const void* k, const void* v, c
                 uint8_t* owner_attended, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * The passes nb_attn_bwd runs, for callers that schedule them separately (for
+ * The steps nb_attn_bwd runs, for callers that schedule them separately (for
  * instance to hand dK/dV to the owner exchange while other work runs) and for
  * per-kernel timing.  Same arguments and conventions as nb_attn_bwd.
- *   nb_attn_bwd_dq:   Delta = dO . (o + o_resid) into ws, then dq.
- *   nb_attn_bwd_dkdv: dk, dv; needs the Delta an earlier nb_attn_bwd_dq call on
- *                     the same stream left in the same ws.
+ *   nb_attn_bwd_prep: Delta = dO . (o + o_resid) into ws, and the work orders
+ *                     (longest items first) of the two passes.
+ *   nb_attn_bwd_main: dq, dk, dv: both passes in one persistent grid (the
+ *                     short dQ items fill the tail of the dK/dV items); needs
+ *                     an nb_attn_bwd_prep call on the same stream and ws before
+ *                     each call.  nb_attn_bwd = prep + main + owner flags.
+ *   nb_attn_bwd_dq:   Delta into ws, then dq alone.
+ *   nb_attn_bwd_dkdv: dk, dv alone; needs the Delta an earlier nb_attn_bwd_dq
+ *                     or nb_attn_bwd_prep call on the same stream left in ws.
  *   nb_owner_attended: owner_attended[o] = 1 iff some real query attended a key
  *                     of chunk o (cp_local_ring page, _owner_grad_dict).
+ * The workspace is written by every one of them (Delta, work orders, queue
+ * counters); calls sharing a workspace must be ordered on one stream.
  */
+int nb_attn_bwd_prep(const void* dout, const void* o, const void* o_resid, const int32_t* seg_buf, int B,
+                     int Hq, int Hkv, int L, int S, int D, int window_left, int dtype, void* ws,
+                     size_t ws_bytes, void* stream);
+int nb_attn_bwd_main(const void* dout, const void* q, const void* k, const void* v, const float* lse,
+                     const int32_t* seg_buf, int B, int Hq, int Hkv, int L, int S, int D, float scale,
+                     int window_left, int dtype, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                     void* stream);
 int nb_attn_bwd_dq(const void* dout, const void* q, const void* k, const void* v, const void* o,
                    const void* o_resid, const float* lse, const int32_t* seg_buf, int B, int Hq,
                    int Hkv, int L, int S, int D, float scale, int window_left, int dtype, void* dq,
@@ -196,7 +212,7 @@ int nb_attn_bwd_dq(const void* dout, const void* q, const void* k, const void* v
 int nb_attn_bwd_dkdv(const void* dout, const void* q, const void* k, const void* v,
                      const float* lse, const int32_t* seg_buf, int B, int Hq, int Hkv, int L, int S,
                      int D, float scale, int window_left, int dtype, void* dk, void* dv,
-                     const void* ws, size_t ws_bytes, void* stream);
+                     void* ws, size_t ws_bytes, void* stream);
 int nb_owner_attended(const int32_t* seg_buf, const int32_t* folded_ids, int B, int L, int S,
                       const int32_t* owner_off, int n_owner, uint8_t* owner_attended, void* stream);
 

@@ -38,6 +38,8 @@ SIGNATURES = {
                          _P, _P, _P, _P, _I, _P, _P, _Z, _P]),
     "nb_attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _Z, _P]),
     "nb_attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _Z, _P]),
+    "nb_attn_bwd_prep": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _Z, _P]),
+    "nb_attn_bwd_main": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P, _Z, _P]),
     "nb_owner_attended": (_I, [_P, _P, _I, _I, _I, _P, _I, _P, _P]),
 }
 

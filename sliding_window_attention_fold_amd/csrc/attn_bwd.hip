@@ -55,48 +55,42 @@ struct DkvCfg {
   static constexpr int AHEAD = (D <= 128 && sizeof(T) == 2) ? 4 : 0;
 };
 
+// LDS of one dK/dV item: two (Q, dO, row metadata) buffers -- one is filled by
+// DMA while the other is read -- and the P hand-over from role A to role B.
 template <typename T, int D>
-__global__ __launch_bounds__((DkvCfg<T, D>::NT), (DkvCfg<T, D>::OCC)) void bwd_dkdv_kernel(BwdParams p) {
+struct DkvSmem {
+  typedef Tile<T, DkvCfg<T, D>::BQ, D> TL;
+  __attribute__((aligned(1024))) T Q0[TL::ELEMS];
+  __attribute__((aligned(1024))) T G0[TL::ELEMS];
+  __attribute__((aligned(1024))) T Q1[TL::ELEMS];
+  __attribute__((aligned(1024))) T G1[TL::ELEMS];
+  __attribute__((aligned(256))) float lse0[64], lse1[64], dl0[64], dl1[64];
+  __attribute__((aligned(256))) int klo0[64], klo1[64];
+  __attribute__((aligned(256))) f32x4 pex[DkvCfg<T, D>::NKG][4][64];  // [key group][value quad][lane][4]
+  int n_tiles_s;
+};
+
+// One dK/dV item f: (kv head, batch row, key tile) with the kv head fastest
+// and the (batch row, key tile) pairs in the order of decreasing work
+// (work_order_kernel), so the long tiles start first.
+template <typename T, int D>
+__device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm, int f) {
   typedef DkvCfg<T, D> C;
   typedef Tile<T, C::BQ, D> TL;
   typedef typename Frag<T>::type F;
-  // two (Q, dO, row metadata) buffers: one is filled by DMA while the other is read
-  __shared__ __attribute__((aligned(1024))) T Q0[TL::ELEMS];
-  __shared__ __attribute__((aligned(1024))) T G0[TL::ELEMS];
-  __shared__ __attribute__((aligned(1024))) T Q1[TL::ELEMS];
-  __shared__ __attribute__((aligned(1024))) T G1[TL::ELEMS];
-  __shared__ __attribute__((aligned(256))) float lse0[64], lse1[64], dl0[64], dl1[64];
-  __shared__ __attribute__((aligned(256))) int klo0[64], klo1[64];
-  // P handed from role A to role B: [key group][value quad][lane][4]
-  __shared__ __attribute__((aligned(256))) f32x4 pex[C::NKG][4][64];
-  __shared__ int n_tiles_s, item_s;
-
-  // Work distribution: a persistent grid (one workgroup per CU slot) pulls
-  // items (kv head, batch row, key tile) from NQ queues; workgroup w serves
-  // queue w % NQ, which holds the flat items f = q, q + NQ, ...  Flat items
-  // list the kv head fastest over the (batch row, key tile) pairs in the order
-  // of decreasing work computed by dkdv_order_kernel, so with 8 queues (one
-  // per XCD, as consecutive workgroups land on consecutive XCDs) each kv head
-  // stays on one XCD, whose L2 then holds the Q/dO rows its key tiles share,
-  // and each XCD runs its longest tiles first.  Which workgroup computes an
-  // item never changes the result.
+  T* const Q0 = sm.Q0; T* const G0 = sm.G0; T* const Q1 = sm.Q1; T* const G1 = sm.G1;
+  float* const lse0 = sm.lse0; float* const lse1 = sm.lse1; float* const dl0 = sm.dl0; float* const dl1 = sm.dl1;
+  int* const klo0 = sm.klo0; int* const klo1 = sm.klo1;
+  auto& pex = sm.pex;
+  int& n_tiles_s = sm.n_tiles_s;
   const int grp = p.Hq / p.Hkv;
   const int n_kt = (p.S + C::BK - 1) / C::BK;
-  const int total = p.B * n_kt * p.Hkv;
-  const int nq = min(kNumQueues, (int)gridDim.x);
-  const int qcls = blockIdx.x % nq;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
   const int kg = w % C::NKG;                      // key group
   const bool role_a = w < C::NKG;                 // A: S, P, dV   B: dP, dS, dK
   const int off = p.S - p.L;
   const TileAccess<T, TL> acc(ln, lane);
   const TileDma<T, C::BQ, D, C::NW> dma;   // Q and dO tiles share one layout
-
-  for (;;) {
-  if (tid == 0) item_s = qcls + nq * atomicAdd(&p.counters[qcls], 1);
-  __syncthreads();
-  const int f = item_s;
-  if (f >= total) break;
   const int kvh = f % p.Hkv;
   const int code = p.order[f / p.Hkv];
   const int b = code / n_kt, kt = code % n_kt;
@@ -122,14 +116,29 @@ __global__ __launch_bounds__((DkvCfg<T, D>::NT), (DkvCfg<T, D>::OCC)) void bwd_d
       if (p.window >= 0) bsi = max(bsi, off + i - p.window);
       pred = bsi <= jmax;
     }
-    const int cnt = __syncthreads_count(pred);
-    if (tid == 0) n_tiles_s += cnt;
-    if (cnt < C::NT) break;
+    // count through the waves' ballots (no extra LDS beyond n_tiles_s)
+    const int wc = __popcll(__ballot(pred));
+    if (lane == 0 && wc) atomicAdd(&n_tiles_s, wc);
+    __syncthreads();
+    if (n_tiles_s < base - t_first + C::NT) break;   // the prefix ended in this chunk
     __syncthreads();
   }
   __syncthreads();
   const int n_t = n_tiles_s;
   const int n_iter = grp * n_t;      // (q head of the group, query tile) steps
+  if (n_iter == 0) {
+    // no query reaches these keys: dK = dV = 0 over the whole tile (16-byte stores)
+    constexpr int V16 = 16 / (int)sizeof(T);
+    const int n16 = (min(C::BK, p.S - j0) * D) / V16;
+    const size_t base = (((size_t)b * p.Hkv + kvh) * p.S + j0) * D;
+    uint4* dkp = reinterpret_cast<uint4*>(reinterpret_cast<T*>(p.dk) + base);
+    uint4* dvp = reinterpret_cast<uint4*>(reinterpret_cast<T*>(p.dv) + base);
+    for (int x = tid; x < n16; x += C::NT) {
+      dkp[x] = uint4{0u, 0u, 0u, 0u};
+      dvp[x] = uint4{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
 
   const T* kvq = reinterpret_cast<const T*>(p.q);
   const T* kvd = reinterpret_cast<const T*>(p.dout);
@@ -267,10 +276,8 @@ __global__ __launch_bounds__((DkvCfg<T, D>::NT), (DkvCfg<T, D>::OCC)) void bwd_d
       }
     }
   }
-  // every wave is done with this item's LDS buffers and item_s before the next fetch
-  __syncthreads();
-  }
 }
+
 
 // ---------------------------------------------------------------- dQ
 
@@ -290,36 +297,47 @@ struct DqCfg {
   static constexpr int AHEAD = (sizeof(T) != 2) ? 0 : (D <= 128) ? 4 : 2;
 };
 
+// LDS of one dQ item: two K/V tile pairs (one filled by DMA while the other is
+// read) and the P / dP exchange of each query group.
 template <typename T, int D>
-__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
+struct DqSmem {
+  typedef Tile<T, DqCfg<T, D>::BN, D> TL;
+  static constexpr int NSB = DqCfg<T, D>::BN / 32;
+  __attribute__((aligned(1024))) T K0[TL::ELEMS];
+  __attribute__((aligned(1024))) T V0[TL::ELEMS];
+  __attribute__((aligned(1024))) T K1[TL::ELEMS];
+  __attribute__((aligned(1024))) T V1[TL::ELEMS];
+  __attribute__((aligned(256))) f32x4 xch[2][4][NSB][4][64];  // [P | dP][group][block][value quad][lane][4]
+};
+
+// One dQ item f: (kv head, q head of its group, batch row, query tile) with
+// the kv head fastest and the (batch row, query tile) pairs longest band first.
+template <typename T, int D>
+__device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, int f) {
   typedef DqCfg<T, D> C;
   typedef Tile<T, C::BN, D> TL;
   typedef typename Frag<T>::type F;
   constexpr int NSB = C::BN / 32;
   constexpr int NM = C::BN / 16;
   constexpr int DH = D / 64;   // 32-wide d blocks of dQ per role
-  __shared__ __attribute__((aligned(1024))) T K0[TL::ELEMS];
-  __shared__ __attribute__((aligned(1024))) T V0[TL::ELEMS];
-  __shared__ __attribute__((aligned(1024))) T K1[TL::ELEMS];
-  __shared__ __attribute__((aligned(1024))) T V1[TL::ELEMS];
-  // P (from A) and dP (from B) per query group: [group][block][value quad][lane][4]
-  __shared__ __attribute__((aligned(256))) f32x4 xch[2][4][NSB][4][64];
-  f32x4 (*xp)[NSB][4][64] = xch[0];
-  f32x4 (*xdp)[NSB][4][64] = xch[1];
-  // prologue scratch, dead before the first exchange (a barrier separates them)
-  float (*dls)[64] = reinterpret_cast<float (*)[64]>(&xch[1][0][0][0][0]);
-  int (*red)[2] = reinterpret_cast<int (*)[2]>(&xch[0][0][0][0][0]);
-
-  // same work order as the forward: kv group fastest, then q head, then query tile
+  T* const K0 = sm.K0; T* const V0 = sm.V0; T* const K1 = sm.K1; T* const V1 = sm.V1;
+  f32x4 (*xp)[NSB][4][64] = sm.xch[0];
+  f32x4 (*xdp)[NSB][4][64] = sm.xch[1];
+  // wave bounds: scratch at the start of xp, dead before the first exchange
+  // (barriers separate them)
+  int (*red)[2] = reinterpret_cast<int (*)[2]>(&sm.xch[0][0][0][0][0]);
   const int grp = p.Hq / p.Hkv;
-  const int ngroups = p.B * p.Hkv;
-  const int gid = blockIdx.x % ngroups, rest = blockIdx.x / ngroups;
-  const int b = gid / p.Hkv, kvh = gid % p.Hkv;
-  const int h = kvh * grp + rest % grp, qt = rest / grp;
+  const int n_qt = (p.L + C::BM - 1) / C::BM;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
   const int qg = w & 3;                 // query group
-  const bool role_a = w < 4;            // A: Q, S, P   B: dO, dP, Delta
+  const bool role_a = w < 4;            // A: Q, S, P   B: dO, dP
   const int off = p.S - p.L;
+  const TileAccess<T, TL> acc(ln, lane);
+  const TileDma<T, C::BN, D, C::NW> dma;   // K and V tiles share one layout
+  const int kvh = f % p.Hkv;
+  const int h = kvh * grp + (f / p.Hkv) % grp;
+  const int code = p.qorder[f / p.Hq];
+  const int b = code / n_qt, qt = code % n_qt;
   const int i = qt * C::BM + 32 * qg + ln;
   const bool in_range = i < p.L;
   const int pos = off + i;
@@ -349,34 +367,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
       if (!in_range) rf[kk] = zero_frag<T>();
     }
   }
-  // Delta_i = dO_i . O_i with O the stored value plus its saved rounding
-  // residual (role B); published for the dK/dV pass, which runs after this one.
-  if (!role_a) {
-    const T* op = reinterpret_cast<const T*>(p.o) + qrow_c * D;
-    const T* olp = p.o_lo ? reinterpret_cast<const T*>(p.o_lo) + qrow_c * D : nullptr;
-    float part = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const F ov = load_frag<T>(op + 16 * kk + 8 * g);
-      const F ol = olp ? load_frag<T>(olp + 16 * kk + 8 * g) : zero_frag<T>();
-#pragma unroll
-      for (int t = 0; t < 8; ++t) part += to_f32(rf[kk][t]) * (to_f32(ov[t]) + to_f32(ol[t]));
-    }
-    float dl = part + __shfl_xor(part, 32);
-    if (!real) dl = 0.f;
-    if (in_range && g == 0) p.delta[qrow] = dl;
-    if (g == 0) dls[qg][ln] = dl;
-  }
+  // Delta of the row (bwd_delta_kernel), 0 for padding rows
+  const float dl = real ? p.delta[qrow_c] : 0.f;
   const float lse2 = real ? p.lse[qrow_c] * kLog2e : 0.f;
   __syncthreads();
-  const float dl = dls[qg][ln];
   int kstart = INT_MAX, kend = INT_MIN;
 #pragma unroll
   for (int x = 0; x < C::NW; ++x) { kstart = min(kstart, red[x][0]); kend = max(kend, red[x][1]); }
 
   const T* __restrict__ kbase = reinterpret_cast<const T*>(p.k) + ((size_t)b * p.Hkv + kvh) * p.S * D;
   const T* __restrict__ vbase = reinterpret_cast<const T*>(p.v) + ((size_t)b * p.Hkv + kvh) * p.S * D;
-  const TileDma<T, C::BN, D, C::NW> dma;   // K and V tiles share one layout
   auto load = [&](T* Ks, T* Vs, int j0) {
     const int nv = min(C::BN, p.S - j0);
     dma.issue(Ks, kbase + (size_t)j0 * D, nv);
@@ -384,7 +384,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   };
   if (kstart < kend) load(K0, V0, kstart);
 
-  const TileAccess<T, TL> acc(ln, lane);
   const int dh0 = role_a ? 0 : DH;      // first 32-wide d block of this wave's dQ half
   f32x16 dqacc[DH];
 #pragma unroll
@@ -474,77 +473,71 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     step(K1, V1, j0 + C::BN);
   }
 
-  if (!in_range) return;
-  T* dqp = reinterpret_cast<T*>(p.dq) + qrow * D;
+  if (in_range) {
+    T* dqp = reinterpret_cast<T*>(p.dq) + qrow * D;
 #pragma unroll
-  for (int d = 0; d < DH; ++d) {
+    for (int d = 0; d < DH; ++d) {
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      store_quad<T>(dqp + 32 * (dh0 + d) + 8 * rq + 4 * g, dqacc[d][4 * rq] * p.scale,
-                    dqacc[d][4 * rq + 1] * p.scale, dqacc[d][4 * rq + 2] * p.scale,
-                    dqacc[d][4 * rq + 3] * p.scale);
+      for (int rq = 0; rq < 4; ++rq) {
+        store_quad<T>(dqp + 32 * (dh0 + d) + 8 * rq + 4 * g, dqacc[d][4 * rq] * p.scale,
+                      dqacc[d][4 * rq + 1] * p.scale, dqacc[d][4 * rq + 2] * p.scale,
+                      dqacc[d][4 * rq + 3] * p.scale);
+      }
     }
   }
 }
 
-// ---------------------------------------------------------------- launch
 
-// ---------------------------------------------------------------- dK/dV work order
+// ---------------------------------------------------------------- Delta
 
-// Items (batch row, key tile) sorted by decreasing work -- the number of
-// 32-row query tiles whose bands reach the tile, counted exactly as the dK/dV
-// kernel counts them -- with ties in decreasing tile order.  One workgroup:
-// exact counts by binary search over the nondecreasing band starts, then a
-// bitonic sort of (work, index) keys in LDS.  More than kOrderMax items keep
-// the natural order.
+// Delta_i = dO_i . O_i for every row (b, h, i), with O the stored value plus
+// its saved rounding residual (fp32-accurate); 0 for padding rows.  Two rows
+// per wave, 32 lanes per row, D / 32 consecutive elements per lane.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
+  constexpr int E = D / 32;
+  const int lane = threadIdx.x & 63, l32 = lane & 31;
+  const long long n_rows = (long long)p.B * p.Hq * p.L;
+  const long long row = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + (lane >> 5);
+  const bool in = row < n_rows;
+  const long long rr = in ? row : n_rows - 1;
+  typedef T VE __attribute__((ext_vector_type(E)));   // the lane's E elements, one vector load
+  const VE dv = *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.dout) + rr * D + l32 * E);
+  const VE ov = *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.o) + rr * D + l32 * E);
+  VE lv = ov;
+  if (p.o_lo) lv = *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.o_lo) + rr * D + l32 * E);
+  float part = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) part += to_f32(dv[e]) * (to_f32(ov[e]) + (p.o_lo ? to_f32(lv[e]) : 0.f));
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) part += __shfl_xor(part, o);
+  if (in && l32 == 0) {
+    const int i = (int)(row % p.L), b = (int)(row / ((long long)p.Hq * p.L));
+    const bool real = p.row_klo[(size_t)b * p.L + i] <= p.S - p.L + i;
+    p.delta[row] = real ? part : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------- work order
+
+// Items of both passes sorted by decreasing work, ties in decreasing item
+// order, in one workgroup (bitonic sort of (work, index) keys in LDS; more than
+// kOrderMax items keep the natural order):
+//   dK/dV: (batch row, key tile) -> number of 32-row query tiles whose bands
+//          reach the tile, counted exactly as the pass counts them (binary
+//          search over the nondecreasing band starts);
+//   dQ:    (batch row, query tile) -> key range of its rows, from the first
+//          row's band start to the last row's position (an estimate when the
+//          first rows are padding -- the order only affects speed).
+// Also empties the work queues of the backward kernel.
 constexpr int kOrderNT = 1024;
 constexpr int kOrderMax = 8192;
 constexpr int kOrderBandMax = 4096;   // query-tile band starts staged in LDS
 
-template <int BK, int BQ>
-__global__ __launch_bounds__(kOrderNT) void dkdv_order_kernel(BwdParams p) {
-  __shared__ unsigned long long keys[kOrderMax];
-  __shared__ int bst[kOrderBandMax];
+// Sort keys[0, N) ascending (N a power of two) and emit the item indices they
+// carry (key = (2^32 - 1 - work) << 32 | (n - 1 - item)).
+__device__ void order_by_work(unsigned long long* keys, int n, int N, int* out) {
   const int tid = threadIdx.x;
-  const int n_kt = (p.S + BK - 1) / BK;
-  const int n = p.B * n_kt;
-  if (tid < kNumQueues) p.counters[tid] = 0;  // the dK/dV pass's work queues start empty
-  if (n > kOrderMax) {
-    for (int i = tid; i < n; i += kOrderNT) p.order[i] = i;
-    return;
-  }
-  const int off = p.S - p.L;
-  const int n_q_tiles = (p.L + BQ - 1) / BQ;
-  // band start of each query tile's first row (nondecreasing along a row)
-  auto band_start_g = [&](int b, int t) {
-    const int r = t * BQ;
-    const int bq = max(0, p.row_klo[(size_t)b * p.L + r]);
-    return p.window >= 0 ? max(bq, off + r - p.window) : bq;
-  };
-  const bool staged = p.B * n_q_tiles <= kOrderBandMax;
-  if (staged)
-    for (int x = tid; x < p.B * n_q_tiles; x += kOrderNT) bst[x] = band_start_g(x / n_q_tiles, x % n_q_tiles);
-  __syncthreads();
-  int N = 1;
-  while (N < n) N <<= 1;
-  for (int i = tid; i < N; i += kOrderNT) {
-    unsigned long long key = ~0ull;  // padding sorts last
-    if (i < n) {
-      const int b = i / n_kt, kt = i % n_kt;
-      const int jmax = min(kt * BK + BK, p.S) - 1;
-      const int t_first = max(0, kt * BK - off) / BQ;
-      int lo = t_first, hi = n_q_tiles;  // first tile in [lo, hi) whose band starts after jmax
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        const int bsm = staged ? bst[b * n_q_tiles + mid] : band_start_g(b, mid);
-        if (bsm <= jmax) lo = mid + 1;
-        else hi = mid;
-      }
-      const unsigned work = (unsigned)(lo - t_first);
-      key = ((unsigned long long)(0xFFFFFFFFu - work) << 32) | (unsigned)(n - 1 - i);
-    }
-    keys[i] = key;
-  }
   __syncthreads();
   for (int k = 2; k <= N; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
@@ -561,53 +554,195 @@ __global__ __launch_bounds__(kOrderNT) void dkdv_order_kernel(BwdParams p) {
       __syncthreads();
     }
   }
-  for (int i = tid; i < n; i += kOrderNT) p.order[i] = n - 1 - (int)(unsigned)(keys[i] & 0xFFFFFFFFu);
+  for (int i = tid; i < n; i += kOrderNT) out[i] = n - 1 - (int)(unsigned)(keys[i] & 0xFFFFFFFFu);
+  __syncthreads();
+}
+
+__device__ __forceinline__ unsigned long long work_key(unsigned work, int i, int n) {
+  return ((unsigned long long)(0xFFFFFFFFu - work) << 32) | (unsigned)(n - 1 - i);
+}
+
+template <int BK, int BQ, int BM>
+__global__ __launch_bounds__(kOrderNT) void work_order_kernel(BwdParams p, int modes) {
+  __shared__ unsigned long long keys[kOrderMax];
+  __shared__ int bst[kOrderBandMax];
+  const int tid = threadIdx.x;
+  const int off = p.S - p.L;
+  if (tid < kNumQueues) p.counters[tid] = 0;  // the backward kernel's work queues start empty
+  if (modes & 1) {
+    const int n_kt = (p.S + BK - 1) / BK;
+    const int n = p.B * n_kt;
+    if (n > kOrderMax) {
+      for (int i = tid; i < n; i += kOrderNT) p.order[i] = i;
+    } else {
+      const int n_q_tiles = (p.L + BQ - 1) / BQ;
+      // band start of each query tile's first row (nondecreasing along a row)
+      auto band_start_g = [&](int b, int t) {
+        const int r = t * BQ;
+        const int bq = max(0, p.row_klo[(size_t)b * p.L + r]);
+        return p.window >= 0 ? max(bq, off + r - p.window) : bq;
+      };
+      const bool staged = p.B * n_q_tiles <= kOrderBandMax;
+      if (staged)
+        for (int x = tid; x < p.B * n_q_tiles; x += kOrderNT) bst[x] = band_start_g(x / n_q_tiles, x % n_q_tiles);
+      __syncthreads();
+      int N = 1;
+      while (N < n) N <<= 1;
+      for (int i = tid; i < N; i += kOrderNT) {
+        unsigned long long key = ~0ull;  // padding sorts last
+        if (i < n) {
+          const int b = i / n_kt, kt = i % n_kt;
+          const int jmax = min(kt * BK + BK, p.S) - 1;
+          const int t_first = max(0, kt * BK - off) / BQ;
+          int lo = t_first, hi = n_q_tiles;  // first tile in [lo, hi) whose band starts after jmax
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            const int bsm = staged ? bst[b * n_q_tiles + mid] : band_start_g(b, mid);
+            if (bsm <= jmax) lo = mid + 1;
+            else hi = mid;
+          }
+          key = work_key((unsigned)(lo - t_first), i, n);
+        }
+        keys[i] = key;
+      }
+      order_by_work(keys, n, N, p.order);
+    }
+  }
+  if (modes & 2) {
+    const int n_qt = (p.L + BM - 1) / BM;
+    const int n = p.B * n_qt;
+    if (n > kOrderMax) {
+      for (int i = tid; i < n; i += kOrderNT) p.qorder[i] = i;
+    } else {
+      int N = 1;
+      while (N < n) N <<= 1;
+      for (int i = tid; i < N; i += kOrderNT) {
+        unsigned long long key = ~0ull;
+        if (i < n) {
+          const int b = i / n_qt, qt = i % n_qt;
+          const int r0 = qt * BM, r1 = min(p.L, r0 + BM) - 1;
+          int bq = max(0, p.row_klo[(size_t)b * p.L + r0]);
+          if (p.window >= 0) bq = max(bq, off + r0 - p.window);
+          key = work_key((unsigned)max(0, off + r1 + 1 - bq), i, n);
+        }
+        keys[i] = key;
+      }
+      order_by_work(keys, n, N, p.qorder);
+    }
+  }
 }
 
 size_t dkdv_order_elems(int B, int S) { return (size_t)B * ((S + 31) / 32); }
+size_t dq_order_elems(int B, int L) { return (size_t)B * ((L + 31) / 32); }
 
-template <typename T, int D>
-static hipError_t launch_dq_t(const BwdParams& p, hipStream_t s) {
-  typedef DqCfg<T, D> C;
-  dim3 grid((unsigned)((p.L + C::BM - 1) / C::BM) * p.Hq * p.B);
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D>), grid, dim3(C::NT), 0, s, p);
-  return hipGetLastError();
+// ---------------------------------------------------------------- backward kernel
+
+// A persistent grid (one workgroup per CU) drains the items of the selected
+// passes (MODE bit 0: dK/dV, bit 1: dQ) from kNumQueues queues; workgroup w
+// serves queue w % NQ, which holds the flat items f = q, q + NQ, ...  The flat
+// list is the dK/dV items (longest first) followed by the dQ items (longest
+// first), each with the kv head fastest: with 8 queues -- one per XCD, as
+// consecutive workgroups land on consecutive XCDs -- every kv head stays on one
+// XCD, whose L2 then holds the K/V and Q/dO rows its items share.  Running
+// both passes in one grid lets the shorter dQ items fill the tail of the dK/dV
+// items.  Which workgroup computes an item never changes the result.
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(512, 1) void bwd_kernel(BwdParams p) {
+  static_assert(DkvCfg<T, D>::NT == 512 && DqCfg<T, D>::NT == 512, "one block shape for both passes");
+  __shared__ union BwdSmem {
+    DkvSmem<T, D> kv;
+    DqSmem<T, D> q;
+  } sm;
+  const int n_kv = (MODE & 1) ? p.B * ((p.S + DkvCfg<T, D>::BK - 1) / DkvCfg<T, D>::BK) * p.Hkv : 0;
+  const int n_q = (MODE & 2) ? p.B * ((p.L + DqCfg<T, D>::BM - 1) / DqCfg<T, D>::BM) * p.Hq : 0;
+  const int total = n_kv + n_q;
+  const int nq = min(kNumQueues, (int)gridDim.x);
+  const int qcls = blockIdx.x % nq;
+  int* const slot = reinterpret_cast<int*>(&sm);  // the fetched item, between items only
+  for (;;) {
+    if (threadIdx.x == 0) *slot = qcls + nq * atomicAdd(&p.counters[qcls], 1);
+    __syncthreads();
+    const int f = *slot;
+    __syncthreads();  // every thread has the item before the item reuses the LDS
+    if (f >= total) break;
+    if constexpr (MODE == 1) {
+      dkdv_item<T, D>(p, sm.kv, f);
+    } else if constexpr (MODE == 2) {
+      dq_item<T, D>(p, sm.q, f);
+    } else {
+      if (f < n_kv) dkdv_item<T, D>(p, sm.kv, f);
+      else dq_item<T, D>(p, sm.q, f - n_kv);
+    }
+    __syncthreads();  // this item's LDS is dead before the next fetch
+  }
 }
 
-template <typename T, int D>
-static hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t s) {
-  typedef DkvCfg<T, D> C;
-  static_assert(C::BK >= 32, "the work-order array is sized for tiles of at least 32 keys");
-  hipLaunchKernelGGL((dkdv_order_kernel<C::BK, C::BQ>), dim3(1), dim3(kOrderNT), 0, s, p);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // persistent grid: one workgroup per CU slot, at most one per item
+// Compute units of the current device (the persistent grid's size).
+static int device_cu_count() {
   int dev = 0, n_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
     n_cu = 256;
-  const long long items = (long long)((p.S + C::BK - 1) / C::BK) * p.Hkv * p.B;
-  dim3 grid((unsigned)std::min<long long>(items, (long long)n_cu * C::OCC));
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), grid, dim3(C::NT), 0, s, p);
+  return n_cu;
+}
+
+template <typename T, int D>
+static hipError_t launch_delta_t(const BwdParams& p, hipStream_t s) {
+  const long long rows = (long long)p.B * p.Hq * p.L;
+  hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-#define NB_DISPATCH(fn)                                      \
-  if (f32) {                                                 \
-    if (D == 64) return fn<float, 64>(p, s);                 \
-    if (D == 128) return fn<float, 128>(p, s);               \
-    if (D == 256) return fn<float, 256>(p, s);               \
-  } else {                                                   \
-    if (D == 64) return fn<bf16, 64>(p, s);                  \
-    if (D == 128) return fn<bf16, 128>(p, s);                \
-    if (D == 256) return fn<bf16, 256>(p, s);                \
-  }                                                          \
+template <typename T, int D>
+static hipError_t launch_order_t(const BwdParams& p, int modes, hipStream_t s) {
+  typedef DkvCfg<T, D> CK;
+  typedef DqCfg<T, D> CQ;
+  static_assert(CK::BK >= 32 && CQ::BM >= 32, "the work-order arrays are sized for tiles of >= 32");
+  hipLaunchKernelGGL((work_order_kernel<CK::BK, CK::BQ, CQ::BM>), dim3(1), dim3(kOrderNT), 0, s, p, modes);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int MODE>
+static hipError_t launch_main_t(const BwdParams& p, hipStream_t s) {
+  const long long n_kv = (MODE & 1) ? (long long)p.B * ((p.S + DkvCfg<T, D>::BK - 1) / DkvCfg<T, D>::BK) * p.Hkv : 0;
+  const long long n_q = (MODE & 2) ? (long long)p.B * ((p.L + DqCfg<T, D>::BM - 1) / DqCfg<T, D>::BM) * p.Hq : 0;
+  dim3 grid((unsigned)std::min<long long>(n_kv + n_q, (long long)device_cu_count()));
+  hipLaunchKernelGGL((bwd_kernel<T, D, MODE>), grid, dim3(512), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_t(const BwdParams& p, int what, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  switch (what) {
+    case kBwdPrep:   // Delta + work orders of both passes
+      e = launch_delta_t<T, D>(p, s);
+      return e != hipSuccess ? e : launch_order_t<T, D>(p, 3, s);
+    case kBwdMain:
+      return launch_main_t<T, D, 3>(p, s);
+    case kBwdDq:     // Delta, then the dQ pass alone
+      e = launch_delta_t<T, D>(p, s);
+      if (e == hipSuccess) e = launch_order_t<T, D>(p, 2, s);
+      return e != hipSuccess ? e : launch_main_t<T, D, 2>(p, s);
+    case kBwdDkdv:   // the dK/dV pass alone (Delta from an earlier dQ / prep call)
+      e = launch_order_t<T, D>(p, 1, s);
+      return e != hipSuccess ? e : launch_main_t<T, D, 1>(p, s);
+  }
   return hipErrorInvalidValue;
+}
 
-hipError_t launch_bwd_dq(const BwdParams& p, int D, bool f32, hipStream_t s) { NB_DISPATCH(launch_dq_t) }
-hipError_t launch_bwd_dkdv(const BwdParams& p, int D, bool f32, hipStream_t s) { NB_DISPATCH(launch_dkdv_t) }
-
-#undef NB_DISPATCH
+hipError_t launch_bwd(const BwdParams& p, int D, bool f32, int what, hipStream_t s) {
+  if (f32) {
+    if (D == 64) return launch_t<float, 64>(p, what, s);
+    if (D == 128) return launch_t<float, 128>(p, what, s);
+    if (D == 256) return launch_t<float, 256>(p, what, s);
+  } else {
+    if (D == 64) return launch_t<bf16, 64>(p, what, s);
+    if (D == 128) return launch_t<bf16, 128>(p, what, s);
+    if (D == 256) return launch_t<bf16, 256>(p, what, s);
+  }
+  return hipErrorInvalidValue;
+}
 
 // ---------------------------------------------------------------- owner flags
 

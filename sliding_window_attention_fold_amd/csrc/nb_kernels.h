@@ -48,7 +48,8 @@ struct BwdParams {
   const float* lse;
   float* delta;
   int* order;        // workspace: dK/dV key tiles (b * n_tiles + tile) by decreasing work
-  int* counters;     // workspace: kNumQueues work-queue counters of the dK/dV pass
+  int* counters;     // workspace: kNumQueues work-queue counters of the backward kernel
+  int* qorder;       // workspace: dQ query tiles (b * n_tiles + tile) by decreasing work
   const int32_t* row_klo;
   void* dq;
   void* dk;
@@ -69,11 +70,15 @@ struct OwnerParams {
 
 hipError_t launch_segment_build(const SegParams& p, hipStream_t s);
 hipError_t launch_attn_fwd(const FwdParams& p, int D, bool f32, hipStream_t s);
-hipError_t launch_bwd_dq(const BwdParams& p, int D, bool f32, hipStream_t s);
-hipError_t launch_bwd_dkdv(const BwdParams& p, int D, bool f32, hipStream_t s);
-// Elements of the dK/dV work-order array for (B, S) (enough for the smallest
-// key tile), followed in the workspace by kNumQueues queue counters.
+// Backward launches: kBwdPrep = Delta + work orders; kBwdMain = both passes in
+// one persistent grid (after kBwdPrep); kBwdDq = Delta + dQ pass; kBwdDkdv =
+// dK/dV pass (after kBwdPrep or kBwdDq on the same workspace).
+enum { kBwdPrep = 0, kBwdMain = 1, kBwdDq = 2, kBwdDkdv = 3 };
+hipError_t launch_bwd(const BwdParams& p, int D, bool f32, int what, hipStream_t s);
+// Elements of the dK/dV and dQ work-order arrays (enough for tiles of >= 32);
+// the workspace also holds kNumQueues queue counters.
 size_t dkdv_order_elems(int B, int S);
+size_t dq_order_elems(int B, int L);
 constexpr int kNumQueues = 8;
 hipError_t launch_owner_flags(const OwnerParams& p, hipStream_t s);
 

@@ -139,6 +139,11 @@ int nb_attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_re
 
 namespace {
 size_t delta_bytes(int B, int Hq, int L) { return (((size_t)B * Hq * L * sizeof(float)) + 255) & ~(size_t)255; }
+// dK/dV work order, the backward kernel's queue counters, dQ work order
+size_t order_bytes(int B, int L, int S) {
+  return ((nb::dkdv_order_elems(B, S) + nb::kNumQueues + nb::dq_order_elems(B, L)) * sizeof(int) + 255) &
+         ~(size_t)255;
+}
 }  // namespace
 
 size_t nb_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, int dtype) {
@@ -146,8 +151,7 @@ size_t nb_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, 
   (void)D;
   (void)dtype;
   if (B < 1 || Hq < 1 || L < 1 || S < 1) return 0;
-  const size_t order = ((nb::dkdv_order_elems(B, S) + nb::kNumQueues) * sizeof(int) + 255) & ~(size_t)255;
-  return delta_bytes(B, Hq, L) + order;
+  return delta_bytes(B, Hq, L) + order_bytes(B, L, S);
 }
 
 }  // extern "C"
@@ -168,6 +172,7 @@ nb::BwdParams bwd_params(const void* dout, const void* q, const void* k, const v
   p.delta = reinterpret_cast<float*>(ws);
   p.order = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + delta_bytes(B, Hq, L));
   p.counters = p.order + nb::dkdv_order_elems(B, S);
+  p.qorder = p.counters + nb::kNumQueues;
   p.row_klo = seg_buf + nb::seg_layout(B, L, S).row_klo;
   p.dq = dq;
   p.dk = dk;
@@ -224,20 +229,46 @@ int nb_attn_bwd_dq(const void* dout, const void* q, const void* k, const void* v
   if (ws_bytes < nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype)) return NB_ERR_WORKSPACE;
   const nb::BwdParams p = bwd_params(dout, q, k, v, o, o_resid, lse, seg_buf, B, Hq, Hkv, L, S, scale,
                                      window_left, dq, nullptr, nullptr, ws);
-  return map_hip(nb::launch_bwd_dq(p, D, dtype == NB_F32, (hipStream_t)stream));
+  return map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdDq, (hipStream_t)stream));
 }
 
 int nb_attn_bwd_dkdv(const void* dout, const void* q, const void* k, const void* v, const float* lse,
                      const int32_t* seg_buf, int B, int Hq, int Hkv, int L, int S, int D, float scale,
-                     int window_left, int dtype, void* dk, void* dv, const void* ws, size_t ws_bytes,
+                     int window_left, int dtype, void* dk, void* dv, void* ws, size_t ws_bytes,
                      void* stream) {
   const void* ptrs[] = {dout, q, k, v, lse, seg_buf, dk, dv, ws};
   int st = attn_common_checks(ptrs, 9, B, Hq, Hkv, L, S, D, scale, dtype);
   if (st != NB_OK) return st;
   if (ws_bytes < nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype)) return NB_ERR_WORKSPACE;
   const nb::BwdParams p = bwd_params(dout, q, k, v, nullptr, nullptr, lse, seg_buf, B, Hq, Hkv, L, S, scale,
-                                     window_left, nullptr, dk, dv, const_cast<void*>(ws));
-  return map_hip(nb::launch_bwd_dkdv(p, D, dtype == NB_F32, (hipStream_t)stream));
+                                     window_left, nullptr, dk, dv, ws);
+  return map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdDkdv, (hipStream_t)stream));
+}
+
+int nb_attn_bwd_prep(const void* dout, const void* o, const void* o_resid, const int32_t* seg_buf, int B, int Hq,
+                     int Hkv, int L, int S, int D, int window_left, int dtype, void* ws, size_t ws_bytes,
+                     void* stream) {
+  const void* ptrs[] = {dout, o, seg_buf, ws};
+  int st = attn_common_checks(ptrs, 4, B, Hq, Hkv, L, S, D, 1.0f, dtype);
+  if (st != NB_OK) return st;
+  if (o_resid != nullptr && !aligned16(o_resid)) return NB_ERR_INVALID_ARG;
+  if (ws_bytes < nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype)) return NB_ERR_WORKSPACE;
+  const nb::BwdParams p = bwd_params(dout, nullptr, nullptr, nullptr, o, o_resid, nullptr, seg_buf, B, Hq, Hkv, L,
+                                     S, 1.0f, window_left, nullptr, nullptr, nullptr, ws);
+  return map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdPrep, (hipStream_t)stream));
+}
+
+int nb_attn_bwd_main(const void* dout, const void* q, const void* k, const void* v, const float* lse,
+                     const int32_t* seg_buf, int B, int Hq, int Hkv, int L, int S, int D, float scale,
+                     int window_left, int dtype, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                     void* stream) {
+  const void* ptrs[] = {dout, q, k, v, lse, seg_buf, dq, dk, dv, ws};
+  int st = attn_common_checks(ptrs, 10, B, Hq, Hkv, L, S, D, scale, dtype);
+  if (st != NB_OK) return st;
+  if (ws_bytes < nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype)) return NB_ERR_WORKSPACE;
+  const nb::BwdParams p = bwd_params(dout, q, k, v, nullptr, nullptr, lse, seg_buf, B, Hq, Hkv, L, S, scale,
+                                     window_left, dq, dk, dv, ws);
+  return map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdMain, (hipStream_t)stream));
 }
 
 int nb_owner_attended(const int32_t* seg_buf, const int32_t* folded_ids, int B, int L, int S,
@@ -263,9 +294,9 @@ int nb_attn_bwd(const void* dout, const void* q, const void* k, const void* v, c
   hipStream_t s = (hipStream_t)stream;
   const nb::BwdParams p = bwd_params(dout, q, k, v, o, o_resid, lse, seg_buf, B, Hq, Hkv, L, S, scale,
                                      window_left, dq, dk, dv, ws);
-  st = map_hip(nb::launch_bwd_dq(p, D, dtype == NB_F32, s));
+  st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdPrep, s));
   if (st != NB_OK) return st;
-  st = map_hip(nb::launch_bwd_dkdv(p, D, dtype == NB_F32, s));
+  st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdMain, s));
   if (st != NB_OK) return st;
   return launch_owner(seg_buf, folded_ids, B, L, S, owner_off, n_owner, owner_attended, s);
 }

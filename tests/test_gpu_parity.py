@@ -157,6 +157,50 @@ def test_deterministic_bitwise():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("name", ["w2s", "w5s"])
+def test_backward_entry_points_agree(name):
+    """nb_attn_bwd, prep + main, and dq + dkdv called separately (twice, so a
+    reused workspace is covered) give bit-identical dQ, dK, dV."""
+    import ctypes
+
+    w = SMALL[name]
+    inp = workload_inputs(w, "bf16")
+    say(f"[entry points] {name}")
+    seg, out, lse, res = run_gpu(inp)
+    dev = torch.device("cuda:0")
+    lib = _lib.load()
+    q, k, v, do = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v, inp.do))
+    _, saved = nb.attn_fwd(q, k, v, seg)
+    B, Hq, L, D = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    wsb = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, _lib.NB_BF16)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
+    sc = D ** -0.5
+    W = inp.window
+    for rep in range(2):
+        dq = torch.full_like(q, float("nan"))
+        dk = torch.full_like(k, float("nan"))
+        dv = torch.full_like(v, float("nan"))
+        _lib.check(lib.nb_attn_bwd_prep(P(do), P(saved.out), P(saved.out_resid), P(seg.buf), B, Hq, Hkv, L, S, D, W,
+                                        _lib.NB_BF16, P(ws), wsb, sp), "prep")
+        _lib.check(lib.nb_attn_bwd_main(P(do), P(q), P(k), P(v), P(saved.lse), P(seg.buf), B, Hq, Hkv, L, S, D, sc,
+                                        W, _lib.NB_BF16, P(dq), P(dk), P(dv), P(ws), wsb, sp), "main")
+        torch.cuda.synchronize()
+        assert torch.equal(dq, res.dq) and torch.equal(dk, res.dk) and torch.equal(dv, res.dv), f"prep+main {rep}"
+        dq2 = torch.full_like(q, float("nan"))
+        dk2 = torch.full_like(k, float("nan"))
+        dv2 = torch.full_like(v, float("nan"))
+        _lib.check(lib.nb_attn_bwd_dq(P(do), P(q), P(k), P(v), P(saved.out), P(saved.out_resid), P(saved.lse),
+                                      P(seg.buf), B, Hq, Hkv, L, S, D, sc, W, _lib.NB_BF16, P(dq2), P(ws), wsb, sp),
+                   "dq")
+        _lib.check(lib.nb_attn_bwd_dkdv(P(do), P(q), P(k), P(v), P(saved.lse), P(seg.buf), B, Hq, Hkv, L, S, D, sc,
+                                        W, _lib.NB_BF16, P(dk2), P(dv2), P(ws), wsb, sp), "dkdv")
+        torch.cuda.synchronize()
+        assert torch.equal(dq2, res.dq) and torch.equal(dk2, res.dk) and torch.equal(dv2, res.dv), f"dq+dkdv {rep}"
+
+
 def test_autograd_function_matches_direct_calls():
     w = SMALL["w2s"]
     inp = workload_inputs(w, "bf16")
