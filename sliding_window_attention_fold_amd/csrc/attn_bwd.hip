@@ -53,19 +53,22 @@ struct DkvCfg {
   // operand fragments read ahead of their MFMA; 0 = plain loop (D = 256 and the
   // float path have no registers to spare)
   static constexpr int AHEAD = (D <= 128 && sizeof(T) == 2) ? 4 : 0;
+  // Q/dO tile buffers: three (copies issued two steps ahead) when they fit
+  static constexpr int TILE_BYTES = BQ * D * (int)sizeof(T);
+  static constexpr int STAGES = (6 * TILE_BYTES + 24 * 1024 <= 160 * 1024) ? 3 : 2;
 };
 
-// LDS of one dK/dV item: two (Q, dO, row metadata) buffers -- one is filled by
-// DMA while the other is read -- and the P hand-over from role A to role B.
+// LDS of one dK/dV item: a ring of (Q, dO, row metadata) buffers -- filled by
+// DMA ahead of the step that reads them -- and the P hand-over from role A to
+// role B.
 template <typename T, int D>
 struct DkvSmem {
   typedef Tile<T, DkvCfg<T, D>::BQ, D> TL;
-  __attribute__((aligned(1024))) T Q0[TL::ELEMS];
-  __attribute__((aligned(1024))) T G0[TL::ELEMS];
-  __attribute__((aligned(1024))) T Q1[TL::ELEMS];
-  __attribute__((aligned(1024))) T G1[TL::ELEMS];
-  __attribute__((aligned(256))) float lse0[64], lse1[64], dl0[64], dl1[64];
-  __attribute__((aligned(256))) int klo0[64], klo1[64];
+  static constexpr int NS = DkvCfg<T, D>::STAGES;
+  __attribute__((aligned(1024))) T Q[NS][TL::ELEMS];
+  __attribute__((aligned(1024))) T G[NS][TL::ELEMS];
+  __attribute__((aligned(256))) float lse[NS][64], dl[NS][64];
+  __attribute__((aligned(256))) int klo[NS][64];
   __attribute__((aligned(256))) f32x4 pex[DkvCfg<T, D>::NKG][4][64];  // [key group][value quad][lane][4]
   int n_tiles_s;
 };
@@ -78,9 +81,6 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   typedef DkvCfg<T, D> C;
   typedef Tile<T, C::BQ, D> TL;
   typedef typename Frag<T>::type F;
-  T* const Q0 = sm.Q0; T* const G0 = sm.G0; T* const Q1 = sm.Q1; T* const G1 = sm.G1;
-  float* const lse0 = sm.lse0; float* const lse1 = sm.lse1; float* const dl0 = sm.dl0; float* const dl1 = sm.dl1;
-  int* const klo0 = sm.klo0; int* const klo1 = sm.klo1;
   auto& pex = sm.pex;
   int& n_tiles_s = sm.n_tiles_s;
   const int grp = p.Hq / p.Hkv;
@@ -153,7 +153,14 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
     if (w == 1) dma_words(ds, p.delta + rb, nr);
     if (w == 2) dma_words(ks, p.row_klo + (size_t)b * p.L + i0, nr);
   };
-  if (n_iter > 0) load(Q0, G0, lse0, dl0, klo0, 0);
+  constexpr int NS = C::STAGES;
+  auto load_slot = [&](int slot, int it) {
+    load(sm.Q[slot], sm.G[slot], sm.lse[slot], sm.dl[slot], sm.klo[slot], it);
+  };
+  // prologue: the first NS - 1 steps' tiles
+#pragma unroll
+  for (int x = 0; x < NS - 1; ++x)
+    if (x < n_iter) load_slot(x, x);
 
   // this lane's key row of K (role A) or V (role B): the B operand of S = Q K^T
   // or dP = dO V^T
@@ -250,18 +257,27 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
     }
   };
 
-  for (int it = 0; it < n_iter; it += 2) {
-    wait_global();
+  // copies per wave per step: the two tiles, plus one metadata row on waves 0-2
+  constexpr int LPT = 2 * TileDma<T, C::BQ, D, C::NW>::PER;
+  // Ring of NS buffers, unrolled NS times so every slot's LDS address is a
+  // constant: step it reads slot it % NS, whose copies were issued NS - 1
+  // steps earlier; copies of later steps may stay in flight.
+  auto stage = [&](int it, int slot) {
+    if (it + NS - 2 < n_iter && NS > 2) {
+      if (w < 3) __builtin_amdgcn_s_waitcnt(0x0F70 | ((NS - 2) * (LPT + 1) < 16 ? (NS - 2) * (LPT + 1) : 15));
+      else __builtin_amdgcn_s_waitcnt(0x0F70 | ((NS - 2) * LPT < 16 ? (NS - 2) * LPT : 15));
+    } else {
+      wait_global();
+    }
     __syncthreads();
-    if (it + 1 < n_iter) load(Q1, G1, lse1, dl1, klo1, it + 1);
+    if (it + NS - 1 < n_iter) load_slot((slot + NS - 1) % NS, it + NS - 1);
     __builtin_amdgcn_sched_barrier(0);
-    step(Q0, G0, lse0, dl0, klo0, it);
-    if (it + 1 >= n_iter) break;
-    wait_global();
-    __syncthreads();
-    if (it + 2 < n_iter) load(Q0, G0, lse0, dl0, klo0, it + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    step(Q1, G1, lse1, dl1, klo1, it + 1);
+    step(sm.Q[slot], sm.G[slot], sm.lse[slot], sm.dl[slot], sm.klo[slot], it);
+  };
+  for (int it = 0; it < n_iter; it += NS) {
+#pragma unroll
+    for (int x = 0; x < NS; ++x)
+      if (it + x < n_iter) stage(it + x, x);
   }
 
   if (j < p.S) {
