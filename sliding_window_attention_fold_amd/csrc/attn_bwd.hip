@@ -509,28 +509,37 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
 // Delta_i = dO_i . O_i for every row (b, h, i), with O the stored value plus
 // its saved rounding residual (fp32-accurate); 0 for padding rows.  Two rows
 // per wave, 32 lanes per row, D / 32 consecutive elements per lane.
+constexpr int kDeltaRowsPerWg = 32;   // 4 waves x 2 rows x kDeltaReps
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
+__device__ __forceinline__ void delta_rows(const BwdParams& p, int wg) {
   constexpr int E = D / 32;
+  constexpr int R = kDeltaRowsPerWg / 8;   // row pairs per wave, loaded together
+  typedef T VE __attribute__((ext_vector_type(E)));   // the lane's E elements, one vector load
   const int lane = threadIdx.x & 63, l32 = lane & 31;
   const long long n_rows = (long long)p.B * p.Hq * p.L;
-  const long long row = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + (lane >> 5);
-  const bool in = row < n_rows;
-  const long long rr = in ? row : n_rows - 1;
-  typedef T VE __attribute__((ext_vector_type(E)));   // the lane's E elements, one vector load
-  const VE dv = *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.dout) + rr * D + l32 * E);
-  const VE ov = *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.o) + rr * D + l32 * E);
-  VE lv = ov;
-  if (p.o_lo) lv = *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.o_lo) + rr * D + l32 * E);
-  float part = 0.f;
+  VE dv[R], ov[R], lv[R];
+  long long row[R];
 #pragma unroll
-  for (int e = 0; e < E; ++e) part += to_f32(dv[e]) * (to_f32(ov[e]) + (p.o_lo ? to_f32(lv[e]) : 0.f));
+  for (int r = 0; r < R; ++r) {
+    row[r] = (long long)wg * kDeltaRowsPerWg + ((threadIdx.x >> 6) * R + r) * 2 + (lane >> 5);
+    const long long rr = row[r] < n_rows ? row[r] : n_rows - 1;
+    dv[r] = *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.dout) + rr * D + l32 * E);
+    ov[r] = *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.o) + rr * D + l32 * E);
+    lv[r] = p.o_lo ? *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.o_lo) + rr * D + l32 * E) : ov[r];
+  }
 #pragma unroll
-  for (int o = 16; o > 0; o >>= 1) part += __shfl_xor(part, o);
-  if (in && l32 == 0) {
-    const int i = (int)(row % p.L), b = (int)(row / ((long long)p.Hq * p.L));
-    const bool real = p.row_klo[(size_t)b * p.L + i] <= p.S - p.L + i;
-    p.delta[row] = real ? part : 0.f;
+  for (int r = 0; r < R; ++r) {
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) part += to_f32(dv[r][e]) * (to_f32(ov[r][e]) + (p.o_lo ? to_f32(lv[r][e]) : 0.f));
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) part += __shfl_xor(part, o);
+    if (row[r] < n_rows && l32 == 0) {
+      const int i = (int)(row[r] % p.L), b = (int)(row[r] / ((long long)p.Hq * p.L));
+      const bool real = p.row_klo[(size_t)b * p.L + i] <= p.S - p.L + i;
+      p.delta[row[r]] = real ? part : 0.f;
+    }
   }
 }
 
@@ -546,8 +555,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 //          row's band start to the last row's position (an estimate when the
 //          first rows are padding -- the order only affects speed).
 // Also empties the work queues of the backward kernel.
-constexpr int kOrderNT = 1024;
-constexpr int kOrderMax = 8192;
+constexpr int kPrepNT = 256;          // threads of the prep kernel's workgroups
+constexpr int kOrderMax = 4096;       // items sorted in LDS
 constexpr int kOrderBandMax = 4096;   // query-tile band starts staged in LDS
 
 // Sort keys[0, N) ascending (N a power of two) and emit the item indices they
@@ -557,7 +566,7 @@ __device__ void order_by_work(unsigned long long* keys, int n, int N, int* out) 
   __syncthreads();
   for (int k = 2; k <= N; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < N; i += kOrderNT) {
+      for (int i = tid; i < N; i += kPrepNT) {
         const int l = i ^ j;
         if (l > i) {
           const unsigned long long a = keys[i], c = keys[l];
@@ -570,7 +579,7 @@ __device__ void order_by_work(unsigned long long* keys, int n, int N, int* out) 
       __syncthreads();
     }
   }
-  for (int i = tid; i < n; i += kOrderNT) out[i] = n - 1 - (int)(unsigned)(keys[i] & 0xFFFFFFFFu);
+  for (int i = tid; i < n; i += kPrepNT) out[i] = n - 1 - (int)(unsigned)(keys[i] & 0xFFFFFFFFu);
   __syncthreads();
 }
 
@@ -579,9 +588,7 @@ __device__ __forceinline__ unsigned long long work_key(unsigned work, int i, int
 }
 
 template <int BK, int BQ, int BM>
-__global__ __launch_bounds__(kOrderNT) void work_order_kernel(BwdParams p, int modes) {
-  __shared__ unsigned long long keys[kOrderMax];
-  __shared__ int bst[kOrderBandMax];
+__device__ void work_order(const BwdParams& p, int modes, unsigned long long* keys, int* bst) {
   const int tid = threadIdx.x;
   const int off = p.S - p.L;
   if (tid < kNumQueues) p.counters[tid] = 0;  // the backward kernel's work queues start empty
@@ -589,7 +596,7 @@ __global__ __launch_bounds__(kOrderNT) void work_order_kernel(BwdParams p, int m
     const int n_kt = (p.S + BK - 1) / BK;
     const int n = p.B * n_kt;
     if (n > kOrderMax) {
-      for (int i = tid; i < n; i += kOrderNT) p.order[i] = i;
+      for (int i = tid; i < n; i += kPrepNT) p.order[i] = i;
     } else {
       const int n_q_tiles = (p.L + BQ - 1) / BQ;
       // band start of each query tile's first row (nondecreasing along a row)
@@ -600,11 +607,11 @@ __global__ __launch_bounds__(kOrderNT) void work_order_kernel(BwdParams p, int m
       };
       const bool staged = p.B * n_q_tiles <= kOrderBandMax;
       if (staged)
-        for (int x = tid; x < p.B * n_q_tiles; x += kOrderNT) bst[x] = band_start_g(x / n_q_tiles, x % n_q_tiles);
+        for (int x = tid; x < p.B * n_q_tiles; x += kPrepNT) bst[x] = band_start_g(x / n_q_tiles, x % n_q_tiles);
       __syncthreads();
       int N = 1;
       while (N < n) N <<= 1;
-      for (int i = tid; i < N; i += kOrderNT) {
+      for (int i = tid; i < N; i += kPrepNT) {
         unsigned long long key = ~0ull;  // padding sorts last
         if (i < n) {
           const int b = i / n_kt, kt = i % n_kt;
@@ -628,11 +635,11 @@ __global__ __launch_bounds__(kOrderNT) void work_order_kernel(BwdParams p, int m
     const int n_qt = (p.L + BM - 1) / BM;
     const int n = p.B * n_qt;
     if (n > kOrderMax) {
-      for (int i = tid; i < n; i += kOrderNT) p.qorder[i] = i;
+      for (int i = tid; i < n; i += kPrepNT) p.qorder[i] = i;
     } else {
       int N = 1;
       while (N < n) N <<= 1;
-      for (int i = tid; i < N; i += kOrderNT) {
+      for (int i = tid; i < N; i += kPrepNT) {
         unsigned long long key = ~0ull;
         if (i < n) {
           const int b = i / n_qt, qt = i % n_qt;
@@ -646,6 +653,16 @@ __global__ __launch_bounds__(kOrderNT) void work_order_kernel(BwdParams p, int m
       order_by_work(keys, n, N, p.qorder);
     }
   }
+}
+
+// The prep launch: workgroups 0 .. gridDim.x - 2 form Delta (32 rows each), the
+// last one computes the work orders (a grid of one workgroup: orders only).
+template <typename T, int D, int BK, int BQ, int BM>
+__global__ __launch_bounds__(kPrepNT) void bwd_prep_kernel(BwdParams p, int modes) {
+  __shared__ unsigned long long keys[kOrderMax];
+  __shared__ int bst[kOrderBandMax];
+  if (blockIdx.x + 1 == gridDim.x) work_order<BK, BQ, BM>(p, modes, keys, bst);
+  else delta_rows<T, D>(p, blockIdx.x);
 }
 
 size_t dkdv_order_elems(int B, int S) { return (size_t)B * ((S + 31) / 32); }
@@ -702,19 +719,16 @@ static int device_cu_count() {
   return n_cu;
 }
 
+// Delta (when with_delta) and the work orders of the passes in `modes`.
 template <typename T, int D>
-static hipError_t launch_delta_t(const BwdParams& p, hipStream_t s) {
-  const long long rows = (long long)p.B * p.Hq * p.L;
-  hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
-template <typename T, int D>
-static hipError_t launch_order_t(const BwdParams& p, int modes, hipStream_t s) {
+static hipError_t launch_prep_t(const BwdParams& p, bool with_delta, int modes, hipStream_t s) {
   typedef DkvCfg<T, D> CK;
   typedef DqCfg<T, D> CQ;
   static_assert(CK::BK >= 32 && CQ::BM >= 32, "the work-order arrays are sized for tiles of >= 32");
-  hipLaunchKernelGGL((work_order_kernel<CK::BK, CK::BQ, CQ::BM>), dim3(1), dim3(kOrderNT), 0, s, p, modes);
+  const long long rows = (long long)p.B * p.Hq * p.L;
+  const unsigned n_delta = with_delta ? (unsigned)((rows + kDeltaRowsPerWg - 1) / kDeltaRowsPerWg) : 0u;
+  hipLaunchKernelGGL((bwd_prep_kernel<T, D, CK::BK, CK::BQ, CQ::BM>), dim3(n_delta + 1), dim3(kPrepNT), 0, s, p,
+                     modes);
   return hipGetLastError();
 }
 
@@ -732,16 +746,14 @@ static hipError_t launch_t(const BwdParams& p, int what, hipStream_t s) {
   hipError_t e = hipSuccess;
   switch (what) {
     case kBwdPrep:   // Delta + work orders of both passes
-      e = launch_delta_t<T, D>(p, s);
-      return e != hipSuccess ? e : launch_order_t<T, D>(p, 3, s);
+      return launch_prep_t<T, D>(p, true, 3, s);
     case kBwdMain:
       return launch_main_t<T, D, 3>(p, s);
-    case kBwdDq:     // Delta, then the dQ pass alone
-      e = launch_delta_t<T, D>(p, s);
-      if (e == hipSuccess) e = launch_order_t<T, D>(p, 2, s);
+    case kBwdDq:     // Delta + the dQ order, then the dQ pass alone
+      e = launch_prep_t<T, D>(p, true, 2, s);
       return e != hipSuccess ? e : launch_main_t<T, D, 2>(p, s);
     case kBwdDkdv:   // the dK/dV pass alone (Delta from an earlier dQ / prep call)
-      e = launch_order_t<T, D>(p, 1, s);
+      e = launch_prep_t<T, D>(p, false, 1, s);
       return e != hipSuccess ? e : launch_main_t<T, D, 1>(p, s);
   }
   return hipErrorInvalidValue;
