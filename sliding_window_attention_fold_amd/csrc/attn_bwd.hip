@@ -69,7 +69,10 @@ struct DkvSmem {
   __attribute__((aligned(1024))) T G[NS][TL::ELEMS];
   __attribute__((aligned(256))) float lse[NS][64], dl[NS][64];
   __attribute__((aligned(256))) int klo[NS][64];
-  __attribute__((aligned(256))) f32x4 pex[DkvCfg<T, D>::NKG][4][64];  // [key group][value quad][lane][4]
+  // P hand-over, double-buffered when the ring has three slots (no barrier at
+  // the top of a step then separates one step's read from the next step's write)
+  static constexpr int NPEX = (NS >= 3) ? 2 : 1;
+  __attribute__((aligned(256))) f32x4 pex[NPEX][DkvCfg<T, D>::NKG][4][64];  // [buf][key group][value quad][lane][4]
   int n_tiles_s;
 };
 
@@ -175,7 +178,8 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
 #pragma unroll
   for (int d = 0; d < D / 32; ++d) gacc[d] = f32x16{};
 
-  auto step = [&](const T* Qs, const T* Gs, const float* ls, const float* ds, const int* ks, int it) {
+  auto step = [&](const T* Qs, const T* Gs, const float* ls, const float* ds, const int* ks, int it, auto&& mid) {
+    auto& px = pex[DkvSmem<T, D>::NPEX > 1 ? (it & 1) : 0];
     const int t = t_first + it % n_t;
     const int i0 = t * C::BQ;
     const int nrows = min(C::BQ, p.L - i0);
@@ -225,16 +229,16 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
         }
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd)
-          pex[kg][qd][lane] = f32x4{sacc[4 * qd], sacc[4 * qd + 1], sacc[4 * qd + 2], sacc[4 * qd + 3]};
+          px[kg][qd][lane] = f32x4{sacc[4 * qd], sacc[4 * qd + 1], sacc[4 * qd + 2], sacc[4 * qd + 3]};
       }
     }
-    __syncthreads();
+    mid();   // the hand-over barrier (and ring maintenance)
     if (!active) return;
     // second half: role A accumulates dV^T = dO^T P, role B dK^T = Q^T dS
     if (!role_a) {
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
-        const f32x4 pq = pex[kg][qd][lane];
+        const f32x4 pq = px[kg][qd][lane];
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds + 8 * qd + 4 * g);  // rows acc_row(4*qd + e, g)
 #pragma unroll
         for (int e = 0; e < 4; ++e) sacc[4 * qd + e] = pq[e] * (sacc[4 * qd + e] - d4[e]);
@@ -257,27 +261,41 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
     }
   };
 
-  // copies per wave per step: the two tiles, plus one metadata row on waves 0-2
-  constexpr int LPT = 2 * TileDma<T, C::BQ, D, C::NW>::PER;
-  // Ring of NS buffers, unrolled NS times so every slot's LDS address is a
-  // constant: step it reads slot it % NS, whose copies were issued NS - 1
-  // steps earlier; copies of later steps may stay in flight.
-  auto stage = [&](int it, int slot) {
-    if (it + NS - 2 < n_iter && NS > 2) {
-      if (w < 3) __builtin_amdgcn_s_waitcnt(0x0F70 | ((NS - 2) * (LPT + 1) < 16 ? (NS - 2) * (LPT + 1) : 15));
-      else __builtin_amdgcn_s_waitcnt(0x0F70 | ((NS - 2) * LPT < 16 ? (NS - 2) * LPT : 15));
-    } else {
-      wait_global();
-    }
+  if constexpr (NS >= 3) {
+    // One barrier per step, at the hand-over: by then every wave has finished
+    // the previous step, so the copies of step it + 2 go into its slot right
+    // after the barrier, and the copies of step it + 1 (issued two steps
+    // earlier) are complete and visible for its first half.  The ring is
+    // unrolled NS times so every slot's LDS address is a constant.
+    auto stage = [&](int it, int slot) {
+      step(sm.Q[slot], sm.G[slot], sm.lse[slot], sm.dl[slot], sm.klo[slot], it, [&]() {
+        if (it + 1 < n_iter) wait_global();
+        __syncthreads();
+        if (it + 2 < n_iter) load_slot((slot + 2) % NS, it + 2);
+      });
+    };
+    wait_global();   // the prologue's copies
     __syncthreads();
-    if (it + NS - 1 < n_iter) load_slot((slot + NS - 1) % NS, it + NS - 1);
-    __builtin_amdgcn_sched_barrier(0);
-    step(sm.Q[slot], sm.G[slot], sm.lse[slot], sm.dl[slot], sm.klo[slot], it);
-  };
-  for (int it = 0; it < n_iter; it += NS) {
+    for (int it = 0; it < n_iter; it += NS) {
 #pragma unroll
-    for (int x = 0; x < NS; ++x)
-      if (it + x < n_iter) stage(it + x, x);
+      for (int x = 0; x < NS; ++x)
+        if (it + x < n_iter) stage(it + x, x);
+    }
+  } else {
+    // two slots: copies for step it + 1 go out after the barrier at the top of
+    // step it, which also makes step it's copies visible
+    auto stage = [&](int it, int slot) {
+      wait_global();
+      __syncthreads();
+      if (it + 1 < n_iter) load_slot((slot + 1) % NS, it + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      step(sm.Q[slot], sm.G[slot], sm.lse[slot], sm.dl[slot], sm.klo[slot], it, [&]() { __syncthreads(); });
+    };
+    for (int it = 0; it < n_iter; it += NS) {
+#pragma unroll
+      for (int x = 0; x < NS; ++x)
+        if (it + x < n_iter) stage(it + x, x);
+    }
   }
 
   if (j < p.S) {
