@@ -337,11 +337,16 @@ template <typename T, int D>
 struct DqSmem {
   typedef Tile<T, DqCfg<T, D>::BN, D> TL;
   static constexpr int NSB = DqCfg<T, D>::BN / 32;
-  __attribute__((aligned(1024))) T K0[TL::ELEMS];
-  __attribute__((aligned(1024))) T V0[TL::ELEMS];
-  __attribute__((aligned(1024))) T K1[TL::ELEMS];
-  __attribute__((aligned(1024))) T V1[TL::ELEMS];
-  __attribute__((aligned(256))) f32x4 xch[2][4][NSB][4][64];  // [P | dP][group][block][value quad][lane][4]
+  static constexpr int TILE_BYTES = TL::ELEMS * (int)sizeof(T);
+  static constexpr int XCH_BYTES = 2 * 4 * NSB * 4 * 64 * 16;
+  // three K/V slots and a double-buffered exchange (one barrier per step) when
+  // they fit, else two slots and one exchange buffer (two barriers per step)
+  static constexpr bool RING3 = 6 * TILE_BYTES + 2 * XCH_BYTES <= 160 * 1024;
+  static constexpr int NS = RING3 ? 3 : 2;
+  static constexpr int NX = RING3 ? 2 : 1;
+  __attribute__((aligned(1024))) T K[NS][TL::ELEMS];
+  __attribute__((aligned(1024))) T V[NS][TL::ELEMS];
+  __attribute__((aligned(256))) f32x4 xch[NX][2][4][NSB][4][64];  // [buf][P | dP][group][block][value quad][lane][4]
 };
 
 // One dQ item f: (kv head, q head of its group, batch row, query tile) with
@@ -354,12 +359,10 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
   constexpr int NSB = C::BN / 32;
   constexpr int NM = C::BN / 16;
   constexpr int DH = D / 64;   // 32-wide d blocks of dQ per role
-  T* const K0 = sm.K0; T* const V0 = sm.V0; T* const K1 = sm.K1; T* const V1 = sm.V1;
-  f32x4 (*xp)[NSB][4][64] = sm.xch[0];
-  f32x4 (*xdp)[NSB][4][64] = sm.xch[1];
-  // wave bounds: scratch at the start of xp, dead before the first exchange
-  // (barriers separate them)
-  int (*red)[2] = reinterpret_cast<int (*)[2]>(&sm.xch[0][0][0][0][0]);
+  constexpr int NS = DqSmem<T, D>::NS;
+  // wave bounds: scratch at the start of the exchange, dead before the first
+  // exchange write (barriers separate them)
+  int (*red)[2] = reinterpret_cast<int (*)[2]>(&sm.xch[0][0][0][0][0][0]);
   const int grp = p.Hq / p.Hkv;
   const int n_qt = (p.L + C::BM - 1) / C::BM;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
@@ -411,19 +414,27 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
 
   const T* __restrict__ kbase = reinterpret_cast<const T*>(p.k) + ((size_t)b * p.Hkv + kvh) * p.S * D;
   const T* __restrict__ vbase = reinterpret_cast<const T*>(p.v) + ((size_t)b * p.Hkv + kvh) * p.S * D;
-  auto load = [&](T* Ks, T* Vs, int j0) {
+  const int nt = kstart < kend ? (kend - kstart + C::BN - 1) / C::BN : 0;   // key tiles of the item
+  auto load = [&](int slot, int n) {
+    const int j0 = kstart + n * C::BN;
     const int nv = min(C::BN, p.S - j0);
-    dma.issue(Ks, kbase + (size_t)j0 * D, nv);
-    dma.issue(Vs, vbase + (size_t)j0 * D, nv);
+    dma.issue(sm.K[slot], kbase + (size_t)j0 * D, nv);
+    dma.issue(sm.V[slot], vbase + (size_t)j0 * D, nv);
   };
-  if (kstart < kend) load(K0, V0, kstart);
+#pragma unroll
+  for (int x = 0; x < NS - 1; ++x)
+    if (x < nt) load(x, x);
 
   const int dh0 = role_a ? 0 : DH;      // first 32-wide d block of this wave's dQ half
   f32x16 dqacc[DH];
 #pragma unroll
   for (int d = 0; d < DH; ++d) dqacc[d] = f32x16{};
 
-  auto step = [&](const T* Ks, const T* Vs, int j0) {
+  auto step = [&](const T* Ks, const T* Vs, int n, auto&& mid) {
+    const int j0 = kstart + n * C::BN;
+    auto& xb = sm.xch[DqSmem<T, D>::NX > 1 ? (n & 1) : 0];
+    f32x4 (*xp)[NSB][4][64] = xb[0];
+    f32x4 (*xdp)[NSB][4][64] = xb[1];
     const bool active = !(j0 >= w_hi || j0 + C::BN <= w_lo);   // same for both roles of the group
     const bool full = w_all_real && j0 >= w_bs_max && j0 + C::BN - 1 <= w_p_min;
     f32x16 sacc[NSB];
@@ -462,7 +473,7 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
         for (int qd = 0; qd < 4; ++qd)
           mine[sb][qd][lane] = f32x4{sacc[sb][4 * qd], sacc[sb][4 * qd + 1], sacc[sb][4 * qd + 2], sacc[sb][4 * qd + 3]};
     }
-    __syncthreads();
+    mid();   // the exchange barrier (and ring maintenance)
     if (!active) return;
     // dS = P (dP - Delta), with the partner's half taken from LDS
     f32x4 (*theirs)[4][64] = role_a ? xdp[qg] : xp[qg];
@@ -493,18 +504,37 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
     }
   };
 
-  for (int j0 = kstart; j0 < kend; j0 += 2 * C::BN) {
+  if constexpr (DqSmem<T, D>::RING3) {
+    // one barrier per step, at the exchange: copies of tile n + 2 go into the
+    // slot tile n - 1 used, and tile n + 1's copies (issued two steps earlier)
+    // are complete and visible before its first half
+    auto stage = [&](int n, int slot) {
+      step(sm.K[slot], sm.V[slot], n, [&]() {
+        if (n + 1 < nt) wait_global();
+        __syncthreads();
+        if (n + 2 < nt) load((slot + 2) % NS, n + 2);
+      });
+    };
     wait_global();
     __syncthreads();
-    if (j0 + C::BN < kend) load(K1, V1, j0 + C::BN);
-    __builtin_amdgcn_sched_barrier(0);
-    step(K0, V0, j0);
-    if (j0 + C::BN >= kend) break;
-    wait_global();
-    __syncthreads();
-    if (j0 + 2 * C::BN < kend) load(K0, V0, j0 + 2 * C::BN);
-    __builtin_amdgcn_sched_barrier(0);
-    step(K1, V1, j0 + C::BN);
+    for (int n = 0; n < nt; n += NS) {
+#pragma unroll
+      for (int x = 0; x < NS; ++x)
+        if (n + x < nt) stage(n + x, x);
+    }
+  } else {
+    auto stage = [&](int n, int slot) {
+      wait_global();
+      __syncthreads();
+      if (n + 1 < nt) load((slot + 1) % NS, n + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      step(sm.K[slot], sm.V[slot], n, [&]() { __syncthreads(); });
+    };
+    for (int n = 0; n < nt; n += NS) {
+#pragma unroll
+      for (int x = 0; x < NS; ++x)
+        if (n + x < nt) stage(n + x, x);
+    }
   }
 
   if (in_range) {
