@@ -76,7 +76,9 @@ def test_mask_equals_interval_form(seed):
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_mask_invariants_on_workloads(cfg):
-    """The benchmark spec invariants on each workload's real doc map, checked per row block."""
+    """The benchmark spec invariants on each workload's real doc map, checked per row block
+    (every row block, except config 4 -- one 65536-key document -- where the first,
+    middle and last blocks are checked)."""
     w = wl.get(cfg)
     dm = wl.make_doc_map(w)
     f = orc.fold_pad(dm.doc_ids, dm.pad_mask)
@@ -84,24 +86,26 @@ def test_mask_invariants_on_workloads(cfg):
     L = w.L
     j = np.arange(S)
     step = 512
+    starts = list(range(0, L, step))
+    if L * S > (1 << 26):
+        starts = sorted({starts[0], starts[len(starts) // 2], starts[-1]})
     for b in range(B):
-        for s0 in range(0, L, step):
+        for s0 in starts:
             rows = np.arange(s0, min(L, s0 + step))
             M = orc.allow_mask(f[b:b + 1], L, w.window, rows=rows)[0, 0]
             p = S - L + rows
+            r = np.arange(len(rows))
             # diagonal always allowed
-            assert M[np.arange(len(rows)), p].all()
+            assert M[r, p].all()
             off = M.copy()
-            off[np.arange(len(rows)), p] = False
-            rr, cc = np.nonzero(off)
-            pp = p[rr]
-            assert (cc <= pp).all()                                      # key not after query
-            assert (f[b, cc] == f[b, pp]).all() and (f[b, pp] > 0).all()  # same doc, not padding
+            off[r, p] = False
+            fp = f[b, p][:, None]
+            ok = (j[None, :] <= p[:, None]) & (f[b][None, :] == fp) & (fp > 0)   # causal, same doc, not padding
             if w.window >= 0:
-                assert (pp - cc <= w.window).all()                      # inside the window
+                ok &= (p[:, None] - j[None, :]) <= w.window                      # inside the window
+            assert not (off & ~ok).any()
             # pad rows: only the (harmless) diagonal
-            pad_rows = f[b, p] <= 0
-            assert (off[pad_rows].sum() == 0)
+            assert not off[f[b, p] <= 0].any()
 
 
 def test_mask_is_full_sequence_slice():
