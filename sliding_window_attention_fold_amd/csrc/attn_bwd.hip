@@ -42,20 +42,31 @@ namespace nb {
 // the roles keeps each wave under 256 registers at D = 256 (K or V rows plus
 // one accumulator), so two waves share each SIMD and hide each other's
 // latency; the matrix-core work is the same as one wave doing both.
+// Shape of the backward kernel's workgroups: groups of 32 keys (dK/dV items)
+// and of 32 query rows (dQ items) per workgroup, two waves per group, and
+// workgroups per CU (the LDS of one workgroup is then 160 KB / OCC at most).
+template <typename T, int D>
+struct BwdShape {
+  static constexpr int GROUPS = 4;
+  static constexpr int OCC = 1;
+  static constexpr int NT = 128 * GROUPS;
+  static constexpr int LDS_BUDGET = 160 * 1024 / OCC;
+};
+
 template <typename T, int D>
 struct DkvCfg {
-  static constexpr int NKG = 4;        // key groups of 32 keys
+  static constexpr int NKG = BwdShape<T, D>::GROUPS;   // key groups of 32 keys
   static constexpr int NW = 2 * NKG;
   static constexpr int NT = 64 * NW;
   static constexpr int BK = 32 * NKG;  // keys per workgroup
   static constexpr int BQ = 32;        // query rows per step
-  static constexpr int OCC = 1;        // workgroups per CU
   // operand fragments read ahead of their MFMA; 0 = plain loop (D = 256 and the
   // float path have no registers to spare)
   static constexpr int AHEAD = (D <= 128 && sizeof(T) == 2) ? 4 : 0;
   // Q/dO tile buffers: three (copies issued two steps ahead) when they fit
   static constexpr int TILE_BYTES = BQ * D * (int)sizeof(T);
-  static constexpr int STAGES = (6 * TILE_BYTES + 24 * 1024 <= 160 * 1024) ? 3 : 2;
+  static constexpr int STAGES =
+      (6 * TILE_BYTES + 2 * NKG * 4 * 64 * 16 + 2048 <= BwdShape<T, D>::LDS_BUDGET) ? 3 : 2;
 };
 
 // LDS of one dK/dV item: a ring of (Q, dO, row metadata) buffers -- filled by
@@ -323,9 +334,10 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
 // each SIMD at D = 256; the matrix-core work is the same as one wave doing all.
 template <typename T, int D>
 struct DqCfg {
-  static constexpr int NW = 8;
+  static constexpr int NQG = BwdShape<T, D>::GROUPS;   // query groups of 32 rows
+  static constexpr int NW = 2 * NQG;
   static constexpr int NT = 64 * NW;
-  static constexpr int BM = 128;                    // query rows per workgroup
+  static constexpr int BM = 32 * NQG;               // query rows per workgroup
   static constexpr int BN = (D * sizeof(T) <= 256) ? 64 : 32;   // keys per tile
   // operand fragments read ahead of their MFMA; 0 = plain loop (float path)
   static constexpr int AHEAD = (sizeof(T) != 2) ? 0 : (D <= 128) ? 4 : 2;
@@ -338,15 +350,16 @@ struct DqSmem {
   typedef Tile<T, DqCfg<T, D>::BN, D> TL;
   static constexpr int NSB = DqCfg<T, D>::BN / 32;
   static constexpr int TILE_BYTES = TL::ELEMS * (int)sizeof(T);
-  static constexpr int XCH_BYTES = 2 * 4 * NSB * 4 * 64 * 16;
+  static constexpr int NQG = DqCfg<T, D>::NQG;
+  static constexpr int XCH_BYTES = 2 * NQG * NSB * 4 * 64 * 16;
   // three K/V slots and a double-buffered exchange (one barrier per step) when
   // they fit, else two slots and one exchange buffer (two barriers per step)
-  static constexpr bool RING3 = 6 * TILE_BYTES + 2 * XCH_BYTES <= 160 * 1024;
+  static constexpr bool RING3 = 6 * TILE_BYTES + 2 * XCH_BYTES <= BwdShape<T, D>::LDS_BUDGET;
   static constexpr int NS = RING3 ? 3 : 2;
   static constexpr int NX = RING3 ? 2 : 1;
   __attribute__((aligned(1024))) T K[NS][TL::ELEMS];
   __attribute__((aligned(1024))) T V[NS][TL::ELEMS];
-  __attribute__((aligned(256))) f32x4 xch[NX][2][4][NSB][4][64];  // [buf][P | dP][group][block][value quad][lane][4]
+  __attribute__((aligned(256))) f32x4 xch[NX][2][NQG][NSB][4][64];  // [buf][P | dP][group][block][value quad][lane][4]
 };
 
 // One dQ item f: (kv head, q head of its group, batch row, query tile) with
@@ -366,8 +379,8 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
   const int grp = p.Hq / p.Hkv;
   const int n_qt = (p.L + C::BM - 1) / C::BM;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
-  const int qg = w & 3;                 // query group
-  const bool role_a = w < 4;            // A: Q, S, P   B: dO, dP
+  const int qg = w % C::NQG;            // query group
+  const bool role_a = w < C::NQG;       // A: Q, S, P   B: dO, dP
   const int off = p.S - p.L;
   const TileAccess<T, TL> acc(ln, lane);
   const TileDma<T, C::BN, D, C::NW> dma;   // K and V tiles share one layout
@@ -557,7 +570,7 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
 // Delta_i = dO_i . O_i for every row (b, h, i), with O the stored value plus
 // its saved rounding residual (fp32-accurate); 0 for padding rows.  Two rows
 // per wave, 32 lanes per row, D / 32 consecutive elements per lane.
-constexpr int kDeltaRowsPerWg = 32;   // 4 waves x 2 rows x kDeltaReps
+constexpr int kDeltaRowsPerWg = 8;   // 4 waves x 2 rows (half a wave per row); small workgroups stream best
 
 template <typename T, int D>
 __device__ __forceinline__ void delta_rows(const BwdParams& p, int wg) {
@@ -604,8 +617,8 @@ __device__ __forceinline__ void delta_rows(const BwdParams& p, int wg) {
 //          first rows are padding -- the order only affects speed).
 // Also empties the work queues of the backward kernel.
 constexpr int kPrepNT = 256;          // threads of the prep kernel's workgroups
-constexpr int kOrderMax = 4096;       // items sorted in LDS
-constexpr int kOrderBandMax = 4096;   // query-tile band starts staged in LDS
+constexpr int kOrderMax = 2048;       // items sorted in LDS
+constexpr int kOrderBandMax = 2048;   // query-tile band starts staged in LDS
 
 // Sort keys[0, N) ascending (N a power of two) and emit the item indices they
 // carry (key = (2^32 - 1 - work) << 32 | (n - 1 - item)).
@@ -703,14 +716,16 @@ __device__ void work_order(const BwdParams& p, int modes, unsigned long long* ke
   }
 }
 
-// The prep launch: workgroups 0 .. gridDim.x - 2 form Delta (32 rows each), the
-// last one computes the work orders (a grid of one workgroup: orders only).
+// The prep launch: workgroup 0 computes the work orders (dispatched first, so
+// the serial sort overlaps the streaming), workgroups 1 .. gridDim.x - 1 form
+// Delta (kDeltaRowsPerWg rows each); a grid of one workgroup computes the
+// orders only.
 template <typename T, int D, int BK, int BQ, int BM>
 __global__ __launch_bounds__(kPrepNT) void bwd_prep_kernel(BwdParams p, int modes) {
   __shared__ unsigned long long keys[kOrderMax];
   __shared__ int bst[kOrderBandMax];
-  if (blockIdx.x + 1 == gridDim.x) work_order<BK, BQ, BM>(p, modes, keys, bst);
-  else delta_rows<T, D>(p, blockIdx.x);
+  if (blockIdx.x == 0) work_order<BK, BQ, BM>(p, modes, keys, bst);
+  else delta_rows<T, D>(p, blockIdx.x - 1);
 }
 
 size_t dkdv_order_elems(int B, int S) { return (size_t)B * ((S + 31) / 32); }
@@ -728,8 +743,9 @@ size_t dq_order_elems(int B, int L) { return (size_t)B * ((L + 31) / 32); }
 // both passes in one grid lets the shorter dQ items fill the tail of the dK/dV
 // items.  Which workgroup computes an item never changes the result.
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(512, 1) void bwd_kernel(BwdParams p) {
-  static_assert(DkvCfg<T, D>::NT == 512 && DqCfg<T, D>::NT == 512, "one block shape for both passes");
+__global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void bwd_kernel(BwdParams p) {
+  static_assert(DkvCfg<T, D>::NT == BwdShape<T, D>::NT && DqCfg<T, D>::NT == BwdShape<T, D>::NT,
+                "one block shape for both passes");
   __shared__ union BwdSmem {
     DkvSmem<T, D> kv;
     DqSmem<T, D> q;
@@ -784,8 +800,8 @@ template <typename T, int D, int MODE>
 static hipError_t launch_main_t(const BwdParams& p, hipStream_t s) {
   const long long n_kv = (MODE & 1) ? (long long)p.B * ((p.S + DkvCfg<T, D>::BK - 1) / DkvCfg<T, D>::BK) * p.Hkv : 0;
   const long long n_q = (MODE & 2) ? (long long)p.B * ((p.L + DqCfg<T, D>::BM - 1) / DqCfg<T, D>::BM) * p.Hq : 0;
-  dim3 grid((unsigned)std::min<long long>(n_kv + n_q, (long long)device_cu_count()));
-  hipLaunchKernelGGL((bwd_kernel<T, D, MODE>), grid, dim3(512), 0, s, p);
+  dim3 grid((unsigned)std::min<long long>(n_kv + n_q, (long long)device_cu_count() * BwdShape<T, D>::OCC));
+  hipLaunchKernelGGL((bwd_kernel<T, D, MODE>), grid, dim3(BwdShape<T, D>::NT), 0, s, p);
   return hipGetLastError();
 }
 
