@@ -27,6 +27,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "nb_device.h"
 #include "nb_kernels.h"
@@ -35,57 +36,81 @@ namespace nb {
 
 // ---------------------------------------------------------------- dK / dV
 
-// NKG key groups of 32 keys, two waves (roles) per group.  Role A holds
-// the group's K rows, forms S = Q K^T and P, hands P to its partner through LDS
-// and accumulates dV^T = dO^T P; role B holds the V rows, forms dP = dO V^T,
-// takes P, forms dS = P (dP - Delta) and accumulates dK^T = Q^T dS.  Splitting
-// the roles keeps each wave under 256 registers at D = 256 (K or V rows plus
-// one accumulator), so two waves share each SIMD and hide each other's
-// latency; the matrix-core work is the same as one wave doing both.
-// Shape of the backward kernel's workgroups: groups of 32 keys (dK/dV items)
-// and of 32 query rows (dQ items) per workgroup, two waves per group, and
-// workgroups per CU (the LDS of one workgroup is then 160 KB / OCC at most).
+// NKG key groups of 32 keys, two waves (roles) per group.  Role A holds the
+// group's K rows, forms S = Q K^T and P, hands P to its partner through LDS and
+// accumulates dV^T = dO^T P; role B holds the V rows, forms dP = dO V^T, takes
+// P, forms dS = P (dP - Delta) and accumulates dK^T = Q^T dS.  Splitting the
+// roles keeps each wave under 256 registers at D = 256 (K or V rows plus one
+// accumulator), so two waves share each SIMD and hide each other's latency
+// (measured: one wave per SIMD with 512 registers and deep operand read-ahead,
+// four waves per workgroup, ran the backward 1.5x slower).
+// Workgroup shape: eight waves (four groups of 32 keys or 32 query rows, two
+// roles each); the LDS of one workgroup is 160 KB / OCC at most.
 template <typename T, int D>
 struct BwdShape {
-  static constexpr int GROUPS = 4;
   static constexpr int OCC = 1;
-  static constexpr int NT = 128 * GROUPS;
+  static constexpr int NT = 512;
   static constexpr int LDS_BUDGET = 160 * 1024 / OCC;
 };
 
 template <typename T, int D>
 struct DkvCfg {
-  static constexpr int NKG = BwdShape<T, D>::GROUPS;   // key groups of 32 keys
-  static constexpr int NW = 2 * NKG;
-  static constexpr int NT = 64 * NW;
+  static constexpr int NT = BwdShape<T, D>::NT;
+  static constexpr int NW = NT / 64;
+  static constexpr int NKG = NW / 2;   // key groups of 32 keys
   static constexpr int BK = 32 * NKG;  // keys per workgroup
   static constexpr int BQ = 32;        // query rows per step
   // operand fragments read ahead of their MFMA; 0 = plain loop (D = 256 and the
   // float path have no registers to spare)
   static constexpr int AHEAD = (D <= 128 && sizeof(T) == 2) ? 4 : 0;
-  // Q/dO tile buffers: three (copies issued two steps ahead) when they fit
   static constexpr int TILE_BYTES = BQ * D * (int)sizeof(T);
-  static constexpr int STAGES =
-      (6 * TILE_BYTES + 2 * NKG * 4 * 64 * 16 + 2048 <= BwdShape<T, D>::LDS_BUDGET) ? 3 : 2;
+  static constexpr int PEX_BYTES = NKG * 4 * 64 * 16;   // one P hand-over buffer
+  static constexpr int META_BYTES = 3 * 64 * 4;         // LSE, Delta, band starts of one step
+  static constexpr bool fits(int ns, int npex) {
+    return ns * (2 * TILE_BYTES + META_BYTES) + npex * PEX_BYTES + 1024 <= BwdShape<T, D>::LDS_BUDGET;
+  }
+  // Schedules (measured per head size):
+  //  - skewed (D > 128): role B one step behind role A; ring slots for the
+  //    previous step, the current one and one step of copies in flight, two
+  //    hand-over buffers;
+  //  - in step, three slots (copies two steps ahead), two hand-over buffers,
+  //    one barrier per step;
+  //  - in step, two slots, one hand-over buffer, two barriers per step.
+  static constexpr bool SKEW = D > 128 && fits(3, 2);
+  static constexpr int STAGES = SKEW ? (fits(4, 2) ? 4 : 3) : fits(3, 2) ? 3 : 2;
+  static constexpr int NPEX = STAGES >= 3 ? 2 : 1;
 };
 
 // LDS of one dK/dV item: a ring of (Q, dO, row metadata) buffers -- filled by
 // DMA ahead of the step that reads them -- and the P hand-over from role A to
 // role B.
 template <typename T, int D>
-struct DkvSmem {
+struct DkvTiles {
   typedef Tile<T, DkvCfg<T, D>::BQ, D> TL;
   static constexpr int NS = DkvCfg<T, D>::STAGES;
   __attribute__((aligned(1024))) T Q[NS][TL::ELEMS];
   __attribute__((aligned(1024))) T G[NS][TL::ELEMS];
+};
+template <typename T, int D>
+struct DkvMeta {
+  static constexpr int NS = DkvCfg<T, D>::STAGES;
   __attribute__((aligned(256))) float lse[NS][64], dl[NS][64];
   __attribute__((aligned(256))) int klo[NS][64];
-  // P hand-over, double-buffered when the ring has three slots (no barrier at
-  // the top of a step then separates one step's read from the next step's write)
-  static constexpr int NPEX = (NS >= 3) ? 2 : 1;
-  __attribute__((aligned(256))) f32x4 pex[NPEX][DkvCfg<T, D>::NKG][4][64];  // [buf][key group][value quad][lane][4]
+  // P hand-over, double-buffered with three slots (no barrier separates one
+  // step's read from the next step's write)
+  __attribute__((aligned(256))) f32x4 pex[DkvCfg<T, D>::NPEX][DkvCfg<T, D>::NKG][4][64];  // [buf][key group][value quad][lane][4]
   int n_tiles_s;
 };
+// Where the row metadata goes decides the register cost of its addresses (an
+// LDS read reaches 64 KB past its address register): the skewed schedule reads
+// two slots' metadata per step and keeps it below the tiles; the in-step
+// schedules keep the tiles at the bottom (measured: fewer scalar spills).
+template <typename T, int D>
+struct DkvSmemMetaFirst : DkvMeta<T, D>, DkvTiles<T, D> {};
+template <typename T, int D>
+struct DkvSmemTilesFirst : DkvTiles<T, D>, DkvMeta<T, D> {};
+template <typename T, int D>
+using DkvSmem = typename std::conditional<DkvCfg<T, D>::SKEW, DkvSmemMetaFirst<T, D>, DkvSmemTilesFirst<T, D>>::type;
 
 // One dK/dV item f: (kv head, batch row, key tile) with the kv head fastest
 // and the (batch row, key tile) pairs in the order of decreasing work
@@ -154,26 +179,33 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
     return;
   }
 
-  const T* kvq = reinterpret_cast<const T*>(p.q);
-  const T* kvd = reinterpret_cast<const T*>(p.dout);
+  // the item's sources (rows of the group's first q head; a few base pointers
+  // instead of the whole parameter block live across the loop)
+  const size_t hb = ((size_t)b * p.Hq + (size_t)kvh * grp) * p.L;
+  const T* const q_it = reinterpret_cast<const T*>(p.q) + hb * D;
+  const T* const do_it = reinterpret_cast<const T*>(p.dout) + hb * D;
+  const float* const lse_it = p.lse + hb;
+  const float* const dl_it = p.delta + hb;
+  const int* const klo_it = p.row_klo + (size_t)b * p.L;
+  const int Lr = p.L;
   auto load = [&](T* Qs, T* Gs, float* ls, float* ds, int* ks, int it) {
     const int hh = it / n_t, t = t_first + it % n_t;
     const int i0 = t * C::BQ;
-    const int nr = min(C::BQ, p.L - i0);
-    const size_t rb = ((size_t)b * p.Hq + kvh * grp + hh) * p.L + i0;
-    dma.issue(Qs, kvq + rb * D, nr);
-    dma.issue(Gs, kvd + rb * D, nr);
-    if (w == 0) dma_words(ls, p.lse + rb, nr);
-    if (w == 1) dma_words(ds, p.delta + rb, nr);
-    if (w == 2) dma_words(ks, p.row_klo + (size_t)b * p.L + i0, nr);
+    const int nr = min(C::BQ, Lr - i0);
+    const size_t rb = (size_t)hh * Lr + i0;
+    dma.issue(Qs, q_it + rb * D, nr);
+    dma.issue(Gs, do_it + rb * D, nr);
+    if (w == 0) dma_words(ls, lse_it + rb, nr);
+    if (w == 1) dma_words(ds, dl_it + rb, nr);
+    if (w == 2) dma_words(ks, klo_it + i0, nr);
   };
   constexpr int NS = C::STAGES;
   auto load_slot = [&](int slot, int it) {
     load(sm.Q[slot], sm.G[slot], sm.lse[slot], sm.dl[slot], sm.klo[slot], it);
   };
-  // prologue: the first NS - 1 steps' tiles
+  // prologue: the copies of the first steps (all that run ahead of step 0)
 #pragma unroll
-  for (int x = 0; x < NS - 1; ++x)
+  for (int x = 0; x < (C::SKEW ? NS - 2 : NS - 1); ++x)
     if (x < n_iter) load_slot(x, x);
 
   // this lane's key row of K (role A) or V (role B): the B operand of S = Q K^T
@@ -189,73 +221,77 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
 #pragma unroll
   for (int d = 0; d < D / 32; ++d) gacc[d] = f32x16{};
 
-  auto step = [&](const T* Qs, const T* Gs, const float* ls, const float* ds, const int* ks, int it, auto&& mid) {
-    auto& px = pex[DkvSmem<T, D>::NPEX > 1 ? (it & 1) : 0];
-    const int t = t_first + it % n_t;
-    const int i0 = t * C::BQ;
-    const int nrows = min(C::BQ, p.L - i0);
+  // One step's facts from its slot's band starts (uniform over the workgroup):
+  // the tile's rows, whether the group's keys meet their bands at all, and
+  // whether every (row, key) pair is inside them (no element mask).
+  struct StepInfo {
+    int i0, nrows;
+    bool active, full;
+  };
+  auto info = [&](const int* ks, int it) {
+    StepInfo si;
+    si.i0 = (t_first + it % n_t) * C::BQ;
+    si.nrows = min(C::BQ, p.L - si.i0);
     // rows of this tile: positions off+i0 .. off+i0+nrows-1; band starts are nondecreasing
-    const int p_min = off + i0, p_max = off + i0 + nrows - 1;
+    const int p_min = off + si.i0, p_max = off + si.i0 + si.nrows - 1;
     auto band = [&](int qi) {
       const int bq = max(0, ks[qi]);
-      return p.window >= 0 ? max(bq, off + i0 + qi - p.window) : bq;
+      return p.window >= 0 ? max(bq, off + si.i0 + qi - p.window) : bq;
     };
-    // (uniform values; readfirstlane lets the compiler branch on the scalar unit)
+    // (readfirstlane lets the compiler branch on the scalar unit)
     const int bs_min = __builtin_amdgcn_readfirstlane(band(0));
-    const int bs_max = __builtin_amdgcn_readfirstlane(band(nrows - 1));
-    const bool active = !(jw > p_max || jw + 31 < bs_min);
-    // every (row, key) pair of the group inside the band: no element mask
-    const bool full = (nrows == C::BQ) && jw >= bs_max && jw + 31 <= p_min;
-
-    // first half: role A forms P and publishes it, role B forms dP
-    f32x16 sacc = f32x16{};
-    if (active) {
-      const T* src = role_a ? Qs : Gs;
-      if constexpr (C::AHEAD > 0) {
-        lds_mfma_pipeline<D / 16, C::AHEAD, F>([&](int kk) { return acc.row(src, 0, kk); },
-                                               [&](int kk, const F& a) { sacc = mma(a, kv[kk], sacc); });
-      } else {
+    const int bs_max = __builtin_amdgcn_readfirstlane(band(si.nrows - 1));
+    si.active = !(jw > p_max || jw + 31 < bs_min);
+    si.full = (si.nrows == C::BQ) && jw >= bs_max && jw + 31 <= p_min;
+    return si;
+  };
+  // acc += rows of src (Q or dO) x this lane's K or V row: S^T or dP^T blocks
+  auto rows_x_kv = [&](const T* src, f32x16& sacc) {
+    if constexpr (C::AHEAD > 0) {
+      lds_mfma_pipeline<D / 16, C::AHEAD, F>([&](int kk) { return acc.row(src, 0, kk); },
+                                             [&](int kk, const F& a) { sacc = mma(a, kv[kk], sacc); });
+    } else {
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) sacc = mma(acc.row(src, 0, kk), kv[kk], sacc);
-      }
-      if (role_a) {
-        // accumulator r: query row acc_row(r, g) of the tile, key j
+      for (int kk = 0; kk < D / 16; ++kk) sacc = mma(acc.row(src, 0, kk), kv[kk], sacc);
+    }
+  };
+  // role A: S -> P in place (exp2 against the rows' LSE, 0 outside the band),
+  // then published for role B; accumulator r is query row acc_row(r, g), key j
+  auto to_p = [&](f32x16& sacc, const float* ls, const int* ks, const StepInfo& si, auto& px) {
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          // rows 8*rq + 4*g + e: their LSE (and band starts) as one 16-byte read
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + 8 * rq + 4 * g);
+    for (int rq = 0; rq < 4; ++rq) {
+      // rows 8*rq + 4*g + e: their LSE (and band starts) as one 16-byte read
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + 8 * rq + 4 * g);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sacc[4 * rq + e] = fast_exp2(fmaf(sacc[4 * rq + e], p.scale_log2, -l4[e] * kLog2e));
-          if (!full) {
-            const int4 k4 = *reinterpret_cast<const int4*>(ks + 8 * rq + 4 * g);
+      for (int e = 0; e < 4; ++e) sacc[4 * rq + e] = fast_exp2(fmaf(sacc[4 * rq + e], p.scale_log2, -l4[e] * kLog2e));
+      if (!si.full) {
+        const int4 k4 = *reinterpret_cast<const int4*>(ks + 8 * rq + 4 * g);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int qi = 8 * rq + 4 * g + e;
-              int bq = max(0, k4[e]);
-              if (p.window >= 0) bq = max(bq, off + i0 + qi - p.window);
-              const bool in = (qi < nrows) & (j >= bq) & (j <= off + i0 + qi);
-              sacc[4 * rq + e] = in ? sacc[4 * rq + e] : 0.f;
-            }
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int qi = 8 * rq + 4 * g + e;
+          int bq = max(0, k4[e]);
+          if (p.window >= 0) bq = max(bq, off + si.i0 + qi - p.window);
+          const bool in = (qi < si.nrows) & (j >= bq) & (j <= off + si.i0 + qi);
+          sacc[4 * rq + e] = in ? sacc[4 * rq + e] : 0.f;
         }
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          px[kg][qd][lane] = f32x4{sacc[4 * qd], sacc[4 * qd + 1], sacc[4 * qd + 2], sacc[4 * qd + 3]};
       }
     }
-    mid();   // the hand-over barrier (and ring maintenance)
-    if (!active) return;
-    // second half: role A accumulates dV^T = dO^T P, role B dK^T = Q^T dS
-    if (!role_a) {
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const f32x4 pq = px[kg][qd][lane];
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds + 8 * qd + 4 * g);  // rows acc_row(4*qd + e, g)
+    for (int qd = 0; qd < 4; ++qd)
+      px[kg][qd][lane] = f32x4{sacc[4 * qd], sacc[4 * qd + 1], sacc[4 * qd + 2], sacc[4 * qd + 3]};
+  };
+  // role B: dP -> dS = P (dP - Delta) in place, P from role A
+  auto to_ds = [&](f32x16& sacc, const auto& px, const float* ds) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[4 * qd + e] = pq[e] * (sacc[4 * qd + e] - d4[e]);
-      }
+    for (int qd = 0; qd < 4; ++qd) {
+      const f32x4 pq = px[kg][qd][lane];
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds + 8 * qd + 4 * g);  // rows acc_row(4*qd + e, g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sacc[4 * qd + e] = pq[e] * (sacc[4 * qd + e] - d4[e]);
     }
-    const T* src = role_a ? Gs : Qs;
+  };
+  // gacc += src^T (P or dS): dV^T = dO^T P (role A) or dK^T = Q^T dS (role B)
+  auto accumulate = [&](const T* src, const f32x16& sacc) {
     if constexpr (C::AHEAD > 0) {
       const F sf[2] = {acc_to_frag<T>(sacc, 0), acc_to_frag<T>(sacc, 1)};
       constexpr int ND = D / 32;
@@ -272,18 +308,86 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
     }
   };
 
-  if constexpr (NS >= 3) {
-    // One barrier per step, at the hand-over: by then every wave has finished
-    // the previous step, so the copies of step it + 2 go into its slot right
-    // after the barrier, and the copies of step it + 1 (issued two steps
-    // earlier) are complete and visible for its first half.  The ring is
-    // unrolled NS times so every slot's LDS address is a constant.
-    auto stage = [&](int it, int slot) {
-      step(sm.Q[slot], sm.G[slot], sm.lse[slot], sm.dl[slot], sm.klo[slot], it, [&]() {
-        if (it + 1 < n_iter) wait_global();
+  if constexpr (C::SKEW) {
+    // Role B runs one step behind role A: in step t role A forms S, P and dV
+    // of step t while role B finishes step t - 1 (dS from the P role A
+    // published then, dK) and forms dP of step t.  Neither waits for the other
+    // inside a step; the one barrier per step (at its end) publishes P, retires
+    // a ring slot and makes the next step's copies visible.  The ring holds the
+    // previous step (role B's Q and Delta), the current one and LA steps of
+    // copies in flight.  The loop is not unrolled over the slots: a copy of
+    // the step per slot and role outgrows the instruction cache.
+    constexpr int LA = NS - 2;
+    const int n_vm = 2 * dma.count() + (w < 3 ? 1 : 0);   // this wave's copies per step
+    wait_global();   // the prologue's copies (steps 0 .. LA - 1)
+    __syncthreads();
+    // Each role runs a loop of its own (same copies and barriers, one branch
+    // per item rather than per step: the register allocator then sees one
+    // role's live values at a time).
+    auto run = [&](auto is_a) {
+      constexpr bool A = decltype(is_a)::value;
+      f32x16 dp = f32x16{};   // role B: dP of the previous step
+      bool act_prev = false;  // role B: the previous step met the group's keys
+      auto stage = [&](int t, int x) {
+        if (t + LA < n_iter) load_slot(x + LA < NS ? x + LA : x + LA - NS, t + LA);   // step t - 2's slot
+        if constexpr (A) {
+          if (t < n_iter) {
+            const StepInfo si = info(sm.klo[x], t);
+            if (si.active) {
+              f32x16 sacc = f32x16{};
+              rows_x_kv(sm.Q[x], sacc);
+              to_p(sacc, sm.lse[x], sm.klo[x], si, pex[t & 1]);
+              __builtin_amdgcn_sched_barrier(0);   // keep the phases' operands apart
+              accumulate(sm.G[x], sacc);
+            }
+          }
+        } else {
+          const int xp = x == 0 ? NS - 1 : x - 1;
+          if (act_prev) {
+            to_ds(dp, pex[(t - 1) & 1], sm.dl[xp]);
+            accumulate(sm.Q[xp], dp);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          act_prev = false;
+          if (t < n_iter) {
+            act_prev = info(sm.klo[x], t).active;
+            if (act_prev) {
+              dp = f32x16{};
+              rows_x_kv(sm.G[x], dp);
+            }
+          }
+        }
+        // step t + 1's copies complete (those of later steps may stay in flight)
+        const int later = min(t + LA, n_iter - 1) - (t + 1);
+        if (t + 1 < n_iter) wait_global_le(later > 0 ? n_vm * later : 0);
         __syncthreads();
-        if (it + 2 < n_iter) load_slot((slot + 2) % NS, it + 2);
-      });
+      };
+      for (int t = 0, x = 0; t <= n_iter; ++t, x = (x + 1 == NS) ? 0 : x + 1) stage(t, x);
+    };
+    if (role_a) run(std::true_type{});
+    else run(std::false_type{});
+  } else if constexpr (NS >= 3) {
+    // Role B in step with role A, one barrier per step, at the hand-over: by
+    // then every wave has finished the previous step, so the copies of step
+    // it + 2 go into its slot right after the barrier, and the copies of step
+    // it + 1 (issued two steps earlier) are complete and visible for its first
+    // half.  The ring is unrolled NS times so every slot's LDS address is a
+    // constant.
+    auto stage = [&](int it, int x) {
+      auto& px = pex[it & 1];
+      const StepInfo si = info(sm.klo[x], it);
+      f32x16 sacc = f32x16{};
+      if (si.active) {
+        rows_x_kv(role_a ? sm.Q[x] : sm.G[x], sacc);
+        if (role_a) to_p(sacc, sm.lse[x], sm.klo[x], si, px);
+      }
+      if (it + 1 < n_iter) wait_global();
+      __syncthreads();   // the hand-over
+      if (it + 2 < n_iter) load_slot((x + 2) % NS, it + 2);
+      if (si.active) {
+        if (!role_a) to_ds(sacc, px, sm.dl[x]);
+        accumulate(role_a ? sm.G[x] : sm.Q[x], sacc);
+      }
     };
     wait_global();   // the prologue's copies
     __syncthreads();
@@ -293,14 +397,25 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
         if (it + x < n_iter) stage(it + x, x);
     }
   } else {
-    // two slots: copies for step it + 1 go out after the barrier at the top of
-    // step it, which also makes step it's copies visible
-    auto stage = [&](int it, int slot) {
+    // Two slots, role B in step with role A: copies for step it + 1 go out
+    // after the barrier at the top of step it (which also makes step it's
+    // copies visible); P crosses at a second barrier inside the step.
+    auto stage = [&](int it, int x) {
       wait_global();
       __syncthreads();
-      if (it + 1 < n_iter) load_slot((slot + 1) % NS, it + 1);
+      if (it + 1 < n_iter) load_slot((x + 1) % NS, it + 1);
       __builtin_amdgcn_sched_barrier(0);
-      step(sm.Q[slot], sm.G[slot], sm.lse[slot], sm.dl[slot], sm.klo[slot], it, [&]() { __syncthreads(); });
+      const StepInfo si = info(sm.klo[x], it);
+      f32x16 sacc = f32x16{};
+      if (si.active) {
+        rows_x_kv(role_a ? sm.Q[x] : sm.G[x], sacc);
+        if (role_a) to_p(sacc, sm.lse[x], sm.klo[x], si, pex[0]);
+      }
+      __syncthreads();   // the hand-over
+      if (si.active) {
+        if (!role_a) to_ds(sacc, pex[0], sm.dl[x]);
+        accumulate(role_a ? sm.G[x] : sm.Q[x], sacc);
+      }
     };
     for (int it = 0; it < n_iter; it += NS) {
 #pragma unroll
@@ -334,7 +449,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
 // each SIMD at D = 256; the matrix-core work is the same as one wave doing all.
 template <typename T, int D>
 struct DqCfg {
-  static constexpr int NQG = BwdShape<T, D>::GROUPS;   // query groups of 32 rows
+  static constexpr int NQG = BwdShape<T, D>::NT / 128;   // query groups of 32 rows
   static constexpr int NW = 2 * NQG;
   static constexpr int NT = 64 * NW;
   static constexpr int BM = 32 * NQG;               // query rows per workgroup
@@ -750,6 +865,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void b
     DkvSmem<T, D> kv;
     DqSmem<T, D> q;
   } sm;
+  auto dkdv = [&](int f) { dkdv_item<T, D>(p, sm.kv, f); };
   const int n_kv = (MODE & 1) ? p.B * ((p.S + DkvCfg<T, D>::BK - 1) / DkvCfg<T, D>::BK) * p.Hkv : 0;
   const int n_q = (MODE & 2) ? p.B * ((p.L + DqCfg<T, D>::BM - 1) / DqCfg<T, D>::BM) * p.Hq : 0;
   const int total = n_kv + n_q;
@@ -763,11 +879,11 @@ __global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void b
     __syncthreads();  // every thread has the item before the item reuses the LDS
     if (f >= total) break;
     if constexpr (MODE == 1) {
-      dkdv_item<T, D>(p, sm.kv, f);
+      dkdv(f);
     } else if constexpr (MODE == 2) {
       dq_item<T, D>(p, sm.q, f);
     } else {
-      if (f < n_kv) dkdv_item<T, D>(p, sm.kv, f);
+      if (f < n_kv) dkdv(f);
       else dq_item<T, D>(p, sm.q, f - n_kv);
     }
     __syncthreads();  // this item's LDS is dead before the next fetch

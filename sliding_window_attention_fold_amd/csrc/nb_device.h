@@ -229,6 +229,14 @@ struct TileDma {
       voff[x] = (uint32_t)(r * RB + ((pc ^ TL::swz(r)) * 16));
     }
   }
+  // number of copies one call of issue() makes from this wave
+  __device__ __forceinline__ int count() const {
+    const int w = wave_id();
+    int c = 0;
+#pragma unroll
+    for (int x = 0; x < PER; ++x) c += (TL::BLOCKS % NW == 0 || w + x * NW < TL::BLOCKS) ? 1 : 0;
+    return c;
+  }
   __device__ __forceinline__ void issue(T* lds, const T* __restrict__ src, int nrows) const {
     // The buffer-resource type exists only for the device target; the host
     // pass (which only needs the kernels' launch stubs) sees an empty body.
@@ -318,6 +326,30 @@ __device__ __forceinline__ void lds_mfma_pipeline(ReadFn&& rd, MmaFn&& mm) {
 
 // Wait until this wave's global reads (including copies into LDS) have landed.
 __device__ __forceinline__ void wait_global() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Waits until at most n (wave-uniform, 0 <= n <= 15; larger n waits for 15) of
+// this wave's vector-memory operations are outstanding.  They complete in
+// issue order, so this waits for everything but the n most recent.
+__device__ __forceinline__ void wait_global_le(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
+    case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
+  }
+}
 
 // Precomputed readers for bf16 tiles.  The XOR swizzle only touches the low 4
 // chunk bits, so every operand address is one of a few per-lane bases plus a
