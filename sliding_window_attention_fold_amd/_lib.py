@@ -1,4 +1,5 @@
-"""ctypes loader for libnbattn.so (the C-ABI declared in include/nbattn.h).
+"""ctypes loader for libnbattn.so (the C-ABI declared in include/nbattn.h and
+include/nbexchange.h).
 
 The library is built in-tree by ``sliding_window_attention_fold_amd.build``.  If it
 is missing, loading fails loudly: there is no fallback implementation.
@@ -15,7 +16,7 @@ NB_BF16, NB_F32 = 0, 1
 NB_SEG_HEADER = 16
 HDR = dict(n_seg=0, max_q=1, max_k=2, status=3, lo=4, B=5, L=6, S=7, window=8, n_real=9)
 
-# name -> (restype, argtypes); every symbol include/nbattn.h declares
+# name -> (restype, argtypes); every symbol include/*.h declares
 _c = ctypes
 _P, _I, _F, _Z = _c.c_void_p, _c.c_int, _c.c_float, _c.c_size_t
 SIGNATURES = {
@@ -41,7 +42,15 @@ SIGNATURES = {
     "nb_attn_bwd_prep": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _Z, _P]),
     "nb_attn_bwd_main": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P, _Z, _P]),
     "nb_owner_attended": (_I, [_P, _P, _I, _I, _I, _P, _I, _P, _P]),
+    # include/nbexchange.h
+    "nb_exchange_plan_elems": (_Z, [_I]),
+    "nb_exchange_plan": (_I, [_P, _P, _I, _I, _I, _P, _Z, _P]),
+    "nb_exchange_send_index_elems": (_Z, [_I, _I]),
+    "nb_exchange_send_index": (_I, [_P, _I, _I, _P, _Z, _P]),
+    "nb_exchange_gather": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "nb_exchange_scatter_add": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
 }
+NB_XCH_MAX_RANKS = 64
 
 _LIB = None
 

@@ -20,6 +20,7 @@ SOURCES = [
     "csrc/segment_build.hip",
     "csrc/attn_fwd.hip",
     "csrc/attn_bwd.hip",
+    "csrc/exchange.hip",
     "csrc/nbattn_host.cpp",
 ]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

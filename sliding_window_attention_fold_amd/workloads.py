@@ -131,7 +131,9 @@ class DocMap:
     owners: List[int] = field(default_factory=list)     # owner rank of each chunk (ascending)
 
 
-def make_doc_map(w: Workload) -> DocMap:
+def global_doc_map(w: Workload):
+    """The whole sequence's doc ids ``[B, S_global]`` (int32) and pad mask (or None),
+    as every context-parallel rank holds them (replicated)."""
     rng = np.random.Generator(np.random.PCG64(w.seed))
     n_rows = w.B if w.per_row_docs else 1
     rows = [_fill_row(rng, w.S_global, w.doc_len) for _ in range(n_rows)]
@@ -140,6 +142,11 @@ def make_doc_map(w: Workload) -> DocMap:
     if w.pad_tail > 0:
         pad = np.zeros_like(glob, dtype=np.uint8)
         pad[:, w.S_global - w.pad_tail:] = 1
+    return glob, pad
+
+
+def make_doc_map(w: Workload) -> DocMap:
+    glob, pad = global_doc_map(w)
     q_end = w.q_start + w.L
     if w.mode == "halo":
         # the neighbourhood starts at the first position of the document that

@@ -10,13 +10,16 @@ import pytest
 from sliding_window_attention_fold_amd import _lib
 from sliding_window_attention_fold_amd import workloads as wl
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "nbattn.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(nb_\w+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, h)).read(), flags=re.S)
+            names |= set(re.findall(r"\b(nb_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported():
@@ -124,3 +127,31 @@ def test_workload_generators_deterministic_and_shaped():
     q2 = wl.make_tensors(w, 256)
     assert all((x == y).all() for x, y in zip(q1, q2))
     assert q1[0].shape == (1, 2, 128, 64) and q1[1].shape == (1, 1, 256, 64)
+
+
+def test_exchange_preflight_rejects_bad_arguments():
+    """The exchange entry points check everything on the host first (no GPU needed:
+    every call below returns before any launch)."""
+    lib = _lib.load()
+    assert lib.nb_exchange_plan_elems(0) == 0 and lib.nb_exchange_plan_elems(65) == 0
+    P = 4
+    n = lib.nb_exchange_plan_elems(P)
+    assert n == 8 + 5 * P + 3 * P * P
+    assert lib.nb_exchange_send_index_elems(P, 30) == 0          # N not a multiple of P
+    assert lib.nb_exchange_send_index_elems(P, 32) == P * 32
+    assert lib.nb_exchange_plan(None, None, 1, 32, P, FAKE, n, None) == _lib.NB_ERR_INVALID_ARG
+    assert lib.nb_exchange_plan(FAKE, None, 1, 30, P, FAKE, n, None) == _lib.NB_ERR_INVALID_ARG
+    assert lib.nb_exchange_plan(FAKE, None, 0, 32, P, FAKE, n, None) == _lib.NB_ERR_INVALID_ARG
+    assert lib.nb_exchange_plan(FAKE, None, 1, 32, 65, FAKE, n, None) == _lib.NB_ERR_INVALID_ARG
+    assert lib.nb_exchange_plan(FAKE, None, 1, 32, P, FAKE, n - 1, None) == _lib.NB_ERR_WORKSPACE
+    assert lib.nb_exchange_send_index(FAKE, P, 32, FAKE, P * 32 - 1, None) == _lib.NB_ERR_WORKSPACE
+    ptrs = (ctypes.c_void_p * P)(*([None] * P))
+    # D * element size must be a multiple of 16 bytes; dtype must be known
+    assert lib.nb_exchange_gather(FAKE, FAKE, 1, 1, 32, 4, P, _lib.NB_BF16, ptrs, None) == _lib.NB_ERR_INVALID_ARG
+    assert lib.nb_exchange_gather(FAKE, FAKE, 1, 1, 32, 8, P, 7, ptrs, None) == _lib.NB_ERR_UNSUPPORTED
+    assert lib.nb_exchange_scatter_add(ptrs, FAKE, 1, 1, 32, 8, P, _lib.NB_BF16, None, None) == \
+        _lib.NB_ERR_INVALID_ARG
+    bad = (ctypes.c_void_p * P)(*([FAKE + 4] + [None] * (P - 1)))   # misaligned rank buffer
+    assert lib.nb_exchange_gather(FAKE, FAKE, 1, 1, 32, 8, P, _lib.NB_BF16, bad, None) == _lib.NB_ERR_INVALID_ARG
+    assert lib.nb_exchange_gather(FAKE, FAKE, 300, 300, 32, 8, P, _lib.NB_BF16, ptrs, None) == \
+        _lib.NB_ERR_INVALID_ARG                                      # B * C > 65535
