@@ -51,7 +51,7 @@ def kernel_source_hash(fname: str) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str, workload: str):
+def read_traffic(kernel: str, workload: str, source: str = ""):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it matches the current source."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
@@ -62,7 +62,7 @@ def read_traffic(kernel: str, workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("source_sha256_16") != kernel_source_hash(KERNELS[kernel][1]):
+    if vals.get("source_sha256_16") != kernel_source_hash(source or KERNELS[kernel][1]):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -101,6 +101,20 @@ def cpu_baseline(w, dm, tensors, rows: int, kv_heads: int):
                       f"{dt:.1f} s"}
 
 
+def calibration_copy(mib: int, dev) -> None:
+    """One plain copy of `mib` MiB read + `mib` MiB written, through the library's own 16-byte streaming copy
+    (the exchange gather of a one-rank world whose single document covers everything), so that hardware byte
+    counters can be scaled by what they read for the same access width."""
+    import torch
+
+    from sliding_window_attention_fold_amd import exchange as xg
+
+    n = (mib << 20) // 256                      # tokens of 128 bf16
+    plan = xg.exchange_plan(torch.ones((1, n), dtype=torch.int32, device=dev), 1)
+    xg.needed_gather(torch.zeros((1, 1, n, 128), dtype=torch.bfloat16, device=dev), plan)
+    torch.cuda.synchronize()
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,7 +125,12 @@ def main() -> int:
     ap.add_argument("--cpu-kv-heads", type=int, default=4, help="kv heads (with their q heads) of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
-                    help="after timing, run one plain device copy of this many MiB (counter calibration)")
+                    help="after timing, run one plain copy of this many MiB with the library's 16-byte streaming "
+                         "copy (counter calibration)")
+    ap.add_argument("--part", choices=["attention", "exchange"], default="attention",
+                    help="attention: the hot path (default); exchange: the emulated needed-range K/V exchange")
+    ap.add_argument("--exchange-config", type=int, default=4,
+                    help="workload whose world the exchange part emulates (default 4: 8 ranks, one document)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -121,6 +140,9 @@ def main() -> int:
     if int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only (WORLD_SIZE > 1)", file=sys.stderr)
         return 2
+
+    if args.part == "exchange":
+        return exchange_main(args)
 
     import numpy as np
     import torch
@@ -214,10 +236,7 @@ def main() -> int:
            for i, n in enumerate(names)}
 
     if args.copy_mib > 0:
-        a = torch.empty((args.copy_mib << 20,), dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
+        calibration_copy(args.copy_mib, dev)
 
     tflops = useful / (ms_step * 1e-3) / 1e12
     dom = max(KERNELS, key=lambda n: per[n])
@@ -255,6 +274,126 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, dm, (q, k, v, do), args.cpu_rows, args.cpu_kv_heads)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def exchange_main(args) -> int:
+    """The needed-range K/V exchange of one layer, emulated for every rank of the world on one GPU: plan
+    and send index from the replicated doc ids, every rank's received K range (gather), and the backward
+    index_add of every rank's dK range (scatter_add).  Workload: the single long document of the needed-range
+    world (8 ranks of 8192 tokens, K [1, 8, 65536, 128] bf16), or --exchange-config's world.  HBM-bound; the roofline
+    is the gather's algorithmic bytes (every received token read once and written once)."""
+    import numpy as np
+    import torch
+
+    from sliding_window_attention_fold_amd import _lib
+    from sliding_window_attention_fold_amd import exchange as xg
+    from sliding_window_attention_fold_amd import workloads as wl
+
+    lib = _lib.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    cfg = args.exchange_config
+    w = wl.get(cfg)
+    ids, pad = wl.global_doc_map(w)
+    Bn, N = ids.shape
+    P, C, D = w.cp_size, w.Hkv, w.D
+    ids_d = torch.from_numpy(ids).to(dev)
+    pad_d = None if pad is None else torch.from_numpy(pad).to(dev)
+    plan = xg.exchange_plan(ids_d, P, pad_d)
+    g = torch.Generator("cpu").manual_seed(w.seed)
+    x = torch.randn((Bn, C, N, D), generator=g).to(torch.bfloat16).to(dev)
+    recv = [torch.empty((Bn, C, int(R), D), dtype=x.dtype, device=dev) for R in plan.recv_len]
+    grads = [torch.randn(t.shape, generator=g).to(torch.bfloat16).to(dev) for t in recv]
+    gx = torch.empty_like(x)
+    n_plan = lib.nb_exchange_plan_elems(P)
+    n_si = lib.nb_exchange_send_index_elems(P, N)
+    si = torch.empty((n_si,), dtype=torch.int32, device=dev)
+    Pp = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    rp = (ctypes.c_void_p * P)(*[t.data_ptr() if t.numel() else None for t in recv])
+    gp = (ctypes.c_void_p * P)(*[t.data_ptr() if t.numel() else None for t in grads])
+    calls = {
+        "plan": lambda: lib.nb_exchange_plan(Pp(ids_d), Pp(pad_d), Bn, N, P, Pp(plan.buf), n_plan, sp),
+        "send_index": lambda: lib.nb_exchange_send_index(Pp(plan.buf), P, N, Pp(si), n_si, sp),
+        "gather": lambda: lib.nb_exchange_gather(Pp(x), Pp(plan.buf), Bn, C, N, D, P, _lib.NB_BF16, rp, sp),
+        "scatter_add": lambda: lib.nb_exchange_scatter_add(gp, Pp(plan.buf), Bn, C, N, D, P, _lib.NB_BF16, Pp(gx),
+                                                           sp),
+    }
+    names = list(calls)
+
+    def step(events=None):
+        for i, n in enumerate(names):
+            if events is not None:
+                events[i].record(stream)
+            st = calls[n]()
+            if st != 0:
+                raise _lib.NbError(st, n)
+        if events is not None:
+            events[len(names)].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for s in range(args.steps):
+        step(evs[s])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    per = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+           for i, n in enumerate(names)}
+    if args.copy_mib > 0:
+        calibration_copy(args.copy_mib, dev)
+    T = int(plan.recv_len.sum())
+    row = C * D * 2
+    gather_bytes = 2 * Bn * T * row
+    scatter_bytes = Bn * (T + N) * row
+    moved = gather_bytes + scatter_bytes
+    rec = {
+        "metric": "emulated needed-range K/V exchange, HBM GB/s (gather + index_add backward)",
+        "value": round(moved / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"config{cfg} world: {w.name}", "cp_size": P, "B": Bn, "C": C, "N": N, "D": D,
+                   "use_halo": plan.use_halo, "halo_size": plan.halo_size, "received_tokens": T,
+                   "bytes_per_step": moved},
+        "ms_per_kernel": {n: round(per[n], 5) for n in names},
+        "roofline": {
+            "kernel": "gather", "bound": "hbm", "achieved": round(gather_bytes / (per["gather"] * 1e-3) / 1e9, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gather_bytes / (per["gather"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "traffic": read_traffic("exchange_gather", f"config{cfg}world", "exchange.hip"),
+            "algorithmic_bytes_per_launch": gather_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        from oracle import exchange_oracle as ex
+        op = ex.a2a_plan(ids, pad, P)
+        xs = x[:, :1].float().cpu().numpy()          # one of the C channels
+        gs = [t[:, :1].float().cpu().numpy() for t in grads]
+        tc = time.perf_counter()
+        ex.a2a_forward(xs, op)
+        ex.a2a_backward(gs, op, xs.shape)
+        dt = time.perf_counter() - tc
+        rec["cpu_baseline"] = {"value": round(moved / C / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"fp64 numpy exchange oracle (plan excluded), channel 0 of {C}, all "
+                                         f"{P} ranks; {dt:.1f} s"}
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

@@ -9,8 +9,9 @@
 // onto the source tokens).  Readings where the page is silent are stated in
 // nbexchange.h.
 //
-// The plan is integer work over the replicated document ids (one workgroup:
-// block-wide reductions per rank and row).  On one device the exchange's
+// The plan is integer work over the replicated document ids (one workgroup
+// per rank: block-wide reductions per row; then one workgroup for the splits
+// and offsets).  On one device the exchange's
 // forward is, per rank, one contiguous copy of x[:, :, s_first_r:real_end_r]
 // (the pieces of all sources in source order are exactly that slice); the
 // backward sums, per token, the gradients of the ranks that needed it, in
@@ -64,54 +65,61 @@ __device__ __forceinline__ int folded(const int32_t* ids, const uint8_t* pad, in
   return (v > 0 && (pad == nullptr || pad[o] == 0)) ? v : 0;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void xch_plan_kernel(const int32_t* ids, const uint8_t* pad, int B,
-                                                                int N, int P, int32_t* plan) {
+// Needed range of rank blockIdx.x: union over the rows of [start of the run
+// holding r L, one past the chunk's last non-padding position).
+__global__ __launch_bounds__(kPlanThreads) void xch_range_kernel(const int32_t* ids, const uint8_t* pad, int B,
+                                                                 int N, int P, int32_t* plan) {
   __shared__ int red[kPlanThreads / 64];
+  const int tid = threadIdx.x, r = blockIdx.x;
+  const int L = N / P;
+  const int lo = r * L, hi = lo + L;
+  int first = INT_MAX, end = -1;
+  for (int b = 0; b < B; ++b) {
+    // last non-padding position of the row's chunk
+    int m = -1;
+    for (int j = lo + tid; j < hi; j += kPlanThreads)
+      if (folded(ids, pad, N, b, j) != 0) m = j;
+    m = block_max(m, red);
+    if (m < 0) continue;   // the row has no real token in this chunk
+    end = max(end, m + 1);
+    // start of the run of equal ids holding position lo: the last j <= lo
+    // whose left neighbour carries another id (0 if none)
+    const int id = folded(ids, pad, N, b, lo);
+    int s = lo;
+    if (id != 0) {
+      int t = 0;
+      for (int j = 1 + tid; j <= lo; j += kPlanThreads)
+        if (folded(ids, pad, N, b, j - 1) != id) t = j;
+      s = block_max(t, red);
+    }
+    first = min(first, s);
+  }
+  if (tid == 0) {
+    const PlanLayout lay(P);
+    plan[lay.s_first + r] = end < 0 ? lo : first;
+    plan[lay.real_end + r] = end < 0 ? lo : end;
+  }
+}
+
+// The rest of the plan from the ranges: straddles, splits, offsets, header.
+__global__ __launch_bounds__(kPlanThreads) void xch_offsets_kernel(int N, int P, int32_t* plan) {
   __shared__ int sf[NB_XCH_MAX_RANKS], re[NB_XCH_MAX_RANKS];
   __shared__ int spl[NB_XCH_MAX_RANKS * NB_XCH_MAX_RANKS];
   const int tid = threadIdx.x;
   const int L = N / P;
-  for (int r = 0; r < P; ++r) {
-    const int lo = r * L, hi = lo + L;
-    int first = INT_MAX, end = -1;
-    for (int b = 0; b < B; ++b) {
-      // last non-padding position of the row's chunk
-      int m = -1;
-      for (int j = lo + tid; j < hi; j += kPlanThreads)
-        if (folded(ids, pad, N, b, j) != 0) m = j;
-      m = block_max(m, red);
-      if (m < 0) continue;   // the row has no real token in this chunk
-      end = max(end, m + 1);
-      // start of the run of equal ids holding position lo: the last j <= lo
-      // whose left neighbour carries another id (0 if none)
-      const int id = folded(ids, pad, N, b, lo);
-      int s = lo;
-      if (id != 0) {
-        int t = 0;
-        for (int j = 1 + tid; j <= lo; j += kPlanThreads)
-          if (folded(ids, pad, N, b, j - 1) != id) t = j;
-        s = block_max(t, red);
-      }
-      first = min(first, s);
-    }
-    if (tid == 0) {
-      sf[r] = end < 0 ? lo : first;
-      re[r] = end < 0 ? lo : end;
-    }
+  const PlanLayout lay(P);
+  if (tid < P) {
+    sf[tid] = plan[lay.s_first + tid];
+    re[tid] = plan[lay.real_end + tid];
   }
   __syncthreads();
-  const PlanLayout lay(P);
   for (int x = tid; x < P * P; x += kPlanThreads) {
     const int s = x / P, r = x % P;
     const int a = max(s * L, sf[r]), e = min((s + 1) * L, re[r]);
     spl[x] = max(0, e - a);
     plan[lay.splits + x] = spl[x];
   }
-  if (tid < P) {
-    plan[lay.s_first + tid] = sf[tid];
-    plan[lay.real_end + tid] = re[tid];
-    plan[lay.back + tid] = tid * L - sf[tid];
-  }
+  if (tid < P) plan[lay.back + tid] = tid * L - sf[tid];
   __syncthreads();
   if (tid < P) {
     // sender tid: where each destination's piece starts in its send buffer
@@ -211,12 +219,25 @@ __global__ __launch_bounds__(kStreamThreads) void xch_scatter_add_kernel(XchPtrs
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    for (int r = 0; r < P; ++r) {
-      if (j < sf[r] || j >= re[r] || grads.p[r] == nullptr) continue;
-      const int R = re[r] - sf[r];
-      const V v = reinterpret_cast<const V*>(grads.p[r])[((size_t)bc * R + (j - sf[r])) * VPR + c];
+    // loads of up to four ranks in flight before their sums (the sums keep rank order)
+    for (int r0 = 0; r0 < P; r0 += 4) {
+      V v[4];
+      bool h[4];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += (float)v[e];
+      for (int u = 0; u < 4; ++u) {
+        const int r = r0 + u;
+        h[u] = r < P && j >= sf[r] && j < re[r] && grads.p[r] != nullptr;
+        if (h[u]) {
+          const int R = re[r] - sf[r];
+          v[u] = reinterpret_cast<const V*>(grads.p[r])[((size_t)bc * R + (j - sf[r])) * VPR + c];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (h[u]) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] += (float)v[u][e];
+        }
     }
     V o;
 #pragma unroll
@@ -271,8 +292,12 @@ int nb_exchange_plan(const int32_t* doc_ids, const uint8_t* pad_mask, int B, int
   if (B < 1 || B > 65535 || !nb::ranks_ok(N, cp_size) || (int64_t)B * N >= ((int64_t)1 << 31))
     return NB_ERR_INVALID_ARG;
   if (plan_elems < nb_exchange_plan_elems(cp_size)) return NB_ERR_WORKSPACE;
-  hipLaunchKernelGGL(nb::xch_plan_kernel, dim3(1), dim3(nb::kPlanThreads), 0, (hipStream_t)stream, doc_ids,
+  hipLaunchKernelGGL(nb::xch_range_kernel, dim3(cp_size), dim3(nb::kPlanThreads), 0, (hipStream_t)stream, doc_ids,
                      pad_mask, B, N, cp_size, plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return nb::map_hip(e);
+  hipLaunchKernelGGL(nb::xch_offsets_kernel, dim3(1), dim3(nb::kPlanThreads), 0, (hipStream_t)stream, N, cp_size,
+                     plan);
   return nb::map_hip(hipGetLastError());
 }
 
