@@ -23,6 +23,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -43,11 +44,23 @@ KERNELS = {
 
 
 def kernel_source_hash(fname: str) -> str:
+    """First 16 hex digits of the sha256 over a kernel source and the local headers it includes (recursively,
+    in include order): a profile taken from other code no longer matches."""
     csrc = os.path.join(ROOT, "sliding_window_attention_fold_amd", "csrc")
     h = hashlib.sha256()
-    for f in (fname, "nb_device.h"):
+    seen = []
+
+    def visit(f):
+        if f in seen or not os.path.exists(os.path.join(csrc, f)):
+            return
+        seen.append(f)
         with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+            data = fh.read()
+        h.update(data)
+        for m in re.finditer(rb'^#include "([^"]+)"', data, re.M):
+            visit(m.group(1).decode())
+
+    visit(fname)
     return h.hexdigest()[:16]
 
 
@@ -129,6 +142,9 @@ def main() -> int:
                          "copy (counter calibration)")
     ap.add_argument("--part", choices=["attention", "exchange"], default="attention",
                     help="attention: the hot path (default); exchange: the emulated needed-range K/V exchange")
+    ap.add_argument("--kv", choices=["concat", "chunks"], default="concat",
+                    help="concat: K/V as one neighbourhood buffer (default); chunks: the window-trimmed owner "
+                         "chunks read in place (ring workloads)")
     ap.add_argument("--exchange-config", type=int, default=4,
                     help="workload whose world the exchange part emulates (default 4: 8 ranks, one document)")
     args = ap.parse_args()
@@ -143,6 +159,8 @@ def main() -> int:
 
     if args.part == "exchange":
         return exchange_main(args)
+    if args.kv == "chunks":
+        return chunks_main(args)
 
     import numpy as np
     import torch
@@ -278,6 +296,141 @@ def main() -> int:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def chunks_main(args) -> int:
+    """The same workload with K/V read in place from the owner chunks, trimmed to the keys the left window
+    reaches (no concatenated neighbourhood): one step = segment build over the trimmed neighbourhood,
+    nb_attn_fwd_chunks, nb_attn_bwd_chunks (which also writes whole chunk-gradient buffers and the
+    per-chunk attended flags).  Same useful FLOPs as the concatenated step."""
+    import numpy as np
+    import torch
+
+    from sliding_window_attention_fold_amd import _lib
+    from sliding_window_attention_fold_amd import api
+    from sliding_window_attention_fold_amd import workloads as wl
+
+    lib = _lib.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = wl.get(args.config)
+    if w.mode != "ring":
+        print("--kv chunks needs a ring workload", file=sys.stderr)
+        return 2
+    dm = wl.make_doc_map(w)
+    q, k, v, do = wl.make_tensors(w, dm.S, "bf16")
+    B, Hq, Hkv, L, S, D, W = w.B, w.Hq, w.Hkv, w.L, dm.S, w.D, w.window
+    scale = D ** -0.5
+    C = len(dm.owner_off) - 1
+    kd, vd = k.to(dev), v.to(dev)
+    k_chunks = [kd[:, :, dm.owner_off[c]:dm.owner_off[c + 1]].contiguous() for c in range(C)]
+    v_chunks = [vd[:, :, dm.owner_off[c]:dm.owner_off[c + 1]].contiguous() for c in range(C)]
+    del kd, vd
+    chunks = api.ring_window_chunks(k_chunks, v_chunks, W)
+    n = len(chunks)
+    S2 = sum(c.length for c in chunks)
+    nb0 = S - S2
+    ids_d = torch.from_numpy(np.ascontiguousarray(dm.doc_ids[:, nb0:])).to(dev)
+    pad_d = None if dm.pad_mask is None else torch.from_numpy(np.ascontiguousarray(dm.pad_mask[:, nb0:])).to(dev)
+    qd, dod = q.to(dev).contiguous(), do.to(dev).contiguous()
+    folded = torch.empty((B, S2), dtype=torch.int32, device=dev)
+    nseg = lib.nb_segment_buffer_elems(B, L, S2)
+    segbuf = torch.empty((nseg,), dtype=torch.int32, device=dev)
+    out, resid = torch.empty_like(qd), torch.empty_like(qd)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+    dq = torch.empty_like(qd)
+    dks = [torch.empty_like(c.k) for c in chunks]
+    dvs = [torch.empty_like(c.v) for c in chunks]
+    att = torch.empty((n,), dtype=torch.uint8, device=dev)
+    ws_bytes = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S2, D, _lib_bf16())
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    Pn, In = ctypes.c_void_p * n, ctypes.c_int32 * n
+    kp, vp = Pn(*[c.k.data_ptr() for c in chunks]), Pn(*[c.v.data_ptr() for c in chunks])
+    dkp, dvp = Pn(*[t.data_ptr() for t in dks]), Pn(*[t.data_ptr() for t in dvs])
+    ln, st, rw = In(*[c.length for c in chunks]), In(*[c.start for c in chunks]), In(*[c.k.shape[2] for c in chunks])
+    cv = lambda a: ctypes.cast(a, ctypes.c_void_p)  # noqa: E731
+    Pp = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    bf = _lib_bf16()
+    calls = {
+        "segment_build": lambda: lib.nb_segment_build(Pp(ids_d), Pp(pad_d), B, S2, L, W, Pp(folded), Pp(segbuf),
+                                                      nseg, sp),
+        "attn_fwd_chunks": lambda: lib.nb_attn_fwd_chunks(Pp(qd), cv(kp), cv(vp), cv(ln), cv(st), cv(rw), n,
+                                                          Pp(out), Pp(resid), Pp(lse), Pp(segbuf), B, Hq, Hkv, L, S2,
+                                                          D, scale, W, 0.0, bf, None, 0, sp),
+        "attn_bwd_chunks": lambda: lib.nb_attn_bwd_chunks(Pp(dod), Pp(qd), cv(kp), cv(vp), cv(ln), cv(st), cv(rw), n,
+                                                          Pp(out), Pp(resid), Pp(lse), Pp(segbuf), Pp(folded), B, Hq,
+                                                          Hkv, L, S2, D, scale, W, bf, Pp(dq), cv(dkp), cv(dvp),
+                                                          Pp(att), Pp(ws), ws_bytes, sp),
+    }
+    names = list(calls)
+
+    def step(events=None):
+        for i, nm in enumerate(names):
+            if events is not None:
+                events[i].record(stream)
+            r = calls[nm]()
+            if r != 0:
+                raise _lib.NbError(r, nm)
+        if events is not None:
+            events[len(names)].record(stream)
+
+    step()
+    torch.cuda.synchronize()
+    off_klo = lib.nb_segment_offset_row_klo(B, L)
+    klo = segbuf[off_klo:off_klo + B * L].view(B, L).long()
+    pos = (S2 - L + torch.arange(L, device=dev)).view(1, L)
+    band_lo = klo if W < 0 else torch.maximum(klo, pos - W)
+    pairs = int(torch.clamp(pos - band_lo + 1, min=0).sum().item())
+    useful = 14.0 * D * Hq * pairs
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for s_ in range(args.steps):
+        step(evs[s_])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    per = {nm: float(np.mean([evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps)]))
+           for i, nm in enumerate(names)}
+    tflops = useful / (ms_step * 1e-3) / 1e12
+    # For comparison only (outside the step): the copy the concatenated path needs first, K and V of every
+    # causally valid chunk concatenated into one neighbourhood buffer (torch.cat, as the page's helper does).
+    k_nb = torch.empty((B, Hkv, S, D), dtype=qd.dtype, device=dev)
+    v_nb = torch.empty_like(k_nb)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cat(k_chunks, dim=2, out=k_nb)
+    c0.record(stream)
+    for _ in range(args.steps):
+        torch.cat(k_chunks, dim=2, out=k_nb)
+        torch.cat(v_chunks, dim=2, out=v_nb)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / args.steps
+    rec = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "concat_copy_avoided_ms": round(copy_ms, 5),
+        "config": {"workload": f"config{args.config}: {w.name}, K/V read in place from window-trimmed chunks",
+                   "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "L": L, "S_concatenated": S, "S_trimmed": S2,
+                   "chunks": [[c.start, c.length, int(c.k.shape[2])] for c in chunks], "window": W,
+                   "pairs_per_head": pairs, "useful_flop_per_step": useful},
+        "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "ms_per_call": {nm: round(per[nm], 5) for nm in names},
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def _lib_bf16() -> int:
+    from sliding_window_attention_fold_amd import _lib
+    return _lib.NB_BF16
 
 
 def exchange_main(args) -> int:

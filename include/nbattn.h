@@ -216,6 +216,46 @@ int nb_attn_bwd_dkdv(const void* dout, const void* q, const void* k, const void*
 int nb_owner_attended(const int32_t* seg_buf, const int32_t* folded_ids, int B, int L, int S,
                       const int32_t* owner_off, int n_owner, uint8_t* owner_attended, void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * Zero-copy neighbourhood: K/V straight from the owners' chunk buffers.
+ *
+ * cp_local_ring page, module docstring and _concat_neighborhood: the
+ * neighbourhood is the causally valid chunks concatenated in ascending owner
+ * order, and with a left window only the keys the window reaches matter.
+ * These entry points take the chunks as a table instead of a concatenated copy:
+ * neighbourhood keys [off_c, off_c + chunk_len[c]) (off_c = sum of the earlier
+ * lengths, S = the total) are rows chunk_start[c] .. of chunk c's buffers
+ * K, V [B, Hkv, chunk_rows[c], D] (HOST arrays of n_chunk device pointers and
+ * sizes, 1 <= n_chunk <= 16, chunk_len >= 1, chunk_start + chunk_len <=
+ * chunk_rows).  So a windowed ring rank passes the last W' rows of the previous
+ * chunk(s) and its own chunk, and nothing is copied.  seg_buf comes from
+ * nb_segment_build over the same neighbourhood's doc ids [B, S].  Chunk
+ * buffers are 16-byte aligned.  Results are bit-identical to nb_attn_fwd /
+ * nb_attn_bwd on the concatenated neighbourhood (the same key tiles in the same
+ * order).  Errors: NB_ERR_INVALID_ARG for a table outside the bounds above,
+ * lengths not summing to S, or a null or misaligned chunk pointer; otherwise as
+ * nb_attn_fwd / nb_attn_bwd.
+ */
+int nb_attn_fwd_chunks(const void* q, const void* const* k_chunk, const void* const* v_chunk,
+                       const int32_t* chunk_len, const int32_t* chunk_start, const int32_t* chunk_rows,
+                       int n_chunk, void* o, void* o_resid, float* lse, const int32_t* seg_buf, int B, int Hq,
+                       int Hkv, int L, int S, int D, float scale, int window_left, float dropout_p, int dtype,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* The backward with the chunk table: dk_chunk[c], dv_chunk[c] (host arrays of
+ * device pointers) are whole chunk-gradient buffers [B, Hkv, chunk_rows[c], D],
+ * fully written -- the gradients of the chunk's neighbourhood keys (0 where no
+ * query attends) and 0 on its rows outside [chunk_start, chunk_start +
+ * chunk_len).  chunk_attended (device [n_chunk], or NULL) receives the
+ * nb_owner_attended flags with the chunks as owners (folded_ids then required).
+ * Workspace as for nb_attn_bwd. */
+int nb_attn_bwd_chunks(const void* dout, const void* q, const void* const* k_chunk, const void* const* v_chunk,
+                       const int32_t* chunk_len, const int32_t* chunk_start, const int32_t* chunk_rows,
+                       int n_chunk, const void* o, const void* o_resid, const float* lse, const int32_t* seg_buf,
+                       const int32_t* folded_ids, int B, int Hq, int Hkv, int L, int S, int D, float scale,
+                       int window_left, int dtype, void* dq, void* const* dk_chunk, void* const* dv_chunk,
+                       uint8_t* chunk_attended, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,6 +42,10 @@ SIGNATURES = {
     "nb_attn_bwd_prep": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _Z, _P]),
     "nb_attn_bwd_main": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P, _Z, _P]),
     "nb_owner_attended": (_I, [_P, _P, _I, _I, _I, _P, _I, _P, _P]),
+    "nb_attn_fwd_chunks": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _F,
+                                _I, _P, _Z, _P]),
+    "nb_attn_bwd_chunks": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F,
+                                _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
     # include/nbexchange.h
     "nb_exchange_plan_elems": (_Z, [_I]),
     "nb_exchange_plan": (_I, [_P, _P, _I, _I, _I, _P, _Z, _P]),

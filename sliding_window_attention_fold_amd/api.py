@@ -21,7 +21,8 @@ import torch
 from . import _lib
 
 __all__ = ["Segments", "OwnerTable", "Saved", "BwdResult", "segment_build", "attn_fwd", "attn_bwd",
-           "NeighbourhoodAttention", "neighbourhood_attention"]
+           "NeighbourhoodAttention", "neighbourhood_attention", "KvChunk", "ChunkSaved", "attn_fwd_chunks",
+           "attn_bwd_chunks", "ring_window_chunks"]
 
 _DTYPES = {torch.bfloat16: _lib.NB_BF16, torch.float32: _lib.NB_F32}
 
@@ -252,3 +253,108 @@ class NeighbourhoodAttention(torch.autograd.Function):
 
 def neighbourhood_attention(q, k, v, seg: Segments, scale: Optional[float] = None):
     return NeighbourhoodAttention.apply(q, k, v, seg, scale)
+
+
+# ------------------------------------------------------------------ zero-copy neighbourhood
+@dataclass
+class KvChunk:
+    """One owner chunk of the neighbourhood, used in place: keys are rows
+    ``[start, start + length)`` of ``k`` / ``v`` ``[B, Hkv, rows, D]``."""
+
+    k: torch.Tensor
+    v: torch.Tensor
+    start: int
+    length: int
+
+
+class ChunkSaved(NamedTuple):
+    q: torch.Tensor
+    chunks: List[KvChunk]
+    out: torch.Tensor
+    out_resid: Optional[torch.Tensor]
+    lse: torch.Tensor
+    seg: Segments
+    scale: float
+
+
+def ring_window_chunks(k_chunks: List[torch.Tensor], v_chunks: List[torch.Tensor], window: int) -> List[KvChunk]:
+    """The windowed ring neighbourhood without a copy: of the causally valid chunks
+    ``0..cp_rank`` (each ``[B, Hkv, L, D]``, the last one the rank's own), keep the
+    own chunk and the last ``window`` keys before it -- the only keys a left window
+    of ``window`` reaches from the shard (cp_local_ring page, module docstring)."""
+    _need(len(k_chunks) == len(v_chunks) and k_chunks, "one K and one V buffer per chunk")
+    L = k_chunks[-1].shape[2]
+    need = L * (len(k_chunks) - 1) if window is None or window < 0 else min(int(window), L * (len(k_chunks) - 1))
+    out: List[KvChunk] = []
+    left = need
+    for kc, vc in zip(reversed(k_chunks[:-1]), reversed(v_chunks[:-1])):
+        if left <= 0:
+            break
+        n = min(left, kc.shape[2])
+        out.append(KvChunk(kc, vc, kc.shape[2] - n, n))
+        left -= n
+    out.reverse()
+    out.append(KvChunk(k_chunks[-1], v_chunks[-1], 0, L))
+    return out
+
+
+def _chunk_args(chunks: List[KvChunk], q: torch.Tensor, seg: Segments):
+    _need(1 <= len(chunks) <= 16, "1 to 16 chunks")
+    B, Hq, L, D = q.shape
+    for c in chunks:
+        _need(c.k.is_cuda and c.k.is_contiguous() and c.v.is_contiguous() and c.k.shape == c.v.shape
+              and c.k.dtype == q.dtype and c.v.dtype == q.dtype and c.k.dim() == 4, "chunk buffers [B, Hkv, rows, D]")
+        _need(c.k.shape[0] == B and c.k.shape[3] == D and c.k.shape[1] == chunks[0].k.shape[1], "chunk shapes")
+        _need(0 <= c.start and c.length >= 1 and c.start + c.length <= c.k.shape[2], "chunk row range")
+    S = sum(c.length for c in chunks)
+    _need(S == seg.S and L == seg.L and B == seg.B, "the chunks must cover the segments' neighbourhood")
+    n = len(chunks)
+    P = ctypes.c_void_p * n
+    I = ctypes.c_int32 * n
+    return (B, Hq, chunks[0].k.shape[1], L, S, D, n,
+            P(*[c.k.data_ptr() for c in chunks]), P(*[c.v.data_ptr() for c in chunks]),
+            I(*[c.length for c in chunks]), I(*[c.start for c in chunks]), I(*[c.k.shape[2] for c in chunks]))
+
+
+def attn_fwd_chunks(q: torch.Tensor, chunks: List[KvChunk], seg: Segments, scale: Optional[float] = None):
+    """Forward reading K/V in place from the chunk buffers; returns ``(out, saved)``."""
+    lib = _lib.load()
+    _need(q.is_cuda and q.is_contiguous() and q.dtype in _DTYPES and q.dim() == 4, "q [B,Hq,L,D] on the device")
+    B, Hq, Hkv, L, S, D, n, kp, vp, ln, st, rw = _chunk_args(chunks, q, seg)
+    scale = D ** -0.5 if scale is None else float(scale)
+    out = torch.empty_like(q)
+    resid = torch.empty_like(q) if q.dtype == torch.bfloat16 else None
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    _lib.check(lib.nb_attn_fwd_chunks(_ptr(q), ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp, ctypes.c_void_p),
+                                      ctypes.cast(ln, ctypes.c_void_p), ctypes.cast(st, ctypes.c_void_p),
+                                      ctypes.cast(rw, ctypes.c_void_p), n, _ptr(out), _ptr(resid), _ptr(lse),
+                                      _ptr(seg.buf), B, Hq, Hkv, L, S, D, scale, seg.window, 0.0, _DTYPES[q.dtype],
+                                      None, 0, _stream_ptr(q.device)), "nb_attn_fwd_chunks")
+    return out, ChunkSaved(q, list(chunks), out, resid, lse, seg, scale)
+
+
+def attn_bwd_chunks(saved: ChunkSaved, grad_out: torch.Tensor):
+    """Backward writing whole chunk-gradient buffers (zeros outside the used rows
+    and for keys no query attends); returns ``(dq, [dk_c], [dv_c], [attended_c])``."""
+    lib = _lib.load()
+    q, chunks, out, resid, lse, seg, scale = saved
+    _need(grad_out.shape == q.shape and grad_out.dtype == q.dtype and grad_out.is_contiguous(),
+          "grad_out must match q")
+    B, Hq, Hkv, L, S, D, n, kp, vp, ln, st, rw = _chunk_args(chunks, q, seg)
+    dq = torch.empty_like(q)
+    dks = [torch.empty_like(c.k) for c in chunks]
+    dvs = [torch.empty_like(c.v) for c in chunks]
+    att = torch.empty((n,), dtype=torch.uint8, device=q.device)
+    ws_bytes = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, _DTYPES[q.dtype])
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=q.device)
+    P = ctypes.c_void_p * n
+    dkp, dvp = P(*[t.data_ptr() for t in dks]), P(*[t.data_ptr() for t in dvs])
+    _lib.check(lib.nb_attn_bwd_chunks(_ptr(grad_out), _ptr(q), ctypes.cast(kp, ctypes.c_void_p),
+                                      ctypes.cast(vp, ctypes.c_void_p), ctypes.cast(ln, ctypes.c_void_p),
+                                      ctypes.cast(st, ctypes.c_void_p), ctypes.cast(rw, ctypes.c_void_p), n,
+                                      _ptr(out), _ptr(resid), _ptr(lse), _ptr(seg.buf), _ptr(seg.folded), B, Hq, Hkv,
+                                      L, S, D, scale, seg.window, _DTYPES[q.dtype], _ptr(dq),
+                                      ctypes.cast(dkp, ctypes.c_void_p), ctypes.cast(dvp, ctypes.c_void_p), _ptr(att),
+                                      _ptr(ws), ws_bytes, _stream_ptr(q.device)), "nb_attn_bwd_chunks")
+    return dq, dks, dvs, [bool(x) for x in att.tolist()]
+

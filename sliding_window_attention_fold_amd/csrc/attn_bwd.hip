@@ -31,6 +31,7 @@
 
 #include "nb_device.h"
 #include "nb_kernels.h"
+#include "nb_kv.h"
 
 namespace nb {
 
@@ -115,7 +116,7 @@ using DkvSmem = typename std::conditional<DkvCfg<T, D>::SKEW, DkvSmemMetaFirst<T
 // One dK/dV item f: (kv head, batch row, key tile) with the kv head fastest
 // and the (batch row, key tile) pairs in the order of decreasing work
 // (work_order_kernel), so the long tiles start first.
-template <typename T, int D>
+template <typename T, int D, bool CH>
 __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm, int f) {
   typedef DkvCfg<T, D> C;
   typedef Tile<T, C::BQ, D> TL;
@@ -168,13 +169,23 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   if (n_iter == 0) {
     // no query reaches these keys: dK = dV = 0 over the whole tile (16-byte stores)
     constexpr int V16 = 16 / (int)sizeof(T);
-    const int n16 = (min(C::BK, p.S - j0) * D) / V16;
-    const size_t base = (((size_t)b * p.Hkv + kvh) * p.S + j0) * D;
-    uint4* dkp = reinterpret_cast<uint4*>(reinterpret_cast<T*>(p.dk) + base);
-    uint4* dvp = reinterpret_cast<uint4*>(reinterpret_cast<T*>(p.dv) + base);
-    for (int x = tid; x < n16; x += C::NT) {
-      dkp[x] = uint4{0u, 0u, 0u, 0u};
-      dvp[x] = uint4{0u, 0u, 0u, 0u};
+    constexpr int RV = D / V16;   // 16-byte vectors per row
+    const int bh = b * p.Hkv + kvh;
+    const int n16 = min(C::BK, p.S - j0) * RV;
+    if constexpr (CH) {
+      for (int x = tid; x < n16; x += C::NT) {
+        const int j = j0 + x / RV, c = x % RV;
+        reinterpret_cast<uint4*>(kv_row<T>(p.kv, kDK, bh, j, D))[c] = uint4{0u, 0u, 0u, 0u};
+        reinterpret_cast<uint4*>(kv_row<T>(p.kv, kDV, bh, j, D))[c] = uint4{0u, 0u, 0u, 0u};
+      }
+    } else {
+      const size_t base = ((size_t)bh * p.S + j0) * D;
+      uint4* dkp = reinterpret_cast<uint4*>(reinterpret_cast<T*>(p.kv.dk[0]) + base);
+      uint4* dvp = reinterpret_cast<uint4*>(reinterpret_cast<T*>(p.kv.dv[0]) + base);
+      for (int x = tid; x < n16; x += C::NT) {
+        dkp[x] = uint4{0u, 0u, 0u, 0u};
+        dvp[x] = uint4{0u, 0u, 0u, 0u};
+      }
     }
     return;
   }
@@ -212,8 +223,13 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   // or dP = dO V^T
   F kv[D / 16];
   {
-    const size_t kr = ((size_t)b * p.Hkv + kvh) * p.S + min(j, p.S - 1);
-    const T* src = reinterpret_cast<const T*>(role_a ? p.k : p.v) + kr * D;
+    const T* src;
+    if constexpr (CH) {
+      src = kv_row<T>(p.kv, role_a ? kK : kV, b * p.Hkv + kvh, min(j, p.S - 1), D);
+    } else {
+      const size_t kr = ((size_t)b * p.Hkv + kvh) * p.S + min(j, p.S - 1);
+      src = reinterpret_cast<const T*>(role_a ? p.kv.k[0] : p.kv.v[0]) + kr * D;
+    }
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) kv[kk] = load_frag<T>(src + 16 * kk + 8 * g);
   }
@@ -425,7 +441,11 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   }
 
   if (j < p.S) {
-    T* dst = reinterpret_cast<T*>(role_a ? p.dv : p.dk) + (((size_t)b * p.Hkv + kvh) * p.S + j) * D;
+    T* dst;
+    if constexpr (CH)
+      dst = kv_row<T>(p.kv, role_a ? kDV : kDK, b * p.Hkv + kvh, j, D);
+    else
+      dst = reinterpret_cast<T*>(role_a ? p.kv.dv[0] : p.kv.dk[0]) + (((size_t)b * p.Hkv + kvh) * p.S + j) * D;
     const float sc = role_a ? 1.f : p.scale;
 #pragma unroll
     for (int d = 0; d < D / 32; ++d) {
@@ -479,7 +499,10 @@ struct DqSmem {
 
 // One dQ item f: (kv head, q head of its group, batch row, query tile) with
 // the kv head fastest and the (batch row, query tile) pairs longest band first.
-template <typename T, int D>
+// KV as in the forward (kKvConcat / kKvPair / kKvAny); under kKvPair an item
+// whose key range touches three or more chunks is appended to p.cross and left
+// to the follow-up kernel, which runs it as kKvAny.
+template <typename T, int D, int KV>
 __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, int f) {
   typedef DqCfg<T, D> C;
   typedef Tile<T, C::BN, D> TL;
@@ -539,15 +562,32 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
   int kstart = INT_MAX, kend = INT_MIN;
 #pragma unroll
   for (int x = 0; x < C::NW; ++x) { kstart = min(kstart, red[x][0]); kend = max(kend, red[x][1]); }
+  kstart = __builtin_amdgcn_readfirstlane(kstart);   // uniform: scalar tile bounds and addresses
+  kend = __builtin_amdgcn_readfirstlane(kend);
 
-  const T* __restrict__ kbase = reinterpret_cast<const T*>(p.k) + ((size_t)b * p.Hkv + kvh) * p.S * D;
-  const T* __restrict__ vbase = reinterpret_cast<const T*>(p.v) + ((size_t)b * p.Hkv + kvh) * p.S * D;
+  const int bh = b * p.Hkv + kvh;
+  // kbase + j * D is key j's row (the concatenated buffer; chunks: see the forward)
+  const T* __restrict__ kbase = reinterpret_cast<const T*>(p.kv.k[0]) + (size_t)bh * p.S * D;
+  const T* __restrict__ vbase = reinterpret_cast<const T*>(p.kv.v[0]) + (size_t)bh * p.S * D;
+  const KvPair<T, C::BN> pair = KV == kKvConcat ? KvPair<T, C::BN>() : KvPair<T, C::BN>(p.kv, bh, kstart, kend, D);
+  if constexpr (KV == kKvPair) {
+    if (!pair.ok) {   // uniform
+      if (threadIdx.x == 0) p.cross[atomicAdd(&p.counters[kCrossCount], 1)] = f;
+      return;
+    }
+  }
   const int nt = kstart < kend ? (kend - kstart + C::BN - 1) / C::BN : 0;   // key tiles of the item
   auto load = [&](int slot, int n) {
     const int j0 = kstart + n * C::BN;
-    const int nv = min(C::BN, p.S - j0);
-    dma.issue(sm.K[slot], kbase + (size_t)j0 * D, nv);
-    dma.issue(sm.V[slot], vbase + (size_t)j0 * D, nv);
+    if constexpr (KV == kKvAny) {
+      kv_tile_load<T, C::BN, D, C::NW>(dma, p.kv, bh, j0, min(C::BN, p.S - j0), sm.K[slot], sm.V[slot]);
+    } else if constexpr (KV == kKvPair) {
+      pair.load(dma, j0, sm.K[slot], sm.V[slot]);
+    } else {
+      const int nv = min(C::BN, p.S - j0);
+      dma.issue(sm.K[slot], kbase + (size_t)j0 * D, nv);
+      dma.issue(sm.V[slot], vbase + (size_t)j0 * D, nv);
+    }
   };
 #pragma unroll
   for (int x = 0; x < NS - 1; ++x)
@@ -767,7 +807,7 @@ template <int BK, int BQ, int BM>
 __device__ void work_order(const BwdParams& p, int modes, unsigned long long* keys, int* bst) {
   const int tid = threadIdx.x;
   const int off = p.S - p.L;
-  if (tid < kNumQueues) p.counters[tid] = 0;  // the backward kernel's work queues start empty
+  if (tid < kNumCounters) p.counters[tid] = 0;  // work queues and the deferred-item list start empty
   if (modes & 1) {
     const int n_kt = (p.S + BK - 1) / BK;
     const int n = p.B * n_kt;
@@ -845,6 +885,7 @@ __global__ __launch_bounds__(kPrepNT) void bwd_prep_kernel(BwdParams p, int mode
 
 size_t dkdv_order_elems(int B, int S) { return (size_t)B * ((S + 31) / 32); }
 size_t dq_order_elems(int B, int L) { return (size_t)B * ((L + 31) / 32); }
+size_t dq_cross_elems(int B, int Hq, int L) { return (size_t)B * Hq * ((L + 31) / 32); }
 
 // ---------------------------------------------------------------- backward kernel
 
@@ -857,7 +898,7 @@ size_t dq_order_elems(int B, int L) { return (size_t)B * ((L + 31) / 32); }
 // XCD, whose L2 then holds the K/V and Q/dO rows its items share.  Running
 // both passes in one grid lets the shorter dQ items fill the tail of the dK/dV
 // items.  Which workgroup computes an item never changes the result.
-template <typename T, int D, int MODE>
+template <typename T, int D, int MODE, int KV>
 __global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void bwd_kernel(BwdParams p) {
   static_assert(DkvCfg<T, D>::NT == BwdShape<T, D>::NT && DqCfg<T, D>::NT == BwdShape<T, D>::NT,
                 "one block shape for both passes");
@@ -865,7 +906,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void b
     DkvSmem<T, D> kv;
     DqSmem<T, D> q;
   } sm;
-  auto dkdv = [&](int f) { dkdv_item<T, D>(p, sm.kv, f); };
+  auto dkdv = [&](int f) { dkdv_item<T, D, KV != kKvConcat>(p, sm.kv, f); };
   const int n_kv = (MODE & 1) ? p.B * ((p.S + DkvCfg<T, D>::BK - 1) / DkvCfg<T, D>::BK) * p.Hkv : 0;
   const int n_q = (MODE & 2) ? p.B * ((p.L + DqCfg<T, D>::BM - 1) / DqCfg<T, D>::BM) * p.Hq : 0;
   const int total = n_kv + n_q;
@@ -881,12 +922,32 @@ __global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void b
     if constexpr (MODE == 1) {
       dkdv(f);
     } else if constexpr (MODE == 2) {
-      dq_item<T, D>(p, sm.q, f);
+      dq_item<T, D, KV>(p, sm.q, f);
     } else {
       if (f < n_kv) dkdv(f);
-      else dq_item<T, D>(p, sm.q, f - n_kv);
+      else dq_item<T, D, KV>(p, sm.q, f - n_kv);
     }
     __syncthreads();  // this item's LDS is dead before the next fetch
+  }
+}
+
+// The dQ items the chunk-table backward deferred (their key ranges touch three
+// or more chunks), taken from p.cross in the order they were appended.
+template <typename T, int D>
+__global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void bwd_dq_cross_kernel(BwdParams p) {
+  __shared__ DqSmem<T, D> sm;
+  int* const slot = reinterpret_cast<int*>(&sm);  // the fetched item, between items only
+  for (;;) {
+    if (threadIdx.x == 0) {
+      const int x = atomicAdd(&p.counters[kCrossNext], 1);
+      *slot = x < p.counters[kCrossCount] ? p.cross[x] : -1;
+    }
+    __syncthreads();
+    const int f = *slot;
+    __syncthreads();
+    if (f < 0) break;
+    dq_item<T, D, kKvAny>(p, sm, f);
+    __syncthreads();
   }
 }
 
@@ -917,7 +978,20 @@ static hipError_t launch_main_t(const BwdParams& p, hipStream_t s) {
   const long long n_kv = (MODE & 1) ? (long long)p.B * ((p.S + DkvCfg<T, D>::BK - 1) / DkvCfg<T, D>::BK) * p.Hkv : 0;
   const long long n_q = (MODE & 2) ? (long long)p.B * ((p.L + DqCfg<T, D>::BM - 1) / DqCfg<T, D>::BM) * p.Hq : 0;
   dim3 grid((unsigned)std::min<long long>(n_kv + n_q, (long long)device_cu_count() * BwdShape<T, D>::OCC));
-  hipLaunchKernelGGL((bwd_kernel<T, D, MODE>), grid, dim3(BwdShape<T, D>::NT), 0, s, p);
+  // the chunk-table variants exist for the full backward only (the split
+  // passes take the concatenated neighbourhood)
+  const bool concat = p.kv.n == 1 && p.kv.start[0] == 0 && p.kv.rows[0] == p.S;
+  if constexpr (MODE == 3) {
+    if (!concat) {
+      hipLaunchKernelGGL((bwd_kernel<T, D, MODE, kKvPair>), grid, dim3(BwdShape<T, D>::NT), 0, s, p);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess || !kv_may_need_general(p.kv, p.window, DqCfg<T, D>::BM, DqCfg<T, D>::BN)) return e;
+      dim3 grid2((unsigned)std::min<long long>(n_q, (long long)device_cu_count() * BwdShape<T, D>::OCC));
+      hipLaunchKernelGGL((bwd_dq_cross_kernel<T, D>), grid2, dim3(BwdShape<T, D>::NT), 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((bwd_kernel<T, D, MODE, kKvConcat>), grid, dim3(BwdShape<T, D>::NT), 0, s, p);
   return hipGetLastError();
 }
 
@@ -969,6 +1043,40 @@ __global__ __launch_bounds__(256) void owner_flags_kernel(OwnerParams p) {
     found = __syncthreads_or(found);
   }
   if (threadIdx.x == 0) p.attended[o] = found ? 1 : 0;
+}
+
+// dK/dV rows of chunk buffers outside the neighbourhood ([0, start) and
+// [start + len, rows) of every (batch, kv head)): exact zeros, as for keys no
+// query attends.
+__global__ __launch_bounds__(256) void kv_zero_outside_kernel(KvChunks c, int BH, int row_vecs) {
+  const int x = blockIdx.y;
+  const int len = c.off[x + 1] - c.off[x];
+  const int rows = c.rows[x], st = c.start[x];
+  const int outside = rows - len;
+  if (outside <= 0) return;
+  const size_t n = (size_t)BH * outside * row_vecs;
+  uint4* dk = reinterpret_cast<uint4*>(c.dk[x]);
+  uint4* dv = reinterpret_cast<uint4*>(c.dv[x]);
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const size_t vec = i % row_vecs, rr = i / row_vecs;
+    const int bh = (int)(rr / outside);
+    int r = (int)(rr % outside);
+    if (r >= st) r += len;
+    const size_t o = ((size_t)bh * rows + r) * row_vecs + vec;
+    dk[o] = uint4{0u, 0u, 0u, 0u};
+    dv[o] = uint4{0u, 0u, 0u, 0u};
+  }
+}
+
+hipError_t launch_kv_zero_outside(const KvChunks& c, int BH, int row_bytes, hipStream_t s) {
+  int64_t most = 0;
+  for (int x = 0; x < c.n; ++x) most = std::max<int64_t>(most, (int64_t)c.rows[x] - (c.off[x + 1] - c.off[x]));
+  if (most == 0) return hipSuccess;
+  const int row_vecs = row_bytes / 16;
+  const int64_t need = ((int64_t)BH * most * row_vecs + 255) / 256;
+  dim3 grid((unsigned)std::min<int64_t>(need, 1024), (unsigned)c.n);
+  hipLaunchKernelGGL(kv_zero_outside_kernel, grid, dim3(256), 0, s, c, BH, row_vecs);
+  return hipGetLastError();
 }
 
 hipError_t launch_owner_flags(const OwnerParams& p, hipStream_t s) {

@@ -23,6 +23,7 @@
 
 #include "nb_device.h"
 #include "nb_kernels.h"
+#include "nb_kv.h"
 
 namespace nb {
 
@@ -44,7 +45,14 @@ struct FwdCfg {
   static constexpr int AHEAD_PV = (D <= 128) ? 3 : 2;
 };
 
-template <typename T, int D>
+// KV selects how K/V rows are found: kKvConcat, one concatenated buffer
+// (p.kv.k[0] / p.kv.v[0], S rows per (batch, kv head)); kKvPair, the chunk
+// table for workgroups whose key range touches at most two chunks (the rest
+// return at once); kKvAny, the chunk table for the workgroups whose range
+// touches three or more (the rest return).  A chunk-table forward launches
+// kKvPair, then kKvAny over the same grid when the chunk lengths allow such
+// ranges, so the common loop carries none of the general lookup's registers.
+template <typename T, int D, int KV>
 __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdParams p) {
   typedef FwdCfg<T, D> C;
   typedef Tile<T, C::BN, D> TL;
@@ -90,16 +98,29 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdP
   int kstart = INT_MAX, kend = INT_MIN;
 #pragma unroll
   for (int x = 0; x < C::NW; ++x) { kstart = min(kstart, red[x][0]); kend = max(kend, red[x][1]); }
+  kstart = __builtin_amdgcn_readfirstlane(kstart);   // uniform: scalar tile bounds and addresses
+  kend = __builtin_amdgcn_readfirstlane(kend);
 
   const size_t qrow = ((size_t)b * p.Hq + h) * p.L + i;
-  const T* __restrict__ kbase = reinterpret_cast<const T*>(p.k) + ((size_t)b * p.Hkv + kvh) * p.S * D;
-  const T* __restrict__ vbase = reinterpret_cast<const T*>(p.v) + ((size_t)b * p.Hkv + kvh) * p.S * D;
-
+  const int bh = b * p.Hkv + kvh;
+  // kbase + j * D is key j's row (the concatenated buffer)
+  const T* __restrict__ kbase = reinterpret_cast<const T*>(p.kv.k[0]) + (size_t)bh * p.S * D;
+  const T* __restrict__ vbase = reinterpret_cast<const T*>(p.kv.v[0]) + (size_t)bh * p.S * D;
+  const KvPair<T, C::BN> pair = KV == kKvConcat ? KvPair<T, C::BN>() : KvPair<T, C::BN>(p.kv, bh, kstart, kend, D);
+  if constexpr (KV != kKvConcat) {
+    if (pair.ok != (KV == kKvPair)) return;   // uniform: the other launch owns it
+  }
   const TileDma<T, C::BN, D, C::NW> dma;   // K and V tiles share one layout
-  auto load = [&](T* Ks, T* Vs, int j0) {
-    const int nv = min(C::BN, p.S - j0);
-    dma.issue(Ks, kbase + (size_t)j0 * D, nv);
-    dma.issue(Vs, vbase + (size_t)j0 * D, nv);
+  auto load = [&](T* Ks, T* Vs, int j0) __attribute__((always_inline)) {
+    if constexpr (KV == kKvAny) {
+      kv_tile_load<T, C::BN, D, C::NW>(dma, p.kv, bh, j0, min(C::BN, p.S - j0), Ks, Vs);
+    } else if constexpr (KV == kKvPair) {
+      pair.load(dma, j0, Ks, Vs);
+    } else {
+      const int nv = min(C::BN, p.S - j0);
+      dma.issue(Ks, kbase + (size_t)j0 * D, nv);
+      dma.issue(Vs, vbase + (size_t)j0 * D, nv);
+    }
   };
   if (kstart < kend) load(K0, V0, kstart);
 
@@ -123,7 +144,7 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdP
   // row's sum of 2^(s - m_ref) over this lane's keys (the other half is in lane^32).
   float m_ref = -INFINITY, l_run = 0.f;
 
-  auto compute = [&](const T* Ks, const T* Vs, int j0) {
+  auto compute = [&](const T* Ks, const T* Vs, int j0) __attribute__((always_inline)) {
     if (j0 >= w_hi || j0 + C::BN <= w_lo) return;
     const bool full = w_all_real && j0 >= w_bs_max && j0 + C::BN - 1 <= w_p_min;
     f32x16 sacc[C::BN / 32];
@@ -210,11 +231,21 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdP
   if (g == 0) p.lse[qrow] = real ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
 }
 
+// The concatenated neighbourhood: one chunk of S rows starting at row 0.
+static bool kv_concatenated(const KvChunks& c, int S) { return c.n == 1 && c.start[0] == 0 && c.rows[0] == S; }
+
 template <typename T, int D>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   typedef FwdCfg<T, D> C;
   dim3 grid((unsigned)((p.L + C::BM - 1) / C::BM) * p.Hq * p.B);
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D>), grid, dim3(C::NT), 0, s, p);
+  if (kv_concatenated(p.kv, p.S)) {
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, kKvConcat>), grid, dim3(C::NT), 0, s, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, kKvPair>), grid, dim3(C::NT), 0, s, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !kv_may_need_general(p.kv, p.window, C::BM, C::BN)) return e;
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, kKvAny>), grid, dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 

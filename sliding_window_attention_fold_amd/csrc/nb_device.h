@@ -237,6 +237,51 @@ struct TileDma {
     for (int x = 0; x < PER; ++x) c += (TL::BLOCKS % NW == 0 || w + x * NW < TL::BLOCKS) ? 1 : 0;
     return c;
   }
+  // Tile rows [r_lo, r_hi) only, from src = the source row of tile row r_lo
+  // (rows at or beyond nrows repeat row nrows - 1); other lanes sit idle.  A
+  // tile whose rows come from several buffers is copied range by range.
+  __device__ __forceinline__ void issue_rows(T* lds, const T* __restrict__ src, int r_lo, int r_hi, int nrows) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int w = wave_id(), l = threadIdx.x & 63;
+    typedef __attribute__((address_space(3))) void lds_void;
+    const int span = min(r_hi, nrows) - r_lo;   // source rows read
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, span * RB, kBufferWord3);
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      const int blk = w + x * NW;
+      const int r = (blk * 64 + l) / TL::CPR;
+      if ((TL::BLOCKS % NW == 0 || blk < TL::BLOCKS) && r >= r_lo && r < r_hi) {
+        const uint32_t o = voff[x] - (uint32_t)((r_lo + r - min(r, nrows - 1)) * RB);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + blk * 64 * TL::EPC), 16, o, 0, 0, 0);
+      }
+    }
+#endif
+  }
+  // All ROWS tile rows, rows [0, n0) from srcA (the source row of tile row 0)
+  // and rows [n0, ROWS) from srcB (the source row of tile row n0), 0 < n0 < ROWS.
+  // A lane's tile row is its offset's row (offsets stay below RB past the row
+  // start), so one compare against n0 * RB picks the source.
+  __device__ __forceinline__ void issue_split(T* lds, const T* __restrict__ srcA, const T* __restrict__ srcB,
+                                              int n0) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int w = wave_id();
+    typedef __attribute__((address_space(3))) void lds_void;
+    const uint32_t cut = (uint32_t)(n0 * RB);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)srcA, (short)0, n0 * RB, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)srcB, (short)0, (ROWS - n0) * RB, kBufferWord3);
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      const int blk = w + x * NW;
+      if (TL::BLOCKS % NW == 0 || blk < TL::BLOCKS) {
+        lds_void* dst = (lds_void*)(lds + blk * 64 * TL::EPC);
+        if (voff[x] < cut) __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, voff[x], 0, 0, 0);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, voff[x] - cut, 0, 0, 0);
+      }
+    }
+#endif
+  }
   __device__ __forceinline__ void issue(T* lds, const T* __restrict__ src, int nrows) const {
     // The buffer-resource type exists only for the device target; the host
     // pass (which only needs the kernels' launch stubs) sees an empty body.

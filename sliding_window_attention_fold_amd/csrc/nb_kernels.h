@@ -26,10 +26,46 @@ struct SegParams {
   int B, S, L, window;
 };
 
+// K/V of the neighbourhood as a table of per-chunk buffers (no concatenated
+// copy): neighbourhood keys [off[c], off[c+1]) are rows start[c] .. of chunk c's
+// buffers K, V (and dK, dV) [B, Hkv, rows[c], D].  One chunk with start 0 and
+// rows S is the concatenated neighbourhood.
+constexpr int kMaxKvChunks = 16;
+// How a kernel variant finds K/V rows (template argument): one concatenated
+// buffer; the chunk table for work whose key range touches at most two chunks
+// (scalar bases, see KvPair); the chunk table for any key range (a lookup per
+// tile, for the rare ranges over three or more chunks).
+constexpr int kKvConcat = 0, kKvPair = 1, kKvAny = 2;
+struct KvChunks {
+  int n;
+  int off[kMaxKvChunks + 1];
+  int start[kMaxKvChunks];
+  int rows[kMaxKvChunks];
+  const void* k[kMaxKvChunks];
+  const void* v[kMaxKvChunks];
+  void* dk[kMaxKvChunks];
+  void* dv[kMaxKvChunks];
+};
+
+// Chunk of neighbourhood key j (0 <= j < S) and the index of its row (batch b,
+// kv head: bh = b * Hkv + h) in that chunk's buffers, counted in rows.  One pass over
+// the chunks with uniform indices, so per-lane keys need no indexed loads.
+__device__ __forceinline__ int kv_locate(const KvChunks& c, int bh, int j, size_t* row) {
+  int x = 0;
+  size_t r = (size_t)bh * c.rows[0] + c.start[0] + j;
+  for (int y = 1; y < c.n; ++y) {
+    if (j >= c.off[y]) {
+      x = y;
+      r = (size_t)bh * c.rows[y] + c.start[y] + (j - c.off[y]);
+    }
+  }
+  *row = r;
+  return x;
+}
+
 struct FwdParams {
   const void* q;
-  const void* k;
-  const void* v;
+  KvChunks kv;
   void* o;
   void* o_lo;        // optional: rounding residual of o (fp32 value minus stored value)
   float* lse;
@@ -40,20 +76,18 @@ struct FwdParams {
 
 struct BwdParams {
   const void* q;
-  const void* k;
-  const void* v;
+  KvChunks kv;       // K, V read and dK, dV written through the chunk table
   const void* o;
   const void* o_lo;  // optional residual saved by the forward
   const void* dout;
   const float* lse;
   float* delta;
   int* order;        // workspace: dK/dV key tiles (b * n_tiles + tile) by decreasing work
-  int* counters;     // workspace: kNumQueues work-queue counters of the backward kernel
+  int* counters;     // workspace: kNumCounters counters (work queues, deferred dQ items)
   int* qorder;       // workspace: dQ query tiles (b * n_tiles + tile) by decreasing work
+  int* cross;        // workspace: dQ items deferred by the chunk-table backward
   const int32_t* row_klo;
   void* dq;
-  void* dk;
-  void* dv;
   int B, Hq, Hkv, L, S, window;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
@@ -75,11 +109,17 @@ hipError_t launch_attn_fwd(const FwdParams& p, int D, bool f32, hipStream_t s);
 // dK/dV pass (after kBwdPrep or kBwdDq on the same workspace).
 enum { kBwdPrep = 0, kBwdMain = 1, kBwdDq = 2, kBwdDkdv = 3 };
 hipError_t launch_bwd(const BwdParams& p, int D, bool f32, int what, hipStream_t s);
-// Elements of the dK/dV and dQ work-order arrays (enough for tiles of >= 32);
-// the workspace also holds kNumQueues queue counters.
+// Zeros the dK/dV rows of the chunk buffers that lie outside the neighbourhood.
+hipError_t launch_kv_zero_outside(const KvChunks& c, int BH, int row_bytes, hipStream_t s);
+// Elements of the dK/dV and dQ work-order arrays and of the deferred dQ item
+// list (enough for tiles of >= 32); the workspace also holds kNumCounters
+// counters: the kNumQueues work queues of the backward kernel, then the length
+// of the deferred list and the follow-up kernel's position in it.
 size_t dkdv_order_elems(int B, int S);
 size_t dq_order_elems(int B, int L);
+size_t dq_cross_elems(int B, int Hq, int L);
 constexpr int kNumQueues = 8;
+constexpr int kCrossCount = kNumQueues, kCrossNext = kNumQueues + 1, kNumCounters = kNumQueues + 2;
 hipError_t launch_owner_flags(const OwnerParams& p, hipStream_t s);
 
 }  // namespace nb

@@ -49,6 +49,53 @@ int attn_common_checks(const void* const* ptrs, int nptrs, int B, int Hq, int Hk
   return NB_OK;
 }
 
+// The concatenated neighbourhood as a one-chunk table.
+nb::KvChunks one_chunk(int S, const void* k, const void* v, void* dk, void* dv) {
+  nb::KvChunks c;
+  std::memset(&c, 0, sizeof(c));
+  c.n = 1;
+  c.off[0] = 0;
+  c.off[1] = S;
+  c.start[0] = 0;
+  c.rows[0] = S;
+  c.k[0] = k;
+  c.v[0] = v;
+  c.dk[0] = dk;
+  c.dv[0] = dv;
+  return c;
+}
+
+// A caller's chunk table: n chunks of len[c] keys starting at row start[c] of
+// buffers with rows[c] rows per (batch, kv head); S = sum of len.
+int chunk_table(const void* const* k, const void* const* v, void* const* dk, void* const* dv, const int32_t* len,
+                const int32_t* start, const int32_t* rows, int n, int B, int Hkv, int S, nb::KvChunks* out) {
+  if (n < 1 || n > nb::kMaxKvChunks || len == nullptr || start == nullptr || rows == nullptr) return NB_ERR_INVALID_ARG;
+  if (k == nullptr || v == nullptr) return NB_ERR_INVALID_ARG;
+  nb::KvChunks c;
+  std::memset(&c, 0, sizeof(c));
+  c.n = n;
+  int64_t acc = 0;
+  for (int x = 0; x < n; ++x) {
+    if (len[x] < 1 || start[x] < 0 || rows[x] < 1 || (int64_t)start[x] + len[x] > rows[x]) return NB_ERR_INVALID_ARG;
+    if ((int64_t)B * Hkv * rows[x] >= kMaxIndex * 2) return NB_ERR_INVALID_ARG;
+    if (k[x] == nullptr || v[x] == nullptr || !aligned16(k[x]) || !aligned16(v[x])) return NB_ERR_INVALID_ARG;
+    if (dk != nullptr && (dk[x] == nullptr || !aligned16(dk[x]))) return NB_ERR_INVALID_ARG;
+    if (dv != nullptr && (dv[x] == nullptr || !aligned16(dv[x]))) return NB_ERR_INVALID_ARG;
+    c.off[x] = (int)acc;
+    c.start[x] = start[x];
+    c.rows[x] = rows[x];
+    c.k[x] = k[x];
+    c.v[x] = v[x];
+    c.dk[x] = dk ? dk[x] : nullptr;
+    c.dv[x] = dv ? dv[x] : nullptr;
+    acc += len[x];
+  }
+  if (acc != S) return NB_ERR_INVALID_ARG;
+  c.off[n] = S;
+  *out = c;
+  return NB_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,20 +156,18 @@ int nb_segment_header(const int32_t* seg_buf, int32_t* host_header, void* stream
 
 size_t nb_attn_fwd_workspace_bytes(int, int, int, int, int, int, int) { return 0; }
 
-int nb_attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_resid, float* lse, const int32_t* seg_buf, int B,
-                int Hq, int Hkv, int L, int S, int D, float scale, int window_left, float dropout_p, int dtype,
-                void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
-  const void* ptrs[] = {q, k, v, o, lse, seg_buf};
-  int st = attn_common_checks(ptrs, 6, B, Hq, Hkv, L, S, D, scale, dtype);
-  if (st != NB_OK) return st;
+}  // extern "C"
+
+namespace {
+
+int attn_fwd_kv(const void* q, const nb::KvChunks& kv, void* o, void* o_resid, float* lse, const int32_t* seg_buf,
+                int B, int Hq, int Hkv, int L, int S, int D, float scale, int window_left, float dropout_p, int dtype,
+                void* stream) {
   if (o_resid != nullptr && !aligned16(o_resid)) return NB_ERR_INVALID_ARG;
   if (dropout_p != 0.f) return NB_ERR_UNSUPPORTED;
   nb::FwdParams p;
   p.q = q;
-  p.k = k;
-  p.v = v;
+  p.kv = kv;
   p.o = o;
   p.o_lo = o_resid;
   p.lse = lse;
@@ -137,12 +182,45 @@ int nb_attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_re
   return map_hip(nb::launch_attn_fwd(p, D, dtype == NB_F32, (hipStream_t)stream));
 }
 
+}  // namespace
+
+extern "C" {
+
+int nb_attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_resid, float* lse, const int32_t* seg_buf, int B,
+                int Hq, int Hkv, int L, int S, int D, float scale, int window_left, float dropout_p, int dtype,
+                void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  const void* ptrs[] = {q, k, v, o, lse, seg_buf};
+  int st = attn_common_checks(ptrs, 6, B, Hq, Hkv, L, S, D, scale, dtype);
+  if (st != NB_OK) return st;
+  return attn_fwd_kv(q, one_chunk(S, k, v, nullptr, nullptr), o, o_resid, lse, seg_buf, B, Hq, Hkv, L, S, D, scale,
+                     window_left, dropout_p, dtype, stream);
+}
+
+int nb_attn_fwd_chunks(const void* q, const void* const* k_chunk, const void* const* v_chunk,
+                       const int32_t* chunk_len, const int32_t* chunk_start, const int32_t* chunk_rows, int n_chunk,
+                       void* o, void* o_resid, float* lse, const int32_t* seg_buf, int B, int Hq, int Hkv, int L,
+                       int S, int D, float scale, int window_left, float dropout_p, int dtype, void* ws,
+                       size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  const void* ptrs[] = {q, o, lse, seg_buf};
+  int st = attn_common_checks(ptrs, 4, B, Hq, Hkv, L, S, D, scale, dtype);
+  if (st != NB_OK) return st;
+  nb::KvChunks kv;
+  st = chunk_table(k_chunk, v_chunk, nullptr, nullptr, chunk_len, chunk_start, chunk_rows, n_chunk, B, Hkv, S, &kv);
+  if (st != NB_OK) return st;
+  return attn_fwd_kv(q, kv, o, o_resid, lse, seg_buf, B, Hq, Hkv, L, S, D, scale, window_left, dropout_p, dtype,
+                     stream);
+}
+
 namespace {
 size_t delta_bytes(int B, int Hq, int L) { return (((size_t)B * Hq * L * sizeof(float)) + 255) & ~(size_t)255; }
-// dK/dV work order, the backward kernel's queue counters, dQ work order
-size_t order_bytes(int B, int L, int S) {
-  return ((nb::dkdv_order_elems(B, S) + nb::kNumQueues + nb::dq_order_elems(B, L)) * sizeof(int) + 255) &
-         ~(size_t)255;
+// dK/dV work order, the backward kernel's counters, dQ work order, deferred dQ items
+size_t order_bytes(int B, int Hq, int L, int S) {
+  return ((nb::dkdv_order_elems(B, S) + nb::kNumCounters + nb::dq_order_elems(B, L) +
+           nb::dq_cross_elems(B, Hq, L)) * sizeof(int) + 255) & ~(size_t)255;
 }
 }  // namespace
 
@@ -151,20 +229,19 @@ size_t nb_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, 
   (void)D;
   (void)dtype;
   if (B < 1 || Hq < 1 || L < 1 || S < 1) return 0;
-  return delta_bytes(B, Hq, L) + order_bytes(B, L, S);
+  return delta_bytes(B, Hq, L) + order_bytes(B, Hq, L, S);
 }
 
 }  // extern "C"
 
 namespace {
 
-nb::BwdParams bwd_params(const void* dout, const void* q, const void* k, const void* v, const void* o,
+nb::BwdParams bwd_params(const void* dout, const void* q, const nb::KvChunks& kv, const void* o,
                          const void* o_resid, const float* lse, const int32_t* seg_buf, int B, int Hq, int Hkv,
-                         int L, int S, float scale, int window_left, void* dq, void* dk, void* dv, void* ws) {
+                         int L, int S, float scale, int window_left, void* dq, void* ws) {
   nb::BwdParams p;
   p.q = q;
-  p.k = k;
-  p.v = v;
+  p.kv = kv;
   p.o = o;
   p.o_lo = o_resid;
   p.dout = dout;
@@ -172,11 +249,10 @@ nb::BwdParams bwd_params(const void* dout, const void* q, const void* k, const v
   p.delta = reinterpret_cast<float*>(ws);
   p.order = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + delta_bytes(B, Hq, L));
   p.counters = p.order + nb::dkdv_order_elems(B, S);
-  p.qorder = p.counters + nb::kNumQueues;
+  p.qorder = p.counters + nb::kNumCounters;
+  p.cross = p.qorder + nb::dq_order_elems(B, L);
   p.row_klo = seg_buf + nb::seg_layout(B, L, S).row_klo;
   p.dq = dq;
-  p.dk = dk;
-  p.dv = dv;
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;
@@ -227,8 +303,8 @@ int nb_attn_bwd_dq(const void* dout, const void* q, const void* k, const void* v
   if (st != NB_OK) return st;
   if (o_resid != nullptr && !aligned16(o_resid)) return NB_ERR_INVALID_ARG;
   if (ws_bytes < nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype)) return NB_ERR_WORKSPACE;
-  const nb::BwdParams p = bwd_params(dout, q, k, v, o, o_resid, lse, seg_buf, B, Hq, Hkv, L, S, scale,
-                                     window_left, dq, nullptr, nullptr, ws);
+  const nb::BwdParams p = bwd_params(dout, q, one_chunk(S, k, v, nullptr, nullptr), o, o_resid, lse, seg_buf, B,
+                                     Hq, Hkv, L, S, scale, window_left, dq, ws);
   return map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdDq, (hipStream_t)stream));
 }
 
@@ -240,8 +316,8 @@ int nb_attn_bwd_dkdv(const void* dout, const void* q, const void* k, const void*
   int st = attn_common_checks(ptrs, 9, B, Hq, Hkv, L, S, D, scale, dtype);
   if (st != NB_OK) return st;
   if (ws_bytes < nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype)) return NB_ERR_WORKSPACE;
-  const nb::BwdParams p = bwd_params(dout, q, k, v, nullptr, nullptr, lse, seg_buf, B, Hq, Hkv, L, S, scale,
-                                     window_left, nullptr, dk, dv, ws);
+  const nb::BwdParams p = bwd_params(dout, q, one_chunk(S, k, v, dk, dv), nullptr, nullptr, lse, seg_buf, B, Hq,
+                                     Hkv, L, S, scale, window_left, nullptr, ws);
   return map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdDkdv, (hipStream_t)stream));
 }
 
@@ -253,8 +329,8 @@ int nb_attn_bwd_prep(const void* dout, const void* o, const void* o_resid, const
   if (st != NB_OK) return st;
   if (o_resid != nullptr && !aligned16(o_resid)) return NB_ERR_INVALID_ARG;
   if (ws_bytes < nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype)) return NB_ERR_WORKSPACE;
-  const nb::BwdParams p = bwd_params(dout, nullptr, nullptr, nullptr, o, o_resid, nullptr, seg_buf, B, Hq, Hkv, L,
-                                     S, 1.0f, window_left, nullptr, nullptr, nullptr, ws);
+  const nb::BwdParams p = bwd_params(dout, nullptr, one_chunk(S, nullptr, nullptr, nullptr, nullptr), o, o_resid,
+                                     nullptr, seg_buf, B, Hq, Hkv, L, S, 1.0f, window_left, nullptr, ws);
   return map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdPrep, (hipStream_t)stream));
 }
 
@@ -266,8 +342,8 @@ int nb_attn_bwd_main(const void* dout, const void* q, const void* k, const void*
   int st = attn_common_checks(ptrs, 10, B, Hq, Hkv, L, S, D, scale, dtype);
   if (st != NB_OK) return st;
   if (ws_bytes < nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype)) return NB_ERR_WORKSPACE;
-  const nb::BwdParams p = bwd_params(dout, q, k, v, nullptr, nullptr, lse, seg_buf, B, Hq, Hkv, L, S, scale,
-                                     window_left, dq, dk, dv, ws);
+  const nb::BwdParams p = bwd_params(dout, q, one_chunk(S, k, v, dk, dv), nullptr, nullptr, lse, seg_buf, B, Hq,
+                                     Hkv, L, S, scale, window_left, dq, ws);
   return map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdMain, (hipStream_t)stream));
 }
 
@@ -277,6 +353,39 @@ int nb_owner_attended(const int32_t* seg_buf, const int32_t* folded_ids, int B, 
   int st = owner_checks(folded_ids, S, owner_off, n_owner, owner_attended);
   if (st != NB_OK) return st;
   return launch_owner(seg_buf, folded_ids, B, L, S, owner_off, n_owner, owner_attended, (hipStream_t)stream);
+}
+
+int nb_attn_bwd_chunks(const void* dout, const void* q, const void* const* k_chunk, const void* const* v_chunk,
+                       const int32_t* chunk_len, const int32_t* chunk_start, const int32_t* chunk_rows, int n_chunk,
+                       const void* o, const void* o_resid, const float* lse, const int32_t* seg_buf,
+                       const int32_t* folded_ids, int B, int Hq, int Hkv, int L, int S, int D, float scale,
+                       int window_left, int dtype, void* dq, void* const* dk_chunk, void* const* dv_chunk,
+                       uint8_t* chunk_attended, void* ws, size_t ws_bytes, void* stream) {
+  const void* ptrs[] = {dout, q, o, lse, seg_buf, dq, ws};
+  int st = attn_common_checks(ptrs, 7, B, Hq, Hkv, L, S, D, scale, dtype);
+  if (st != NB_OK) return st;
+  if (o_resid != nullptr && !aligned16(o_resid)) return NB_ERR_INVALID_ARG;
+  if (ws_bytes < nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype)) return NB_ERR_WORKSPACE;
+  if (dk_chunk == nullptr || dv_chunk == nullptr) return NB_ERR_INVALID_ARG;
+  nb::KvChunks kv;
+  st = chunk_table(k_chunk, v_chunk, dk_chunk, dv_chunk, chunk_len, chunk_start, chunk_rows, n_chunk, B, Hkv, S, &kv);
+  if (st != NB_OK) return st;
+  int32_t off[nb::kMaxKvChunks + 1];
+  for (int x = 0; x <= n_chunk; ++x) off[x] = kv.off[x];
+  if (chunk_attended != nullptr) {
+    st = owner_checks(folded_ids, S, off, n_chunk, chunk_attended);
+    if (st != NB_OK) return st;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const nb::BwdParams p = bwd_params(dout, q, kv, o, o_resid, lse, seg_buf, B, Hq, Hkv, L, S, scale, window_left,
+                                     dq, ws);
+  st = map_hip(nb::launch_kv_zero_outside(kv, B * Hkv, D * (dtype == NB_F32 ? 4 : 2), s));
+  if (st != NB_OK) return st;
+  st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdPrep, s));
+  if (st != NB_OK) return st;
+  st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdMain, s));
+  if (st != NB_OK || chunk_attended == nullptr) return st;
+  return launch_owner(seg_buf, folded_ids, B, L, S, off, n_chunk, chunk_attended, s);
 }
 
 int nb_attn_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o, const void* o_resid,
@@ -292,8 +401,8 @@ int nb_attn_bwd(const void* dout, const void* q, const void* k, const void* v, c
   st = owner_checks(folded_ids, S, owner_off, n_owner, owner_attended);
   if (st != NB_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  const nb::BwdParams p = bwd_params(dout, q, k, v, o, o_resid, lse, seg_buf, B, Hq, Hkv, L, S, scale,
-                                     window_left, dq, dk, dv, ws);
+  const nb::BwdParams p = bwd_params(dout, q, one_chunk(S, k, v, dk, dv), o, o_resid, lse, seg_buf, B, Hq, Hkv, L,
+                                     S, scale, window_left, dq, ws);
   st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdPrep, s));
   if (st != NB_OK) return st;
   st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdMain, s));
