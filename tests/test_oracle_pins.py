@@ -75,8 +75,8 @@ def test_mask_equals_interval_form(seed):
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-    """Mask invariants (per-document causal, bottom-right, window, padding) on each workload's real doc map, checked per row block
-    """north_star invariants on each workload's real doc map, checked per row block
+def test_mask_invariants_on_workloads(cfg):
+    """Mask invariants on each workload's real doc map, checked per row block
     (every row block, except config 4 -- one 65536-key document -- where the first,
     middle and last blocks are checked)."""
     w = wl.get(cfg)
