@@ -140,8 +140,11 @@ def main() -> int:
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one plain copy of this many MiB with the library's 16-byte streaming "
                          "copy (counter calibration)")
-    ap.add_argument("--part", choices=["attention", "exchange"], default="attention",
-                    help="attention: the hot path (default); exchange: the emulated needed-range K/V exchange")
+    ap.add_argument("--part", choices=["attention", "exchange", "ring"], default="attention",
+                    help="attention: the hot path (default); exchange: the emulated needed-range K/V exchange; "
+                         "ring: the global-layer ring (per-chunk attention, online merges)")
+    ap.add_argument("--ring-config", type=int, default=2,
+                    help="ring workload whose world the global-layer ring runs on (default 2)")
     ap.add_argument("--kv", choices=["concat", "chunks"], default="concat",
                     help="concat: K/V as one neighbourhood buffer (default); chunks: the window-trimmed owner "
                          "chunks read in place (ring workloads)")
@@ -159,6 +162,8 @@ def main() -> int:
 
     if args.part == "exchange":
         return exchange_main(args)
+    if args.part == "ring":
+        return ring_main(args)
     if args.kv == "chunks":
         return chunks_main(args)
 
@@ -424,6 +429,206 @@ def chunks_main(args) -> int:
         "ms_per_call": {nm: round(per[nm], 5) for nm in names},
         "roofline": None, "cpu_baseline": None,
     }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def ring_main(args) -> int:
+    """The global-layer ring of one rank, every chunk resident on one GPU: the rank's queries against the K/V
+    chunks of owners rank, rank-1, ..., 0 (own chunk causal, the rest non-causal, per-document masking, no
+    window), each chunk's (out, lse) merged online (the cross chunks at their live rows), the merged output
+    rounded, then every chunk's backward with the global out/lse (Delta formed once) summing dQ in fp32.
+    Workload: --ring-config's world (default config 2: 4-way ring, rank 3, 4096-token chunks) as a full-attention
+    layer.  Also timed, outside the step: the same attention as one pass over the chunk table."""
+    import numpy as np
+    import torch
+
+    from sliding_window_attention_fold_amd import _lib
+    from sliding_window_attention_fold_amd import workloads as wl
+
+    lib = _lib.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = wl.get(args.ring_config)
+    if w.mode != "ring":
+        print("--part ring needs a ring workload", file=sys.stderr)
+        return 2
+    r, Lc = w.cp_rank, w.L
+    B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
+    S = (r + 1) * Lc
+    glob, pad = wl.global_doc_map(w)
+    q, k, v, do = wl.make_tensors(w, S, "bf16")
+    qd, dod = q.to(dev).contiguous(), do.to(dev).contiguous()
+    order = [r] + list(range(r - 1, -1, -1))
+    kc = [k[:, :, o * Lc:(o + 1) * Lc].contiguous().to(dev) for o in order]
+    vc = [v[:, :, o * Lc:(o + 1) * Lc].contiguous().to(dev) for o in order]
+    starts = [o * Lc for o in order]
+    ids_d = torch.from_numpy(np.ascontiguousarray(glob[:, :S])).to(dev)
+    pad_d = None if pad is None else torch.from_numpy(np.ascontiguousarray(pad[:, :S])).to(dev)
+    bf = _lib.NB_BF16
+    scale = D ** -0.5
+    nseg = lib.nb_segment_buffer_elems(B, Lc, S)
+    segbuf = torch.empty((nseg,), dtype=torch.int32, device=dev)
+    folded = torch.empty((B, S), dtype=torch.int32, device=dev)
+    out_step = torch.empty_like(qd)
+    lse_step = torch.empty((B, Hq, Lc), dtype=torch.float32, device=dev)
+    out_acc = torch.empty((B, Hq, Lc, D), dtype=torch.float32, device=dev)
+    lse_acc = torch.empty((B, Hq, Lc), dtype=torch.float32, device=dev)
+    out, resid = torch.empty_like(qd), torch.empty_like(qd)
+    live_idx = torch.empty((B * Lc,), dtype=torch.int32, device=dev)
+    n_live = torch.empty((1,), dtype=torch.int32, device=dev)
+    dq_c = torch.empty_like(qd)
+    dq_acc = torch.empty((B, Hq, Lc, D), dtype=torch.float32, device=dev)
+    dks = [torch.empty_like(t) for t in kc]
+    dvs = [torch.empty_like(t) for t in vc]
+    ws_bytes = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, Lc, Lc, D, bf)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    Pp = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    R = B * Hq * Lc
+    q0 = r * Lc
+
+    calls = [("segments", lambda: lib.nb_segment_build(Pp(ids_d), Pp(pad_d), B, S, Lc, -1, Pp(folded), Pp(segbuf),
+                                                         nseg, sp)),
+             ]
+    for c, o in enumerate(order):
+        calls.append((f"fwd_chunk{o}", lambda c=c: lib.nb_ring_chunk_fwd(
+            Pp(qd), Pp(kc[c]), Pp(vc[c]), Pp(out_step), Pp(lse_step), Pp(segbuf), B, Hq, Hkv, Lc, Lc, D, q0,
+            starts[c], scale, bf, sp)))
+        if c == 0:
+            calls.append((f"merge{o}", lambda: lib.nb_ring_merge(Pp(out_acc), Pp(lse_acc), Pp(out_step), Pp(lse_step),
+                                                                 R, D, bf, 1, sp)))
+        else:
+            calls.append((f"live_rows{o}", lambda c=c: lib.nb_ring_live_rows(Pp(segbuf), B, Lc, Lc, q0, starts[c],
+                                                                             Pp(live_idx), Pp(n_live), sp)))
+            calls.append((f"merge_live{o}", lambda: lib.nb_ring_merge_live(
+                Pp(out_acc), Pp(lse_acc), Pp(out_step), Pp(lse_step), Pp(live_idx), Pp(n_live), B * Lc, B, Hq, Lc,
+                D, bf, sp)))
+    calls.append(("finalize", lambda: lib.nb_ring_finalize(Pp(out_acc), Pp(out), Pp(resid), R, D, bf, sp)))
+    for c, o in enumerate(order):
+        # Delta once (first chunk); the chunks' dQ summed in fp32 by the kernels themselves
+        fl = _lib.NB_RING_DQ_F32_SET if c == 0 else (_lib.NB_RING_DQ_F32_ADD | _lib.NB_RING_DELTA_READY)
+        calls.append((f"bwd_chunk{o}", lambda c=c, fl=fl: lib.nb_ring_chunk_bwd(
+            Pp(dod), Pp(qd), Pp(kc[c]), Pp(vc[c]), Pp(out), Pp(resid), Pp(lse_acc), Pp(segbuf), B, Hq, Hkv, Lc, Lc,
+            D, q0, starts[c], scale, bf, Pp(dq_acc), Pp(dks[c]), Pp(dvs[c]), fl, Pp(ws), ws_bytes, sp)))
+
+    def step(events=None):
+        for i, (nm, fn) in enumerate(calls):
+            if events is not None:
+                events[i].record(stream)
+            rc = fn()
+            if rc != 0:
+                raise _lib.NbError(rc, nm)
+        if events is not None:
+            events[len(calls)].record(stream)
+
+    step()
+    torch.cuda.synchronize()
+    off_klo = lib.nb_segment_offset_row_klo(B, Lc)
+    klo = segbuf[off_klo:off_klo + B * Lc].view(B, Lc).long()
+    pos = (q0 + torch.arange(Lc, device=dev)).view(1, Lc)
+    pairs = int(torch.clamp(pos - klo + 1, min=0).sum().item())
+    useful = 14.0 * D * Hq * pairs
+    bwd_flop = 10.0 * D * Hq * pairs
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for s_ in range(args.steps):
+        step(evs[s_])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    per = {nm: float(np.mean([evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps)]))
+           for i, (nm, _) in enumerate(calls)}
+    bwd_ms = sum(v_ for nm, v_ in per.items() if nm.startswith("bwd_chunk"))
+    tflops = useful / (ms_step * 1e-3) / 1e12
+
+    # the same attention in one pass over the chunk table (outside the step, for comparison)
+    asc = list(range(r + 1))
+    Pn, In = ctypes.c_void_p * (r + 1), ctypes.c_int32 * (r + 1)
+    kp = Pn(*[kc[order.index(o)].data_ptr() for o in asc])
+    vp = Pn(*[vc[order.index(o)].data_ptr() for o in asc])
+    dkp = Pn(*[dks[order.index(o)].data_ptr() for o in asc])
+    dvp = Pn(*[dvs[order.index(o)].data_ptr() for o in asc])
+    ln, st, rw = In(*([Lc] * (r + 1))), In(*([0] * (r + 1))), In(*([Lc] * (r + 1)))
+    cv = lambda a: ctypes.cast(a, ctypes.c_void_p)  # noqa: E731
+    lse1 = torch.empty((B, Hq, Lc), dtype=torch.float32, device=dev)
+    ws1_bytes = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, Lc, S, D, bf)
+    ws1 = torch.empty((ws1_bytes,), dtype=torch.uint8, device=dev)
+    seg1 = torch.empty((lib.nb_segment_buffer_elems(B, Lc, S),), dtype=torch.int32, device=dev)
+    fold1 = torch.empty((B, S), dtype=torch.int32, device=dev)
+
+    def one_pass():
+        for rc, nm in ((lib.nb_segment_build(Pp(ids_d), Pp(pad_d), B, S, Lc, -1, Pp(fold1), Pp(seg1), seg1.numel(),
+                                             sp), "segments"),
+                       (lib.nb_attn_fwd_chunks(Pp(qd), cv(kp), cv(vp), cv(ln), cv(st), cv(rw), r + 1, Pp(out),
+                                               Pp(resid), Pp(lse1), Pp(seg1), B, Hq, Hkv, Lc, S, D, scale, -1, 0.0,
+                                               bf, None, 0, sp), "fwd"),
+                       (lib.nb_attn_bwd_chunks(Pp(dod), Pp(qd), cv(kp), cv(vp), cv(ln), cv(st), cv(rw), r + 1,
+                                               Pp(out), Pp(resid), Pp(lse1), Pp(seg1), None, B, Hq, Hkv, Lc, S, D,
+                                               scale, -1, bf, Pp(dq_c), cv(dkp), cv(dvp), None, Pp(ws1), ws1_bytes,
+                                               sp), "bwd")):
+            if rc != 0:
+                raise _lib.NbError(rc, nm)
+
+    one_pass()
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(args.steps):
+        one_pass()
+    c1.record(stream)
+    torch.cuda.synchronize()
+    one_ms = c0.elapsed_time(c1) / args.steps
+
+    rec = {
+        "metric": "global-layer ring fwd+bwd useful TFLOP/s per shard; % of bf16 MFMA peak (MI355X)",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"config{args.ring_config} world as a global (full-attention) layer: ring rank {r} of "
+                               f"{w.cp_size}, {r + 1} chunks of {Lc} tokens, per-chunk attention + online merges",
+                   "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "chunk": Lc, "chunks": r + 1, "window": -1,
+                   "doc_lengths": list(w.doc_len), "pairs_per_head": pairs, "useful_flop_per_step": useful},
+        "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "ms_per_call": {nm: round(v_, 5) for nm, v_ in per.items()},
+        "one_pass_ms": round(one_ms, 5),
+        "roofline": {"kernel": "per-chunk backward (prep + main, all chunks)", "bound": "mfma",
+                     "achieved": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(bwd_flop / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flop_per_step": bwd_flop},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import ring_oracle as ro
+        rows = min(Lc, args.cpu_rows)
+        nh = min(Hq, 4)                     # q heads 0 .. nh-1 and their kv heads
+        qs, dos = q[:, :nh, :rows], do[:, :nh, :rows]
+        kv_h = max(1, nh // (Hq // Hkv))
+        ids_f = glob[:, :S].copy()
+        if pad is not None:
+            ids_f[pad[:, :S] != 0] = 0
+        q_ids = ids_f[:, q0:q0 + rows]
+        t_start = time.perf_counter()
+        acc = lacc = None
+        for o in order:
+            so, sl = ro.chunk_forward(qs, k[:, :kv_h, o * Lc:(o + 1) * Lc], v[:, :kv_h, o * Lc:(o + 1) * Lc], q_ids,
+                                      ids_f[:, o * Lc:(o + 1) * Lc], q0, o * Lc, o == r, scale)
+            acc, lacc = ro.merge(acc, lacc, so, sl)
+        for o in order:
+            ro.chunk_backward(qs, k[:, :kv_h, o * Lc:(o + 1) * Lc], v[:, :kv_h, o * Lc:(o + 1) * Lc], dos, acc, lacc,
+                              q_ids, ids_f[:, o * Lc:(o + 1) * Lc], q0, o * Lc, o == r, scale)
+        dt = time.perf_counter() - t_start
+        m = ro.chunk_mask(q_ids, ids_f[:, :S], q0, 0, True)
+        sample_pairs = int(m.sum()) * nh
+        rec["cpu_baseline"] = {"value": round(14.0 * D * sample_pairs / dt / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": torch.get_num_threads(), "kind": "oracle",
+                               "sample": f"fp64 numpy ring oracle, q heads 0-{nh - 1}, query rows 0-{rows - 1} of the shard, "
+                                         f"all {r + 1} chunks, forward + merges + backward; {dt:.1f} s"}
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -1,5 +1,5 @@
-"""ctypes loader for libnbattn.so (the C-ABI declared in include/nbattn.h and
-include/nbexchange.h).
+"""ctypes loader for libnbattn.so (the C-ABI declared in include/nbattn.h,
+include/nbexchange.h and include/nbring.h).
 
 The library is built in-tree by ``sliding_window_attention_fold_amd.build``.  If it
 is missing, loading fails loudly: there is no fallback implementation.
@@ -18,7 +18,7 @@ HDR = dict(n_seg=0, max_q=1, max_k=2, status=3, lo=4, B=5, L=6, S=7, window=8, n
 
 # name -> (restype, argtypes); every symbol include/*.h declares
 _c = ctypes
-_P, _I, _F, _Z = _c.c_void_p, _c.c_int, _c.c_float, _c.c_size_t
+_P, _I, _F, _Z, _L = _c.c_void_p, _c.c_int, _c.c_float, _c.c_size_t, _c.c_int64
 SIGNATURES = {
     "nb_status_string": (_c.c_char_p, [_I]),
     "nb_version": (_I, []),
@@ -53,8 +53,17 @@ SIGNATURES = {
     "nb_exchange_send_index": (_I, [_P, _I, _I, _P, _Z, _P]),
     "nb_exchange_gather": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "nb_exchange_scatter_add": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "nb_ring_chunk_fwd": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "nb_ring_merge": (_I, [_P, _P, _P, _P, _L, _I, _I, _I, _P]),
+    "nb_ring_live_rows": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "nb_ring_merge_live": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "nb_ring_finalize": (_I, [_P, _P, _P, _L, _I, _I, _P]),
+    "nb_ring_chunk_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
+                               _P, _P, _P, _I, _P, _Z, _P]),
+    "nb_ring_grad_add": (_I, [_P, _P, _L, _I, _I, _P]),
 }
 NB_XCH_MAX_RANKS = 64
+NB_RING_DELTA_READY, NB_RING_DQ_F32_SET, NB_RING_DQ_F32_ADD = 1, 2, 4
 
 _LIB = None
 

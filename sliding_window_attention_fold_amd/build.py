@@ -21,6 +21,7 @@ SOURCES = [
     "csrc/attn_fwd.hip",
     "csrc/attn_bwd.hip",
     "csrc/exchange.hip",
+    "csrc/ring.hip",
     "csrc/nbattn_host.cpp",
 ]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -128,7 +128,8 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
   const int kg = w % C::NKG;                      // key group
   const bool role_a = w < C::NKG;                 // A: S, P, dV   B: dP, dS, dK
-  const int off = p.S - p.L;
+  const int off = p.q_off;                        // row i sits at key position off + i
+  const int kor = p.k_origin;                     // row_klo values count keys from here
   const TileAccess<T, TL> acc(ln, lane);
   const TileDma<T, C::BQ, D, C::NW> dma;   // Q and dO tiles share one layout
   const int kvh = f % p.Hkv;
@@ -152,7 +153,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
     int pred = 0;
     if (t < n_q_tiles) {
       const int i = t * C::BQ;
-      int bsi = p.row_klo[(size_t)b * p.L + i];
+      int bsi = p.row_klo[(size_t)b * p.L + i] - kor;
       if (p.window >= 0) bsi = max(bsi, off + i - p.window);
       pred = bsi <= jmax;
     }
@@ -251,7 +252,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
     // rows of this tile: positions off+i0 .. off+i0+nrows-1; band starts are nondecreasing
     const int p_min = off + si.i0, p_max = off + si.i0 + si.nrows - 1;
     auto band = [&](int qi) {
-      const int bq = max(0, ks[qi]);
+      const int bq = max(0, ks[qi] - kor);
       return p.window >= 0 ? max(bq, off + si.i0 + qi - p.window) : bq;
     };
     // (readfirstlane lets the compiler branch on the scalar unit)
@@ -285,7 +286,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int qi = 8 * rq + 4 * g + e;
-          int bq = max(0, k4[e]);
+          int bq = max(0, k4[e] - kor);
           if (p.window >= 0) bq = max(bq, off + si.i0 + qi - p.window);
           const bool in = (qi < si.nrows) & (j >= bq) & (j <= off + si.i0 + qi);
           sacc[4 * rq + e] = in ? sacc[4 * rq + e] : 0.f;
@@ -519,7 +520,6 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
   const int qg = w % C::NQG;            // query group
   const bool role_a = w < C::NQG;       // A: Q, S, P   B: dO, dP
-  const int off = p.S - p.L;
   const TileAccess<T, TL> acc(ln, lane);
   const TileDma<T, C::BN, D, C::NW> dma;   // K and V tiles share one layout
   const int kvh = f % p.Hkv;
@@ -528,11 +528,12 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
   const int b = code / n_qt, qt = code % n_qt;
   const int i = qt * C::BM + 32 * qg + ln;
   const bool in_range = i < p.L;
-  const int pos = off + i;
-  int bs = pos + 1;
+  const int pq = p.q_off + i;               // the row's key position
+  const int pos = min(pq, p.S - 1);         // its band's last key
+  int bs = pq + 1;
   if (in_range) {
-    bs = max(0, p.row_klo[(size_t)b * p.L + i]);  // clamp: never index before the neighbourhood
-    if (p.window >= 0) bs = max(bs, pos - p.window);
+    bs = max(0, p.row_klo[(size_t)b * p.L + i] - p.k_origin);  // clamp: never index before the keys
+    if (p.window >= 0) bs = max(bs, pq - p.window);
   }
   const bool real = in_range && bs <= pos;
   // (uniform; readfirstlane makes the tile decisions scalar branches)
@@ -705,7 +706,7 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
     }
   }
 
-  if (in_range) {
+  if (in_range && p.dq_mode == kDqStore) {
     T* dqp = reinterpret_cast<T*>(p.dq) + qrow * D;
 #pragma unroll
     for (int d = 0; d < DH; ++d) {
@@ -714,6 +715,22 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
         store_quad<T>(dqp + 32 * (dh0 + d) + 8 * rq + 4 * g, dqacc[d][4 * rq] * p.scale,
                       dqacc[d][4 * rq + 1] * p.scale, dqacc[d][4 * rq + 2] * p.scale,
                       dqacc[d][4 * rq + 3] * p.scale);
+      }
+    }
+  } else if (in_range) {   // fp32 dQ accumulator: set, or add this call's contribution
+    float* dqp = reinterpret_cast<float*>(p.dq) + qrow * D;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        f32x4* dst = reinterpret_cast<f32x4*>(dqp + 32 * (dh0 + d) + 8 * rq + 4 * g);
+        f32x4 x = f32x4{dqacc[d][4 * rq] * p.scale, dqacc[d][4 * rq + 1] * p.scale, dqacc[d][4 * rq + 2] * p.scale,
+                        dqacc[d][4 * rq + 3] * p.scale};
+        if (p.dq_mode == kDqAddF32) {
+          const f32x4 a = *dst;
+          x = f32x4{a[0] + x[0], a[1] + x[1], a[2] + x[2], a[3] + x[3]};
+        }
+        *dst = x;
       }
     }
   }
@@ -753,7 +770,7 @@ __device__ __forceinline__ void delta_rows(const BwdParams& p, int wg) {
     for (int o = 16; o > 0; o >>= 1) part += __shfl_xor(part, o);
     if (row[r] < n_rows && l32 == 0) {
       const int i = (int)(row[r] % p.L), b = (int)(row[r] / ((long long)p.Hq * p.L));
-      const bool real = p.row_klo[(size_t)b * p.L + i] <= p.S - p.L + i;
+      const bool real = p.row_klo[(size_t)b * p.L + i] - p.k_origin <= p.q_off + i;
       p.delta[row[r]] = real ? part : 0.f;
     }
   }
@@ -806,7 +823,7 @@ __device__ __forceinline__ unsigned long long work_key(unsigned work, int i, int
 template <int BK, int BQ, int BM>
 __device__ void work_order(const BwdParams& p, int modes, unsigned long long* keys, int* bst) {
   const int tid = threadIdx.x;
-  const int off = p.S - p.L;
+  const int off = p.q_off;
   if (tid < kNumCounters) p.counters[tid] = 0;  // work queues and the deferred-item list start empty
   if (modes & 1) {
     const int n_kt = (p.S + BK - 1) / BK;
@@ -818,7 +835,7 @@ __device__ void work_order(const BwdParams& p, int modes, unsigned long long* ke
       // band start of each query tile's first row (nondecreasing along a row)
       auto band_start_g = [&](int b, int t) {
         const int r = t * BQ;
-        const int bq = max(0, p.row_klo[(size_t)b * p.L + r]);
+        const int bq = max(0, p.row_klo[(size_t)b * p.L + r] - p.k_origin);
         return p.window >= 0 ? max(bq, off + r - p.window) : bq;
       };
       const bool staged = p.B * n_q_tiles <= kOrderBandMax;
@@ -860,9 +877,9 @@ __device__ void work_order(const BwdParams& p, int modes, unsigned long long* ke
         if (i < n) {
           const int b = i / n_qt, qt = i % n_qt;
           const int r0 = qt * BM, r1 = min(p.L, r0 + BM) - 1;
-          int bq = max(0, p.row_klo[(size_t)b * p.L + r0]);
+          int bq = max(0, p.row_klo[(size_t)b * p.L + r0] - p.k_origin);
           if (p.window >= 0) bq = max(bq, off + r0 - p.window);
-          key = work_key((unsigned)max(0, off + r1 + 1 - bq), i, n);
+          key = work_key((unsigned)max(0, min(off + r1 + 1, p.S) - bq), i, n);
         }
         keys[i] = key;
       }
@@ -1001,6 +1018,8 @@ static hipError_t launch_t(const BwdParams& p, int what, hipStream_t s) {
   switch (what) {
     case kBwdPrep:   // Delta + work orders of both passes
       return launch_prep_t<T, D>(p, true, 3, s);
+    case kBwdOrders:   // the work orders alone (Delta already in the workspace)
+      return launch_prep_t<T, D>(p, false, 3, s);
     case kBwdMain:
       return launch_main_t<T, D, 3>(p, s);
     case kBwdDq:     // Delta + the dQ order, then the dQ pass alone

@@ -74,14 +74,14 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdP
   const int b = gid / p.Hkv, kvh = gid % p.Hkv;
   const int h = kvh * grp + rest % grp, qt = rest / grp;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
-  const int off = p.S - p.L;
   const int i = qt * C::BM + 32 * w + ln;
   const bool in_range = i < p.L;
-  const int pos = off + i;
-  int bs = pos + 1;
+  const int pq = p.q_off + i;               // the row's key position
+  const int pos = min(pq, p.S - 1);         // its band's last key
+  int bs = pq + 1;
   if (in_range) {
-    bs = max(0, p.row_klo[(size_t)b * p.L + i]);  // clamp: never index before the neighbourhood
-    if (p.window >= 0) bs = max(bs, pos - p.window);
+    bs = max(0, p.row_klo[(size_t)b * p.L + i] - p.k_origin);  // clamp: never index before the keys
+    if (p.window >= 0) bs = max(bs, pq - p.window);
   }
   const bool real = in_range && bs <= pos;
 

@@ -71,6 +71,12 @@ struct FwdParams {
   float* lse;
   const int32_t* row_klo;
   int B, Hq, Hkv, L, S, window;
+  // Query row i sits at key position q_off + i; row_klo values count keys from
+  // k_origin.  Neighbourhood attention: q_off = S - L, k_origin = 0.  A ring
+  // chunk: row_klo in global positions, k_origin = the chunk's first global
+  // position, q_off = the shard's first global position - k_origin (>= S for
+  // an earlier owner's chunk, whose keys then all precede the queries).
+  int q_off, k_origin;
   float scale_log2;  // softmax scale * log2(e)
 };
 
@@ -89,6 +95,8 @@ struct BwdParams {
   const int32_t* row_klo;
   void* dq;
   int B, Hq, Hkv, L, S, window;
+  int q_off, k_origin;   // as in FwdParams
+  int dq_mode;       // kDqStore: dq is T, written; kDqSetF32 / kDqAddF32: dq is fp32, set / added to
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
 };
@@ -106,8 +114,10 @@ hipError_t launch_segment_build(const SegParams& p, hipStream_t s);
 hipError_t launch_attn_fwd(const FwdParams& p, int D, bool f32, hipStream_t s);
 // Backward launches: kBwdPrep = Delta + work orders; kBwdMain = both passes in
 // one persistent grid (after kBwdPrep); kBwdDq = Delta + dQ pass; kBwdDkdv =
-// dK/dV pass (after kBwdPrep or kBwdDq on the same workspace).
-enum { kBwdPrep = 0, kBwdMain = 1, kBwdDq = 2, kBwdDkdv = 3 };
+// dK/dV pass (after kBwdPrep or kBwdDq on the same workspace); kBwdOrders =
+// the work orders alone (Delta left in the workspace by an earlier kBwdPrep).
+enum { kBwdPrep = 0, kBwdMain = 1, kBwdDq = 2, kBwdDkdv = 3, kBwdOrders = 4 };
+enum { kDqStore = 0, kDqSetF32 = 1, kDqAddF32 = 2 };
 hipError_t launch_bwd(const BwdParams& p, int D, bool f32, int what, hipStream_t s);
 // Zeros the dK/dV rows of the chunk buffers that lie outside the neighbourhood.
 hipError_t launch_kv_zero_outside(const KvChunks& c, int BH, int row_bytes, hipStream_t s);

@@ -15,6 +15,7 @@
 #include <cstring>
 
 #include "../../include/nbattn.h"
+#include "../../include/nbring.h"
 #include "nb_kernels.h"
 
 namespace {
@@ -160,9 +161,10 @@ size_t nb_attn_fwd_workspace_bytes(int, int, int, int, int, int, int) { return 0
 
 namespace {
 
+// q_off / k_origin: see FwdParams (the neighbourhood call: S - L and 0).
 int attn_fwd_kv(const void* q, const nb::KvChunks& kv, void* o, void* o_resid, float* lse, const int32_t* seg_buf,
                 int B, int Hq, int Hkv, int L, int S, int D, float scale, int window_left, float dropout_p, int dtype,
-                void* stream) {
+                void* stream, int q_off = -1, int k_origin = 0) {
   if (o_resid != nullptr && !aligned16(o_resid)) return NB_ERR_INVALID_ARG;
   if (dropout_p != 0.f) return NB_ERR_UNSUPPORTED;
   nb::FwdParams p;
@@ -178,6 +180,8 @@ int attn_fwd_kv(const void* q, const nb::KvChunks& kv, void* o, void* o_resid, f
   p.L = L;
   p.S = S;
   p.window = window_left < 0 ? -1 : window_left;
+  p.q_off = q_off < 0 ? S - L : q_off;
+  p.k_origin = k_origin;
   p.scale_log2 = scale * 1.4426950408889634f;
   return map_hip(nb::launch_attn_fwd(p, D, dtype == NB_F32, (hipStream_t)stream));
 }
@@ -238,7 +242,8 @@ namespace {
 
 nb::BwdParams bwd_params(const void* dout, const void* q, const nb::KvChunks& kv, const void* o,
                          const void* o_resid, const float* lse, const int32_t* seg_buf, int B, int Hq, int Hkv,
-                         int L, int S, float scale, int window_left, void* dq, void* ws) {
+                         int L, int S, float scale, int window_left, void* dq, void* ws, int q_off = -1,
+                         int k_origin = 0) {
   nb::BwdParams p;
   p.q = q;
   p.kv = kv;
@@ -259,6 +264,9 @@ nb::BwdParams bwd_params(const void* dout, const void* q, const nb::KvChunks& kv
   p.L = L;
   p.S = S;
   p.window = window_left < 0 ? -1 : window_left;
+  p.q_off = q_off < 0 ? S - L : q_off;
+  p.k_origin = k_origin;
+  p.dq_mode = nb::kDqStore;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   return p;
@@ -408,6 +416,40 @@ int nb_attn_bwd(const void* dout, const void* q, const void* k, const void* v, c
   st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdMain, s));
   if (st != NB_OK) return st;
   return launch_owner(seg_buf, folded_ids, B, L, S, owner_off, n_owner, owner_attended, s);
+}
+
+int nb_ring_chunk_fwd(const void* q, const void* k, const void* v, void* out, float* lse, const int32_t* seg_buf,
+                      int B, int Hq, int Hkv, int L, int Lk, int D, int q_start, int k_start, float scale, int dtype,
+                      void* stream) {
+  const void* ptrs[] = {q, k, v, out, lse, seg_buf};
+  int st = attn_common_checks(ptrs, 6, B, Hq, Hkv, L, Lk, D, scale, dtype);
+  if (st != NB_OK) return st;
+  if (k_start < 0 || k_start > q_start || (int64_t)q_start + L >= kMaxIndex) return NB_ERR_INVALID_ARG;
+  return attn_fwd_kv(q, one_chunk(Lk, k, v, nullptr, nullptr), out, nullptr, lse, seg_buf, B, Hq, Hkv, L, Lk, D,
+                     scale, -1, 0.f, dtype, stream, q_start - k_start, k_start);
+}
+
+int nb_ring_chunk_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o,
+                      const void* o_resid, const float* lse, const int32_t* seg_buf, int B, int Hq, int Hkv, int L,
+                      int Lk, int D, int q_start, int k_start, float scale, int dtype, void* dq, void* dk, void* dv,
+                      int flags, void* ws, size_t ws_bytes, void* stream) {
+  const void* ptrs[] = {dout, q, k, v, o, lse, seg_buf, dq, dk, dv, ws};
+  int st = attn_common_checks(ptrs, 11, B, Hq, Hkv, L, Lk, D, scale, dtype);
+  if (st != NB_OK) return st;
+  if (o_resid != nullptr && !aligned16(o_resid)) return NB_ERR_INVALID_ARG;
+  if (k_start < 0 || k_start > q_start || (int64_t)q_start + L >= kMaxIndex) return NB_ERR_INVALID_ARG;
+  if (flags & ~(NB_RING_DELTA_READY | NB_RING_DQ_F32_SET | NB_RING_DQ_F32_ADD)) return NB_ERR_INVALID_ARG;
+  if ((flags & NB_RING_DQ_F32_SET) && (flags & NB_RING_DQ_F32_ADD)) return NB_ERR_INVALID_ARG;
+  if (ws_bytes < nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, Lk, D, dtype)) return NB_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  nb::BwdParams p = bwd_params(dout, q, one_chunk(Lk, k, v, dk, dv), o, o_resid, lse, seg_buf, B, Hq, Hkv, L, Lk,
+                               scale, -1, dq, ws, q_start - k_start, k_start);
+  p.dq_mode = (flags & NB_RING_DQ_F32_SET) ? nb::kDqSetF32 : (flags & NB_RING_DQ_F32_ADD) ? nb::kDqAddF32
+                                                                                            : nb::kDqStore;
+  st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, (flags & NB_RING_DELTA_READY) ? nb::kBwdOrders : nb::kBwdPrep,
+                              s));
+  if (st != NB_OK) return st;
+  return map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdMain, s));
 }
 
 }  // extern "C"

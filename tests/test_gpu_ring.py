@@ -1,0 +1,197 @@
+"""GPU parity of the global-layer ring attention (include/nbring.h) against the
+fp64 ring oracle (oracle/ring_oracle.py), through the C-ABI.
+
+Per-chunk forward (own chunk causal, earlier owners' chunks non-causal) and
+backward with the global out/lse, the -inf-safe merge and its live-row form
+(the live-row list bit-exact), the final rounding, and the whole ring of a
+rank against one softmax over its causal neighbourhood; bf16 and float32, head
+dims 64 / 128 / 256, padding tails, several batch rows, GQA.  Tolerances as in
+gpu_cases (bf16 2e-2, float32 1e-4; -inf LSE exactly).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import nbattn_oracle as orc
+from oracle import ring_oracle as ro
+from sliding_window_attention_fold_amd import ring
+from gpu_cases import assert_close, say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _ids(rng, B, N, lo, hi, pad_tail=0):
+    ids = np.zeros((B, N), dtype=np.int32)
+    for b in range(B):
+        pos, d = 0, 1
+        while pos < N:
+            n = int(rng.integers(lo, hi + 1))
+            ids[b, pos:pos + n] = d
+            pos, d = pos + n, d + 1
+        if pad_tail:
+            ids[b, N - pad_tail:] = 0
+    return ids
+
+
+class World:
+    def __init__(self, seed, B, Hq, Hkv, D, Lc, P, lo, hi, pad_tail, dt):
+        rng = np.random.default_rng(seed)
+        g = torch.Generator("cpu").manual_seed(seed)
+        self.B, self.Hq, self.Hkv, self.D, self.Lc, self.P, self.dt = B, Hq, Hkv, D, Lc, P, dt
+        self.ids = _ids(rng, B, P * Lc, lo, hi, pad_tail)
+        N = P * Lc
+        self.q = torch.randn((B, Hq, N, D), generator=g).to(DT[dt])
+        self.k = torch.randn((B, Hkv, N, D), generator=g).to(DT[dt])
+        self.v = torch.randn((B, Hkv, N, D), generator=g).to(DT[dt])
+        self.do = torch.randn((B, Hq, N, D), generator=g).to(DT[dt])
+        self.scale = D ** -0.5
+
+    def shard(self, t, r):
+        return t[:, :, r * self.Lc:(r + 1) * self.Lc].contiguous()
+
+    def segs(self, r):
+        return ring.ring_segments(torch.from_numpy(self.ids).to(DEV), r * self.Lc, self.Lc)
+
+
+CASES = [  # seed, B, Hq, Hkv, D, Lc, P, rank, doc lengths lo..hi, pad tail, dtype
+    (1, 1, 2, 1, 64, 96, 3, 2, 10, 70, 0, "bf16"),
+    (2, 2, 4, 2, 128, 130, 4, 3, 1, 200, 17, "bf16"),
+    (3, 1, 4, 2, 256, 128, 3, 2, 100, 400, 0, "bf16"),
+    (4, 1, 2, 1, 128, 64, 2, 1, 5, 40, 9, "f32"),
+    (5, 2, 2, 2, 256, 70, 3, 1, 30, 90, 5, "f32"),
+    (6, 1, 2, 1, 64, 100, 4, 3, 400, 400, 0, "bf16"),   # one document over the whole sequence
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_chunk_forward_and_ring_merge(case):
+    seed, B, Hq, Hkv, D, Lc, P, r, lo, hi, pt, dt = case
+    w = World(seed, B, Hq, Hkv, D, Lc, P, lo, hi, pt, dt)
+    say(f"[ring] fwd case seed={seed} D={D} Lc={Lc} rank={r} {dt}")
+    segs = w.segs(r)
+    q = w.shard(w.q, r).to(DEV)
+    q_ids = w.ids[:, r * Lc:(r + 1) * Lc]
+    order = [r] + list(range(r - 1, -1, -1))
+    kc = [w.shard(w.k, o).to(DEV) for o in order]
+    vc = [w.shard(w.v, o).to(DEV) for o in order]
+    starts = [o * Lc for o in order]
+    out_ref = lse_ref = None
+    out_acc = torch.full((B, Hq, Lc, D), float("nan"), dtype=torch.float32, device=DEV)   # init ignores them
+    lse_acc = torch.full((B, Hq, Lc), float("nan"), dtype=torch.float32, device=DEV)
+    for c, o in enumerate(order):
+        so, sl = ring.chunk_fwd(q, kc[c], vc[c], segs, starts[c])
+        ro_, rl_ = ro.chunk_forward(w.shard(w.q, r), w.shard(w.k, o), w.shard(w.v, o), q_ids,
+                                    w.ids[:, o * Lc:(o + 1) * Lc], r * Lc, o * Lc, o == r, w.scale)
+        assert_close(f"chunk {o} out", so.float().cpu().numpy(), ro_, dt)
+        assert_close(f"chunk {o} lse", sl.cpu().numpy(), rl_, dt)
+        assert not so.float().cpu().numpy()[np.isneginf(rl_)].any()
+        # the live rows: exactly the rows with a key in the chunk
+        idx, n = ring.live_rows(segs, Lc, o * Lc)
+        live = np.flatnonzero(ro.chunk_mask(q_ids, w.ids[:, o * Lc:(o + 1) * Lc], r * Lc, o * Lc, o == r).any(axis=2))
+        assert int(n.item()) == len(live) and idx[:len(live)].cpu().numpy().tolist() == live.tolist()
+        if c == 0:
+            ring.merge_(out_acc, lse_acc, so, sl, init=True)
+        else:
+            ring.merge_live_(out_acc, lse_acc, so, sl, idx, n)
+        out_ref, lse_ref = ro.merge(out_ref, lse_ref, so.double().cpu().numpy(), sl.double().cpu().numpy())
+    # the merges against the oracle's merge of the same chunk results (fp32 arithmetic)
+    assert_close("merged out", out_acc.cpu().numpy(), out_ref, "f32")
+    assert_close("merged lse", lse_acc.cpu().numpy(), lse_ref, "f32")
+    # and the whole ring against one softmax over the causal neighbourhood
+    S = (r + 1) * Lc
+    o_full, l_full = orc.attention_forward(w.shard(w.q, r), w.k[:, :, :S], w.v[:, :, :S], w.ids[:, :S], -1, w.scale)
+    assert_close("ring out", out_acc.cpu().numpy(), o_full, dt)
+    assert_close("ring lse", lse_acc.cpu().numpy(), l_full, dt)
+    out2, lse2 = ring.ring_forward(q, kc, vc, segs, starts, live=False)
+    assert torch.equal(lse2, lse_acc) and torch.equal(out2, out_acc)
+
+
+def test_merge_edge_rows():
+    say("[ring] merge edge rows")
+    g = torch.Generator("cpu").manual_seed(7)
+    B, H, L, D = 2, 3, 37, 128
+    oa = torch.randn((B, H, L, D), generator=g)
+    la = torch.randn((B, H, L), generator=g) * 3
+    ob = torch.randn((B, H, L, D), generator=g).to(torch.bfloat16)
+    lb = torch.randn((B, H, L), generator=g) * 3
+    la[0, 0, :5] = float("-inf")
+    oa[0, 0, :5] = 0
+    lb[0, 0, 3:9] = float("-inf")
+    ob[0, 0, 3:9] = 0
+    out_ref, lse_ref = ro.merge(oa.double().numpy(), la.double().numpy(), ob.double().numpy(), lb.double().numpy())
+    oa_d, la_d = oa.to(DEV), la.to(DEV)
+    ring.merge_(oa_d, la_d, ob.to(DEV), lb.to(DEV))
+    assert_close("out", oa_d.cpu().numpy(), out_ref, "f32")
+    assert_close("lse", la_d.cpu().numpy(), lse_ref, "f32")
+    assert not torch.isnan(oa_d).any()
+    assert torch.equal(oa_d[0, 0, 3:5].cpu(), torch.zeros((2, D)))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_finalize_and_grad_add(dt):
+    say(f"[ring] finalize / grad_add {dt}")
+    g = torch.Generator("cpu").manual_seed(11)
+    acc = torch.randn((3, 5, 17, 64), generator=g)
+    out, resid = ring.finalize(acc.to(DEV), DT[dt])
+    assert torch.equal(out.cpu(), acc.to(DT[dt]))
+    want = (acc - acc.to(DT[dt]).float()).to(DT[dt])
+    assert torch.equal(resid.cpu(), want)
+    a = torch.randn((4, 1000), generator=g)
+    s = torch.randn((4, 1000), generator=g).to(DT[dt])
+    a_d = a.to(DEV)
+    ring.grad_add_(a_d, s.to(DEV))
+    assert torch.equal(a_d.cpu(), a + s.float())
+    ring.grad_add_(a_d, s.to(DEV), init=True)
+    assert torch.equal(a_d.cpu(), s.float())
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_chunk_backward_with_global_out(case):
+    seed, B, Hq, Hkv, D, Lc, P, r, lo, hi, pt, dt = case
+    w = World(seed, B, Hq, Hkv, D, Lc, P, lo, hi, pt, dt)
+    say(f"[ring] bwd case seed={seed} D={D} Lc={Lc} rank={r} {dt}")
+    segs = w.segs(r)
+    q, do = w.shard(w.q, r).to(DEV), w.shard(w.do, r).to(DEV)
+    order = [r] + list(range(r - 1, -1, -1))
+    kc = [w.shard(w.k, o).to(DEV) for o in order]
+    vc = [w.shard(w.v, o).to(DEV) for o in order]
+    starts = [o * Lc for o in order]
+    out_acc, lse_acc = ring.ring_forward(q, kc, vc, segs, starts)
+    out, resid = ring.finalize(out_acc, DT[dt])
+    dq, dks, dvs = ring.ring_backward(do, q, kc, vc, out, resid, lse_acc, segs, starts)
+    # the oracle's per-chunk backward on the same global out (fp32-accurate) and lse
+    out_np, lse_np = out_acc.double().cpu().numpy(), lse_acc.double().cpu().numpy()
+    q_ids = w.ids[:, r * Lc:(r + 1) * Lc]
+    dq_ref = np.zeros(q.shape)
+    for c, o in enumerate(order):
+        a, bk, bv = ro.chunk_backward(w.shard(w.q, r), w.shard(w.k, o), w.shard(w.v, o), w.shard(w.do, r), out_np,
+                                      lse_np, q_ids, w.ids[:, o * Lc:(o + 1) * Lc], r * Lc, o * Lc, o == r, w.scale)
+        dq_ref += a
+        assert_close(f"dK owner {o}", dks[c].float().cpu().numpy(), bk, dt)
+        assert_close(f"dV owner {o}", dvs[c].float().cpu().numpy(), bv, dt)
+    assert_close("dQ", dq.cpu().numpy(), dq_ref, dt)
+    # one chunk's contribution stored in the input dtype (no accumulator)
+    dq_own, dk_own, _ = ring.chunk_bwd(do, q, kc[0], vc[0], out, resid, lse_acc, segs, starts[0])
+    a, bk, _ = ro.chunk_backward(w.shard(w.q, r), w.shard(w.k, r), w.shard(w.v, r), w.shard(w.do, r), out_np, lse_np,
+                                 q_ids, q_ids, r * Lc, r * Lc, True, w.scale)
+    assert_close("dQ own chunk", dq_own.float().cpu().numpy(), a, dt)
+    assert torch.equal(dk_own, dks[0])
+    # and against the analytic gradients of one attention over the neighbourhood
+    S = (r + 1) * Lc
+    dq_f, dk_f, dv_f = orc.attention_backward(w.shard(w.q, r), w.k[:, :, :S], w.v[:, :, :S], w.shard(w.do, r),
+                                              w.ids[:, :S], -1, w.scale)
+    assert_close("dQ (neighbourhood)", dq.cpu().numpy(), dq_f, dt)
+    for c, o in enumerate(order):
+        assert_close(f"dK (neighbourhood) owner {o}", dks[c].float().cpu().numpy(), dk_f[:, :, o * Lc:(o + 1) * Lc], dt)
+
+
+def test_rejects_a_later_owner_chunk():
+    from sliding_window_attention_fold_amd import _lib
+    w = World(1, 1, 2, 1, 64, 64, 2, 10, 30, 0, "bf16")
+    segs = w.segs(0)
+    q = w.shard(w.q, 0).to(DEV)
+    k = w.shard(w.k, 1).to(DEV)
+    with pytest.raises(_lib.NbError):
+        ring.chunk_fwd(q, k, k, segs, 64)
