@@ -195,3 +195,65 @@ def test_rejects_a_later_owner_chunk():
     k = w.shard(w.k, 1).to(DEV)
     with pytest.raises(_lib.NbError):
         ring.chunk_fwd(q, k, k, segs, 64)
+
+
+def test_full_size_ring_sampled_rows_and_sum_rules():
+    """The bench workload at its real size (config 2's world as a global layer: rank 3 of 4, chunks of 4096,
+    Hq=16, Hkv=8, D=256, bf16): sampled rows of out, lse and dQ against the oracle, and two rules that hold
+    at any size -- over all chunks and keys, dV sums to the group's dO over its real rows (each real row's
+    probabilities sum to one) and dK sums to zero (each real row's dS sums to zero)."""
+    from sliding_window_attention_fold_amd import workloads as wl
+    w = wl.get(2)
+    r, Lc, D = w.cp_rank, w.L, w.D
+    S = (r + 1) * Lc
+    glob, pad = wl.global_doc_map(w)
+    ids = glob[:, :S].astype(np.int32)
+    if pad is not None:
+        ids[pad[:, :S] != 0] = 0
+    q, k, v, do = wl.make_tensors(w, S, "bf16")
+    say(f"[ring] full size: Lc={Lc} chunks={r + 1} Hq={w.Hq} D={D}")
+    segs = ring.ring_segments(torch.from_numpy(ids).to(DEV), r * Lc, Lc)
+    order = [r] + list(range(r - 1, -1, -1))
+    kc = [k[:, :, o * Lc:(o + 1) * Lc].contiguous().to(DEV) for o in order]
+    vc = [v[:, :, o * Lc:(o + 1) * Lc].contiguous().to(DEV) for o in order]
+    starts = [o * Lc for o in order]
+    qd, dod = q.to(DEV), do.to(DEV)
+    out_acc, lse_acc = ring.ring_forward(qd, kc, vc, segs, starts)
+    out, resid = ring.finalize(out_acc, torch.bfloat16)
+    dq, dks, dvs = ring.ring_backward(dod, qd, kc, vc, out, resid, lse_acc, segs, starts)
+    torch.cuda.synchronize()
+    scale = D ** -0.5
+    q0 = r * Lc
+    heads = [0, 1, w.Hq - 1]
+    grp = w.Hq // w.Hkv
+    out_np, lse_np = out_acc.double().cpu().numpy(), lse_acc.double().cpu().numpy()
+    for i0 in (0, 2000, Lc - 64):
+        rows = slice(i0, i0 + 64)
+        q_ids = ids[:, q0 + i0:q0 + i0 + 64]
+        for h in heads:
+            qs, ds = q[:, h:h + 1, rows], do[:, h:h + 1, rows]
+            kvh = h // grp
+            acc = lacc = None
+            dq_ref = 0.0
+            for o in order:
+                kk, vv = k[:, kvh:kvh + 1, o * Lc:(o + 1) * Lc], v[:, kvh:kvh + 1, o * Lc:(o + 1) * Lc]
+                so, sl = ro.chunk_forward(qs, kk, vv, q_ids, ids[:, o * Lc:(o + 1) * Lc], q0 + i0, o * Lc, o == r,
+                                          scale)
+                acc, lacc = ro.merge(acc, lacc, so, sl)
+            for o in order:
+                kk, vv = k[:, kvh:kvh + 1, o * Lc:(o + 1) * Lc], v[:, kvh:kvh + 1, o * Lc:(o + 1) * Lc]
+                a, _, _ = ro.chunk_backward(qs, kk, vv, ds, out_np[:, h:h + 1, rows], lse_np[:, h:h + 1, rows], q_ids,
+                                            ids[:, o * Lc:(o + 1) * Lc], q0 + i0, o * Lc, o == r, scale)
+                dq_ref = dq_ref + a
+            assert_close(f"out rows {i0}+ head {h}", out_np[:, h:h + 1, rows], acc, "bf16")
+            assert_close(f"lse rows {i0}+ head {h}", lse_np[:, h:h + 1, rows], lacc, "bf16")
+            assert_close(f"dQ rows {i0}+ head {h}", dq[:, h:h + 1, rows].cpu().numpy(), dq_ref, "bf16")
+    real = torch.from_numpy(ids[:, q0:q0 + Lc] > 0)
+    dv_sum = sum(t.double().sum(dim=2) for t in dvs).cpu()                    # [B, Hkv, D]
+    dk_sum = sum(t.double().sum(dim=2) for t in dks).cpu()
+    do_real = (do.double() * real[:, None, :, None]).sum(dim=2)               # [B, Hq, D]
+    want = do_real.view(w.B, w.Hkv, grp, D).sum(dim=2)
+    scale_dv = want.abs().max().item()
+    assert torch.allclose(dv_sum, want, atol=2e-2 * scale_dv, rtol=0), (dv_sum - want).abs().max()
+    dk_scale = sum(t.double().abs().sum(dim=2) for t in dks).cpu().max().item()
+    assert dk_sum.abs().max().item() <= 2e-2 * dk_scale
