@@ -578,6 +578,7 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
     }
   }
   const int nt = kstart < kend ? (kend - kstart + C::BN - 1) / C::BN : 0;   // key tiles of the item
+  if (nt == 0 && p.dq_mode == kDqAddF32) return;   // uniform: no key, nothing to add
   auto load = [&](int slot, int n) {
     const int j0 = kstart + n * C::BN;
     if constexpr (KV == kKvAny) {
