@@ -194,7 +194,7 @@ def main() -> int:
     dq = torch.empty_like(qd)
     dk = torch.empty_like(kd)
     dv = torch.empty_like(vd)
-    ws_bytes = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, _lib.NB_BF16)
+    ws_bytes = lib.nb_attn_bwd_workspace_bytes_window(B, Hq, Hkv, L, S, D, _lib.NB_BF16, W)
     ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
     n_owner = len(dm.owner_off) - 1
     attended = torch.empty((n_owner,), dtype=torch.uint8, device=dev)

@@ -153,10 +153,19 @@ int nb_attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_re
                 void* stream);
 
 /* Bytes of workspace nb_attn_bwd needs: the Delta rows (B * Hq * L floats),
- * then the work orders of the two passes and the backward kernel's work-queue
- * counters (B * ceil(S / 32) + 8 + B * ceil(L / 32) ints), each part 256-byte
- * aligned. */
+ * then the work orders of the two passes, the backward kernel's counters and
+ * the list of deferred dQ items (B * ceil(S / 32) + 10 + B * ceil(L / 32) +
+ * B * Hq * ceil(L / 32) ints), each part 256-byte aligned. */
 size_t nb_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, int dtype);
+
+/* The same plus, with a left window 0 <= window_left <= 4096, a banded dS
+ * buffer (B * Hq * L rows of round_up(window_left + 96, 32) elements of
+ * dtype).  Given a workspace of this size, nb_attn_bwd and nb_attn_bwd_main on
+ * a windowed neighbourhood have the dK/dV pass store dS and form dQ = dS K
+ * from it instead of recomputing S and dP (dK, dV unchanged bit for bit; dQ
+ * within the usual tolerance).  Equal to nb_attn_bwd_workspace_bytes without a
+ * window. */
+size_t nb_attn_bwd_workspace_bytes_window(int B, int Hq, int Hkv, int L, int S, int D, int dtype, int window_left);
 
 /*
  * Backward with no forward recompute: dQ and dK/dV from the saved O and LSE.

@@ -187,8 +187,12 @@ def attn_fwd(q: torch.Tensor, k_nb: torch.Tensor, v_nb: torch.Tensor, seg: Segme
     return out, Saved(q, k_nb, v_nb, out, resid, lse, seg, scale)
 
 
-def attn_bwd(saved: Saved, grad_out: torch.Tensor, owners: Optional[OwnerTable] = None) -> BwdResult:
-    """Backward from the saved forward (no recompute).
+def attn_bwd(saved: Saved, grad_out: torch.Tensor, owners: Optional[OwnerTable] = None,
+             stored_ds: bool = True) -> BwdResult:
+    """Backward from the saved forward (no recompute).  ``stored_ds``: with a
+    left window, give the library room to store dS and form dQ from it (the
+    faster form; dK/dV identical, dQ equal up to rounding order); ``False``
+    keeps the dQ pass that recomputes S and dP.
 
     Returns ``BwdResult(dq, dk_by_owner, dv_by_owner, attended, dk, dv)``; the
     per-owner entries are views of ``dk``/``dv`` (exact zeros for owners that were
@@ -207,7 +211,9 @@ def attn_bwd(saved: Saved, grad_out: torch.Tensor, owners: Optional[OwnerTable] 
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     att = torch.empty((max(n_owner, 1),), dtype=torch.uint8, device=q.device)
-    ws_bytes = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, _DTYPES[q.dtype])
+    # with a window, room for the banded dS (the backward then forms dQ from it)
+    ws_bytes = (lib.nb_attn_bwd_workspace_bytes_window(B, Hq, Hkv, L, S, D, _DTYPES[q.dtype], seg.window)
+                if stored_ds else lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, _DTYPES[q.dtype]))
     ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=q.device)
     off_c = (ctypes.c_int32 * len(off))(*off)
     _lib.check(lib.nb_attn_bwd(_ptr(grad_out), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(resid), _ptr(lse),

@@ -116,7 +116,9 @@ using DkvSmem = typename std::conditional<DkvCfg<T, D>::SKEW, DkvSmemMetaFirst<T
 // One dK/dV item f: (kv head, batch row, key tile) with the kv head fastest
 // and the (batch row, key tile) pairs in the order of decreasing work
 // (work_order_kernel), so the long tiles start first.
-template <typename T, int D, bool CH>
+// DS: the item may store dS (p.dsbuf non-null); compiled into the dK/dV-only
+// kernel alone, so the combined kernel carries none of its registers.
+template <typename T, int D, bool CH, bool DS>
 __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm, int f) {
   typedef DkvCfg<T, D> C;
   typedef Tile<T, C::BQ, D> TL;
@@ -307,6 +309,41 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
       for (int e = 0; e < 4; ++e) sacc[4 * qd + e] = pq[e] * (sacc[4 * qd + e] - d4[e]);
     }
   };
+  // role B: step it's dS (this lane's key j, rows acc_row(r, g)) into the
+  // banded buffer, when there is one (the dQ pass then reads it).  The buffer
+  // is 32-row x 32-key blocks (row-major, 32 * 32 elements each): a lane's 16
+  // values go through one buffer resource, a scalar block offset, one lane
+  // offset for the whole item and a constant offset per row.
+  const int ds_nb = p.ds_w >> 5;                      // blocks per 32-row tile
+  const int ds_ntq = (p.L + 31) >> 5;                 // 32-row tiles per head
+  const int ds_lane = (ln + 4 * g * 32) * (int)sizeof(T);
+  auto store_ds = [&](const f32x16& ds, int it, const int* ks) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int hh = it / n_t, tq = t_first + it % n_t, i0 = tq * C::BQ;
+    int bs0 = max(0, ks[0] - kor);
+    if (p.window >= 0) bs0 = max(bs0, off + i0 - p.window);
+    bs0 = __builtin_amdgcn_readfirstlane(bs0);
+    const int blk = ((b * p.Hq + kvh * grp + hh) * ds_ntq + tq) * ds_nb + ((jw - (bs0 & ~31)) >> 5);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(p.dsbuf, (short)0, p.ds_bytes, kBufferWord3);
+    const int nrows = p.L - i0;
+    if (j < p.S) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (acc_row(r, g) < nrows) {
+          const int voff = ds_lane + (8 * (r >> 2) + (r & 3)) * 32 * (int)sizeof(T);
+          if constexpr (sizeof(T) == 2) {
+            const bf16 v = to_elem<bf16>(ds[r]);
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), rs, voff,
+                                                      blk * 32 * 32 * 2, 0);
+          } else {
+            const float v = ds[r];
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, voff, blk * 32 * 32 * 4, 0);
+          }
+        }
+      }
+    }
+#endif
+  };
   // gacc += src^T (P or dS): dV^T = dO^T P (role A) or dK^T = Q^T dS (role B)
   auto accumulate = [&](const T* src, const f32x16& sacc) {
     if constexpr (C::AHEAD > 0) {
@@ -362,6 +399,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
           const int xp = x == 0 ? NS - 1 : x - 1;
           if (act_prev) {
             to_ds(dp, pex[(t - 1) & 1], sm.dl[xp]);
+            if (DS && p.dsbuf) store_ds(dp, t - 1, sm.klo[xp]);
             accumulate(sm.Q[xp], dp);
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -402,7 +440,10 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
       __syncthreads();   // the hand-over
       if (it + 2 < n_iter) load_slot((x + 2) % NS, it + 2);
       if (si.active) {
-        if (!role_a) to_ds(sacc, px, sm.dl[x]);
+        if (!role_a) {
+          to_ds(sacc, px, sm.dl[x]);
+          if (DS && p.dsbuf) store_ds(sacc, it, sm.klo[x]);
+        }
         accumulate(role_a ? sm.G[x] : sm.Q[x], sacc);
       }
     };
@@ -430,7 +471,10 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
       }
       __syncthreads();   // the hand-over
       if (si.active) {
-        if (!role_a) to_ds(sacc, pex[0], sm.dl[x]);
+        if (!role_a) {
+          to_ds(sacc, pex[0], sm.dl[x]);
+          if (DS && p.dsbuf) store_ds(sacc, it, sm.klo[x]);
+        }
         accumulate(role_a ? sm.G[x] : sm.Q[x], sacc);
       }
     };
@@ -738,6 +782,159 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
 }
 
 
+// ---------------------------------------------------------------- dQ from stored dS
+
+// dQ = scale * dS K from the banded dS the dK/dV items stored (windowed
+// neighbourhoods), with no recompute of S or dP.  One workgroup per (128 query
+// rows, q head, batch row), four waves of 32 rows; the work is the forward's
+// P V half: K tiles copied into LDS asynchronously and read transposed as the A
+// operand of dQ^T = K^T dS^T, the B operand (dS^T, this lane's query row) read
+// from the buffer in the accumulator order the forward feeds P^T in.  A wave
+// reads the same 32-key blocks the dK/dV items wrote for its 32-row tile: from
+// the first row's band start rounded down to 32 up to the last row's position.
+template <typename T, int D>
+struct DqsCfg {
+  static constexpr int NW = 4;
+  static constexpr int NT = 64 * NW;
+  static constexpr int BM = 32 * NW;
+  static constexpr int BN = (D <= 128) ? 64 : 32;   // keys per tile
+  static constexpr int AHEAD = (D <= 128) ? 3 : 2;   // as the forward's P V half
+  static constexpr int OCC = (sizeof(T) == 2) ? 2 : 1;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, (DqsCfg<T, D>::OCC)) void dq_ds_kernel(BwdParams p) {
+  typedef DqsCfg<T, D> C;
+  typedef Tile<T, C::BN, D> TL;
+  typedef typename Frag<T>::type F;
+  typedef typename Quad<T>::type Q4;
+  __shared__ __attribute__((aligned(1024))) T K0[TL::ELEMS];
+  __shared__ __attribute__((aligned(1024))) T K1[TL::ELEMS];
+  __shared__ int red[C::NW][2];
+  const int grp = p.Hq / p.Hkv;
+  const int ngroups = p.B * p.Hkv;
+  const int gid = blockIdx.x % ngroups, rest = blockIdx.x / ngroups;
+  const int b = gid / p.Hkv, kvh = gid % p.Hkv;
+  const int h = kvh * grp + rest % grp, qt = rest / grp;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
+  const int i0 = qt * C::BM + 32 * w;   // this wave's 32-row tile
+  const int i = i0 + ln;
+  const bool in_range = i < p.L;
+  int kb = INT_MAX, ke = INT_MIN;       // the tile's blocks: keys kb .. ke (kb a multiple of 32)
+  if (i0 < p.L) {
+    int bs0 = max(0, p.row_klo[(size_t)b * p.L + i0] - p.k_origin);
+    if (p.window >= 0) bs0 = max(bs0, p.q_off + i0 - p.window);
+    kb = bs0 & ~31;
+    ke = min(p.q_off + min(i0 + 31, p.L - 1), p.S - 1);
+  }
+  kb = __builtin_amdgcn_readfirstlane(kb);
+  ke = __builtin_amdgcn_readfirstlane(ke);
+  const bool w_any = kb <= ke;
+  if (lane == 0) { red[w][0] = w_any ? kb : INT_MAX; red[w][1] = w_any ? ke + 1 : INT_MIN; }
+  __syncthreads();
+  int kstart = INT_MAX, kend = INT_MIN;
+#pragma unroll
+  for (int x = 0; x < C::NW; ++x) { kstart = min(kstart, red[x][0]); kend = max(kend, red[x][1]); }
+  kstart = __builtin_amdgcn_readfirstlane(kstart);
+  kend = __builtin_amdgcn_readfirstlane(kend);
+
+  const int bh = b * p.Hkv + kvh;
+  const T* __restrict__ kbase = reinterpret_cast<const T*>(p.kv.k[0]) + (size_t)bh * p.S * D;
+  // this lane's row in the tile's 32 x 32 dS blocks (see the dK/dV item's store)
+  const int ds_nb = p.ds_w >> 5, ds_ntq = (p.L + 31) >> 5;
+  const T* __restrict__ drow = reinterpret_cast<const T*>(p.dsbuf) +
+                               ((size_t)(b * p.Hq + h) * ds_ntq + min(i0, p.L - 1) / 32) * ds_nb * 1024 + ln * 32;
+  const TileDma<T, C::BN, D, C::NW> dma;
+  const TileAccess<T, TL> acc(ln, lane);
+  auto load = [&](T* Ks, int j0) { dma.issue(Ks, kbase + (size_t)j0 * D, min(C::BN, p.S - j0)); };
+  // the B-operand fragments of one tile (zeros outside the wave's blocks, for
+  // keys past S and for rows past L)
+  constexpr int NM = C::BN / 16;
+  auto ds_frags = [&](F* fr, int j0) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int jw = j0 + 32 * (m >> 1);
+      fr[m] = F{};
+      if (jw >= kb && jw <= ke && in_range) {
+        const int c = ((jw - kb) >> 5) * 1024 + 16 * (m & 1) + 4 * g;
+        const Q4 x = *reinterpret_cast<const Q4*>(drow + c);
+        const Q4 y = *reinterpret_cast<const Q4*>(drow + c + 8);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          fr[m][t] = x[t];
+          fr[m][4 + t] = y[t];
+        }
+        if (jw + 32 > p.S) {   // keys past the neighbourhood were never written
+          const int k0 = jw + 16 * (m & 1) + 4 * g;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if (k0 + t >= p.S) fr[m][t] = to_elem<T>(0.f);
+            if (k0 + 8 + t >= p.S) fr[m][4 + t] = to_elem<T>(0.f);
+          }
+        }
+      }
+    }
+  };
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) oacc[d] = f32x16{};
+  constexpr int ND = D / 32;
+  auto compute = [&](const T* Ks, const F* fr, int j0) __attribute__((always_inline)) {
+    if (!w_any || j0 > ke || j0 + C::BN <= kb) return;
+    lds_mfma_pipeline<NM * ND, C::AHEAD, F>(
+        [&](int x) { return acc.col(Ks, x % ND, x / ND); },
+        [&](int x, const F& a) { oacc[x % ND] = mma(a, fr[x / ND], oacc[x % ND]); });
+  };
+  F f0[NM], f1[NM];
+  if (kstart < kend) {
+    load(K0, kstart);
+    ds_frags(f0, kstart);
+  }
+  for (int j0 = kstart; j0 < kend; j0 += 2 * C::BN) {
+    wait_global();
+    __syncthreads();
+    if (j0 + C::BN < kend) {
+      load(K1, j0 + C::BN);
+      ds_frags(f1, j0 + C::BN);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(K0, f0, j0);
+    if (j0 + C::BN >= kend) break;
+    wait_global();
+    __syncthreads();
+    if (j0 + 2 * C::BN < kend) {
+      load(K0, j0 + 2 * C::BN);
+      ds_frags(f0, j0 + 2 * C::BN);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(K1, f1, j0 + C::BN);
+  }
+
+  if (!in_range) return;
+  const size_t qrow = ((size_t)b * p.Hq + h) * p.L + i;
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) {
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int dd = 32 * d + 8 * rq + 4 * g;
+      const float v0 = oacc[d][4 * rq] * p.scale, v1 = oacc[d][4 * rq + 1] * p.scale;
+      const float v2 = oacc[d][4 * rq + 2] * p.scale, v3 = oacc[d][4 * rq + 3] * p.scale;
+      if (p.dq_mode == kDqStore) {
+        store_quad<T>(reinterpret_cast<T*>(p.dq) + qrow * D + dd, v0, v1, v2, v3);
+      } else {
+        f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.dq) + qrow * D + dd);
+        f32x4 x = f32x4{v0, v1, v2, v3};
+        if (p.dq_mode == kDqAddF32) {
+          const f32x4 a = *dst;
+          x = f32x4{a[0] + x[0], a[1] + x[1], a[2] + x[2], a[3] + x[3]};
+        }
+        *dst = x;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- Delta
 
 // Delta_i = dO_i . O_i for every row (b, h, i), with O the stored value plus
@@ -924,7 +1121,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void b
     DkvSmem<T, D> kv;
     DqSmem<T, D> q;
   } sm;
-  auto dkdv = [&](int f) { dkdv_item<T, D, KV != kKvConcat>(p, sm.kv, f); };
+  auto dkdv = [&](int f) { dkdv_item<T, D, KV != kKvConcat, MODE == 1>(p, sm.kv, f); };
   const int n_kv = (MODE & 1) ? p.B * ((p.S + DkvCfg<T, D>::BK - 1) / DkvCfg<T, D>::BK) * p.Hkv : 0;
   const int n_q = (MODE & 2) ? p.B * ((p.L + DqCfg<T, D>::BM - 1) / DqCfg<T, D>::BM) * p.Hq : 0;
   const int total = n_kv + n_q;
@@ -1006,6 +1203,18 @@ static hipError_t launch_main_t(const BwdParams& p, hipStream_t s) {
       if (e != hipSuccess || !kv_may_need_general(p.kv, p.window, DqCfg<T, D>::BM, DqCfg<T, D>::BN)) return e;
       dim3 grid2((unsigned)std::min<long long>(n_q, (long long)device_cu_count() * BwdShape<T, D>::OCC));
       hipLaunchKernelGGL((bwd_dq_cross_kernel<T, D>), grid2, dim3(BwdShape<T, D>::NT), 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (MODE == 3) {
+    if (p.dsbuf != nullptr) {   // dK/dV items storing dS, then dQ = dS K
+      const long long n_kv1 = (long long)p.B * ((p.S + DkvCfg<T, D>::BK - 1) / DkvCfg<T, D>::BK) * p.Hkv;
+      dim3 grid1((unsigned)std::min<long long>(n_kv1, (long long)device_cu_count() * BwdShape<T, D>::OCC));
+      hipLaunchKernelGGL((bwd_kernel<T, D, 1, kKvConcat>), grid1, dim3(BwdShape<T, D>::NT), 0, s, p);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      dim3 grid2((unsigned)((p.L + DqsCfg<T, D>::BM - 1) / DqsCfg<T, D>::BM) * p.Hq * p.B);
+      hipLaunchKernelGGL((dq_ds_kernel<T, D>), grid2, dim3(DqsCfg<T, D>::NT), 0, s, p);
       return hipGetLastError();
     }
   }

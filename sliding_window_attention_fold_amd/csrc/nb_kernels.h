@@ -97,6 +97,14 @@ struct BwdParams {
   int B, Hq, Hkv, L, S, window;
   int q_off, k_origin;   // as in FwdParams
   int dq_mode;       // kDqStore: dq is T, written; kDqSetF32 / kDqAddF32: dq is fp32, set / added to
+  // Optional banded dS (windowed neighbourhoods): per (batch row, q head,
+  // 32-row query tile) ds_w / 32 blocks of 32 rows x 32 keys (row-major T), the
+  // tile's keys from its first row's band start rounded down to 32.  Non-null:
+  // the dK/dV items store dS there and dQ = dS K runs as a separate pass
+  // instead of the dQ items.
+  void* dsbuf;
+  int ds_w;
+  int ds_bytes;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
 };

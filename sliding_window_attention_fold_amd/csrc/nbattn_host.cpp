@@ -239,6 +239,38 @@ size_t nb_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, 
 }  // extern "C"
 
 namespace {
+// The banded dS of the windowed backward: row width (keys) and bytes; 0 when
+// the window is absent or too wide for the buffer to pay.
+constexpr int kMaxDsWindow = 4096;
+int ds_width(int window) { return (window + 96 + 31) / 32 * 32; }
+size_t ds_bytes(int B, int Hq, int L, int window, int dtype) {
+  if (window < 0 || window > kMaxDsWindow || B < 1 || Hq < 1 || L < 1) return 0;
+  const size_t n = ((size_t)B * Hq * ((L + 31) / 32 * 32) * ds_width(window) * (dtype == NB_F32 ? 4 : 2) + 255) &
+                   ~(size_t)255;
+  return n < ((size_t)1 << 31) ? n : 0;   // buffer offsets stay in 31 bits
+}
+// Turns the stored-dS backward on when the workspace holds the buffer.
+void enable_ds(nb::BwdParams& p, void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int L, int S, int D,
+               int window_left, int dtype) {
+  const size_t base = nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype);
+  const size_t db = ds_bytes(B, Hq, L, window_left, dtype);
+  if (db == 0 || ws_bytes < base + db) return;
+  p.dsbuf = reinterpret_cast<char*>(ws) + base;
+  p.ds_w = ds_width(window_left);
+  p.ds_bytes = (int)db;
+}
+}  // namespace
+
+extern "C" {
+
+size_t nb_attn_bwd_workspace_bytes_window(int B, int Hq, int Hkv, int L, int S, int D, int dtype, int window_left) {
+  const size_t base = nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype);
+  return base == 0 ? 0 : base + ds_bytes(B, Hq, L, window_left, dtype);
+}
+
+}  // extern "C"
+
+namespace {
 
 nb::BwdParams bwd_params(const void* dout, const void* q, const nb::KvChunks& kv, const void* o,
                          const void* o_resid, const float* lse, const int32_t* seg_buf, int B, int Hq, int Hkv,
@@ -267,6 +299,9 @@ nb::BwdParams bwd_params(const void* dout, const void* q, const nb::KvChunks& kv
   p.q_off = q_off < 0 ? S - L : q_off;
   p.k_origin = k_origin;
   p.dq_mode = nb::kDqStore;
+  p.dsbuf = nullptr;
+  p.ds_w = 0;
+  p.ds_bytes = 0;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   return p;
@@ -350,8 +385,9 @@ int nb_attn_bwd_main(const void* dout, const void* q, const void* k, const void*
   int st = attn_common_checks(ptrs, 10, B, Hq, Hkv, L, S, D, scale, dtype);
   if (st != NB_OK) return st;
   if (ws_bytes < nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype)) return NB_ERR_WORKSPACE;
-  const nb::BwdParams p = bwd_params(dout, q, one_chunk(S, k, v, dk, dv), nullptr, nullptr, lse, seg_buf, B, Hq,
-                                     Hkv, L, S, scale, window_left, dq, ws);
+  nb::BwdParams p = bwd_params(dout, q, one_chunk(S, k, v, dk, dv), nullptr, nullptr, lse, seg_buf, B, Hq, Hkv, L,
+                               S, scale, window_left, dq, ws);
+  enable_ds(p, ws, ws_bytes, B, Hq, Hkv, L, S, D, window_left, dtype);
   return map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdMain, (hipStream_t)stream));
 }
 
@@ -409,8 +445,9 @@ int nb_attn_bwd(const void* dout, const void* q, const void* k, const void* v, c
   st = owner_checks(folded_ids, S, owner_off, n_owner, owner_attended);
   if (st != NB_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  const nb::BwdParams p = bwd_params(dout, q, one_chunk(S, k, v, dk, dv), o, o_resid, lse, seg_buf, B, Hq, Hkv, L,
-                                     S, scale, window_left, dq, ws);
+  nb::BwdParams p = bwd_params(dout, q, one_chunk(S, k, v, dk, dv), o, o_resid, lse, seg_buf, B, Hq, Hkv, L, S,
+                               scale, window_left, dq, ws);
+  enable_ds(p, ws, ws_bytes, B, Hq, Hkv, L, S, D, window_left, dtype);
   st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdPrep, s));
   if (st != NB_OK) return st;
   st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdMain, s));

@@ -73,7 +73,7 @@ def test_chunks_match_concatenated_bitwise(case):
     out, saved = nb.attn_fwd(q, k, v, seg)
     offs = np.concatenate([[0], np.cumsum(lens)]).tolist()
     owners = nb.OwnerTable(offs, list(range(len(lens))))
-    ref = nb.attn_bwd(saved, do, owners)
+    ref = nb.attn_bwd(saved, do, owners, stored_ds=False)   # the chunk path's dQ pass recomputes S and dP too
     # the same keys embedded at random rows of larger chunk buffers
     chunks = []
     for c, n in enumerate(lens):

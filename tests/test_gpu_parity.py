@@ -160,7 +160,11 @@ def test_deterministic_bitwise():
 @pytest.mark.parametrize("name", ["w2s", "w5s"])
 def test_backward_entry_points_agree(name):
     """nb_attn_bwd, prep + main, and dq + dkdv called separately (twice, so a
-    reused workspace is covered) give bit-identical dQ, dK, dV."""
+    reused workspace is covered) give bit-identical dQ, dK, dV on the plain
+    workspace; with the windowed workspace (stored dS, dQ = dS K) nb_attn_bwd
+    and prep + main agree bit for bit, dK and dV equal the plain path's bit for
+    bit and dQ agrees within the bf16 tolerance (the stored path rounds the
+    same dS to bf16, from S and dP accumulated in another order)."""
     import ctypes
 
     w = SMALL[name]
@@ -175,30 +179,56 @@ def test_backward_entry_points_agree(name):
     Hkv, S = k.shape[1], k.shape[2]
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
     sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    wsb = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, _lib.NB_BF16)
-    ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
     sc = D ** -0.5
     W = inp.window
-    for rep in range(2):
-        dq = torch.full_like(q, float("nan"))
-        dk = torch.full_like(k, float("nan"))
-        dv = torch.full_like(v, float("nan"))
+    wsb_plain = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, _lib.NB_BF16)
+    wsb_win = lib.nb_attn_bwd_workspace_bytes_window(B, Hq, Hkv, L, S, D, _lib.NB_BF16, W)
+    assert (wsb_win > wsb_plain) == (W >= 0)
+    off_c = (ctypes.c_int32 * 2)(0, S)
+    att = torch.empty((1,), dtype=torch.uint8, device=dev)
+
+    def full(wsb):
+        ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
+        g = [torch.full_like(t, float("nan")) for t in (q, k, v)]
+        _lib.check(lib.nb_attn_bwd(P(do), P(q), P(k), P(v), P(saved.out), P(saved.out_resid), P(saved.lse),
+                                   P(seg.buf), P(seg.folded), B, Hq, Hkv, L, S, D, sc, W, _lib.NB_BF16, P(g[0]),
+                                   P(g[1]), P(g[2]), ctypes.cast(off_c, ctypes.c_void_p), 1, P(att), P(ws), wsb, sp),
+                   "nb_attn_bwd")
+        return g
+
+    def prep_main(wsb, ws):
+        g = [torch.full_like(t, float("nan")) for t in (q, k, v)]
         _lib.check(lib.nb_attn_bwd_prep(P(do), P(saved.out), P(saved.out_resid), P(seg.buf), B, Hq, Hkv, L, S, D, W,
                                         _lib.NB_BF16, P(ws), wsb, sp), "prep")
         _lib.check(lib.nb_attn_bwd_main(P(do), P(q), P(k), P(v), P(saved.lse), P(seg.buf), B, Hq, Hkv, L, S, D, sc,
-                                        W, _lib.NB_BF16, P(dq), P(dk), P(dv), P(ws), wsb, sp), "main")
+                                        W, _lib.NB_BF16, P(g[0]), P(g[1]), P(g[2]), P(ws), wsb, sp), "main")
+        return g
+
+    plain = full(wsb_plain)
+    win = full(wsb_win)
+    for x, y in zip(win, (res.dq, res.dk, res.dv)):      # the Python binding takes the windowed workspace
+        assert torch.equal(x, y)
+    assert torch.equal(win[1], plain[1]) and torch.equal(win[2], plain[2])
+    assert_close("dQ stored-dS vs recompute", win[0].float().cpu().numpy(), plain[0].float().cpu().numpy(), "bf16")
+    ws_p = torch.empty((wsb_plain,), dtype=torch.uint8, device=dev)
+    ws_w = torch.empty((wsb_win,), dtype=torch.uint8, device=dev)
+    for rep in range(2):
+        a = prep_main(wsb_plain, ws_p)
+        bw = prep_main(wsb_win, ws_w)
         torch.cuda.synchronize()
-        assert torch.equal(dq, res.dq) and torch.equal(dk, res.dk) and torch.equal(dv, res.dv), f"prep+main {rep}"
+        assert all(torch.equal(x, y) for x, y in zip(a, plain)), f"prep+main plain {rep}"
+        assert all(torch.equal(x, y) for x, y in zip(bw, win)), f"prep+main windowed {rep}"
         dq2 = torch.full_like(q, float("nan"))
         dk2 = torch.full_like(k, float("nan"))
         dv2 = torch.full_like(v, float("nan"))
         _lib.check(lib.nb_attn_bwd_dq(P(do), P(q), P(k), P(v), P(saved.out), P(saved.out_resid), P(saved.lse),
-                                      P(seg.buf), B, Hq, Hkv, L, S, D, sc, W, _lib.NB_BF16, P(dq2), P(ws), wsb, sp),
-                   "dq")
+                                      P(seg.buf), B, Hq, Hkv, L, S, D, sc, W, _lib.NB_BF16, P(dq2), P(ws_p), wsb_plain,
+                                      sp), "dq")
         _lib.check(lib.nb_attn_bwd_dkdv(P(do), P(q), P(k), P(v), P(saved.lse), P(seg.buf), B, Hq, Hkv, L, S, D, sc,
-                                        W, _lib.NB_BF16, P(dk2), P(dv2), P(ws), wsb, sp), "dkdv")
+                                        W, _lib.NB_BF16, P(dk2), P(dv2), P(ws_p), wsb_plain, sp), "dkdv")
         torch.cuda.synchronize()
-        assert torch.equal(dq2, res.dq) and torch.equal(dk2, res.dk) and torch.equal(dv2, res.dv), f"dq+dkdv {rep}"
+        assert torch.equal(dq2, plain[0]) and torch.equal(dk2, plain[1]) and torch.equal(dv2, plain[2]), \
+            f"dq+dkdv {rep}"
 
 
 def test_autograd_function_matches_direct_calls():
