@@ -797,7 +797,7 @@ struct DqsCfg {
   static constexpr int NW = 4;
   static constexpr int NT = 64 * NW;
   static constexpr int BM = 32 * NW;
-  static constexpr int BN = (D <= 128) ? 64 : 32;   // keys per tile
+  static constexpr int BN = 64;   // keys per tile (no Q fragments to hold: room for 64 at D = 256)
   static constexpr int AHEAD = (D <= 128) ? 3 : 2;   // as the forward's P V half
   static constexpr int OCC = (sizeof(T) == 2) ? 2 : 1;
 };

@@ -376,24 +376,22 @@ __device__ __forceinline__ void wait_global() { __builtin_amdgcn_s_waitcnt(0x0F7
 // this wave's vector-memory operations are outstanding.  They complete in
 // issue order, so this waits for everything but the n most recent.
 __device__ __forceinline__ void wait_global_le(int n) {
+  // vmcnt is bits 3:0 and 15:14 of the operand; expcnt and lgkmcnt left at their maxima
+#define NB_VMCNT(c) __builtin_amdgcn_s_waitcnt(0x0F70 | ((c) & 15) | (((c) >> 4) << 14))
   switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
-    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
-    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
-    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
-    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
-    case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
+    case 0: NB_VMCNT(0); break;    case 1: NB_VMCNT(1); break;    case 2: NB_VMCNT(2); break;
+    case 3: NB_VMCNT(3); break;    case 4: NB_VMCNT(4); break;    case 5: NB_VMCNT(5); break;
+    case 6: NB_VMCNT(6); break;    case 7: NB_VMCNT(7); break;    case 8: NB_VMCNT(8); break;
+    case 9: NB_VMCNT(9); break;    case 10: NB_VMCNT(10); break;  case 11: NB_VMCNT(11); break;
+    case 12: NB_VMCNT(12); break;  case 13: NB_VMCNT(13); break;  case 14: NB_VMCNT(14); break;
+    case 15: NB_VMCNT(15); break;  case 16: NB_VMCNT(16); break;  case 17: NB_VMCNT(17); break;
+    case 18: NB_VMCNT(18); break;  case 19: NB_VMCNT(19); break;  case 20: NB_VMCNT(20); break;
+    case 21: NB_VMCNT(21); break;  case 22: NB_VMCNT(22); break;  case 23: NB_VMCNT(23); break;
+    case 24: NB_VMCNT(24); break;  case 25: NB_VMCNT(25); break;  case 26: NB_VMCNT(26); break;
+    case 27: NB_VMCNT(27); break;  case 28: NB_VMCNT(28); break;  case 29: NB_VMCNT(29); break;
+    case 30: NB_VMCNT(30); break;  default: NB_VMCNT(31); break;
   }
+#undef NB_VMCNT
 }
 
 // Precomputed readers for bf16 tiles.  The XOR swizzle only touches the low 4
