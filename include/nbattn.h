@@ -158,9 +158,9 @@ int nb_attn_fwd(const void* q, const void* k, const void* v, void* o, void* o_re
  * B * Hq * ceil(L / 32) ints), each part 256-byte aligned. */
 size_t nb_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, int dtype);
 
-/* The same plus, with a left window 0 <= window_left <= 4096, a banded dS
- * buffer (B * Hq * L rows of round_up(window_left + 96, 32) elements of
- * dtype).  Given a workspace of this size, nb_attn_bwd and nb_attn_bwd_main on
+/* The same plus, with a left window 0 <= window_left <= 4096 and D = 256, a
+ * banded dS buffer (B * Hq * round_up(L, 32) rows of round_up(window_left + 96,
+ * 32) elements of dtype; at most 2 GiB, else none).  Given a workspace of this size, nb_attn_bwd and nb_attn_bwd_main on
  * a windowed neighbourhood have the dK/dV pass store dS and form dQ = dS K
  * from it instead of recomputing S and dP (dK, dV unchanged bit for bit; dQ
  * within the usual tolerance).  Equal to nb_attn_bwd_workspace_bytes without a

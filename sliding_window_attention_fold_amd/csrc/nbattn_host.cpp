@@ -240,11 +240,13 @@ size_t nb_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, 
 
 namespace {
 // The banded dS of the windowed backward: row width (keys) and bytes; 0 when
-// the window is absent or too wide for the buffer to pay.
+// the window is absent or too wide for the buffer to pay, or at head dims
+// below 256, where the dQ items that recompute S and dP measured faster (their
+// dK/dV steps have no spare registers for the stores' bookkeeping there either).
 constexpr int kMaxDsWindow = 4096;
 int ds_width(int window) { return (window + 96 + 31) / 32 * 32; }
-size_t ds_bytes(int B, int Hq, int L, int window, int dtype) {
-  if (window < 0 || window > kMaxDsWindow || B < 1 || Hq < 1 || L < 1) return 0;
+size_t ds_bytes(int B, int Hq, int L, int D, int window, int dtype) {
+  if (D != 256 || window < 0 || window > kMaxDsWindow || B < 1 || Hq < 1 || L < 1) return 0;
   const size_t n = ((size_t)B * Hq * ((L + 31) / 32 * 32) * ds_width(window) * (dtype == NB_F32 ? 4 : 2) + 255) &
                    ~(size_t)255;
   return n < ((size_t)1 << 31) ? n : 0;   // buffer offsets stay in 31 bits
@@ -253,7 +255,7 @@ size_t ds_bytes(int B, int Hq, int L, int window, int dtype) {
 void enable_ds(nb::BwdParams& p, void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int L, int S, int D,
                int window_left, int dtype) {
   const size_t base = nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype);
-  const size_t db = ds_bytes(B, Hq, L, window_left, dtype);
+  const size_t db = ds_bytes(B, Hq, L, D, window_left, dtype);
   if (db == 0 || ws_bytes < base + db) return;
   p.dsbuf = reinterpret_cast<char*>(ws) + base;
   p.ds_w = ds_width(window_left);
@@ -265,7 +267,7 @@ extern "C" {
 
 size_t nb_attn_bwd_workspace_bytes_window(int B, int Hq, int Hkv, int L, int S, int D, int dtype, int window_left) {
   const size_t base = nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype);
-  return base == 0 ? 0 : base + ds_bytes(B, Hq, L, window_left, dtype);
+  return base == 0 ? 0 : base + ds_bytes(B, Hq, L, D, window_left, dtype);
 }
 
 }  // extern "C"
