@@ -824,8 +824,14 @@ __global__ __launch_bounds__(256, (DqsCfg<T, D>::OCC)) void dq_ds_kernel(BwdPara
   if (i0 < p.L) {
     int bs0 = max(0, p.row_klo[(size_t)b * p.L + i0] - p.k_origin);
     if (p.window >= 0) bs0 = max(bs0, p.q_off + i0 - p.window);
-    kb = bs0 & ~31;
-    ke = min(p.q_off + min(i0 + 31, p.L - 1), p.S - 1);
+    const int e = min(p.q_off + min(i0 + 31, p.L - 1), p.S - 1);
+    // A tile whose first band starts past its last key has no key at all (a
+    // one-row padding tile at the end: band start S): no dK/dV item visits it,
+    // so none of its blocks is written and none may be read.
+    if (bs0 <= e) {
+      kb = bs0 & ~31;
+      ke = e;
+    }
   }
   kb = __builtin_amdgcn_readfirstlane(kb);
   ke = __builtin_amdgcn_readfirstlane(ke);

@@ -1,5 +1,7 @@
 """HIP path vs the fp64 oracle, every element, at sizes the oracle finishes in
 seconds (several tiles and ragged tails), plus the edge cases of the method."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -165,7 +167,6 @@ def test_backward_entry_points_agree(name):
     and prep + main agree bit for bit, dK and dV equal the plain path's bit for
     bit and dQ agrees within the bf16 tolerance (the stored path rounds the
     same dS to bf16, from S and dP accumulated in another order)."""
-    import ctypes
 
     w = SMALL[name]
     inp = workload_inputs(w, "bf16")
@@ -268,3 +269,59 @@ def test_owner_dict_wrapped_owners_are_zero():
     for o in (2, 3):
         assert r.dk_by_owner[o].shape == (1, 1, 128, 64) and (r.dk_by_owner[o].float() == 0).all()
         assert not r.attended[o]
+
+
+STORED_DS_CASES = [  # seed, B, Hq, Hkv, L, S, window, doc lengths lo..hi, pad tail, dtype
+    (31, 1, 2, 1, 97, 333, 0, 5, 60, 0, "bf16"),      # window 0: the diagonal only
+    (32, 2, 4, 2, 130, 161, 1, 1, 40, 7, "bf16"),     # window 1, two batch rows, padding tail
+    (33, 1, 4, 1, 200, 515, 33, 20, 300, 0, "bf16"),  # GQA 4, keys not a multiple of 32
+    (34, 2, 2, 2, 64, 64, 100, 10, 50, 3, "f32"),     # window wider than the neighbourhood
+    (35, 1, 2, 1, 257, 1100, 700, 100, 900, 31, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", STORED_DS_CASES)
+def test_stored_ds_backward_edges(case):
+    """The stored-dS backward (D = 256 with a window) at ragged sizes: against the
+    oracle element by element, and against the recompute form (dK, dV bit-identical,
+    dQ within tolerance)."""
+    seed, B, Hq, Hkv, L, S, W, lo, hi, pt, dt = case
+    rng = np.random.default_rng(seed)
+    ids = np.zeros((B, S), dtype=np.int32)
+    for b in range(B):
+        pos, d = 0, 1
+        while pos < S:
+            n = int(rng.integers(lo, hi + 1))
+            ids[b, pos:pos + n] = d
+            pos, d = pos + n, d + 1
+    pad = None
+    if pt:
+        pad = np.zeros((B, S), dtype=np.uint8)
+        pad[:, S - pt:] = 1
+    inp = custom_inputs(ids, pad, Hq, Hkv, 256, L, W, dt, seed)
+    say(f"[stored dS] seed={seed} B={B} L={L} S={S} W={W} {dt}")
+    full_parity(inp, dt)   # the Python binding takes the stored-dS workspace
+    dev = torch.device("cuda:0")
+    pad_d = None if pad is None else torch.from_numpy(pad).to(dev)
+    seg = nb.segment_build(torch.from_numpy(ids).to(dev), L, W, pad_d)
+    q, k, v, do = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v, inp.do))
+    _, saved = nb.attn_fwd(q, k, v, seg)
+    a = nb.attn_bwd(saved, do, stored_ds=True)
+    r = nb.attn_bwd(saved, do, stored_ds=False)
+    assert torch.equal(a.dk, r.dk) and torch.equal(a.dv, r.dv)
+    assert_close("dQ stored vs recompute", a.dq.float().cpu().numpy(), r.dq.float().cpu().numpy(), dt)
+    # the workspace's old contents must not matter: filled with 0xff bytes (NaN in
+    # either dtype) it gives the same bits (a dS block read but never written shows)
+    lib = _lib.load()
+    D, code = q.shape[3], _lib.NB_BF16 if dt == "bf16" else _lib.NB_F32
+    wsb = lib.nb_attn_bwd_workspace_bytes_window(B, Hq, Hkv, L, S, D, code, W)
+    ws = torch.full((wsb,), 0xFF, dtype=torch.uint8, device=dev)
+    g = [torch.empty_like(t) for t in (q, k, v)]
+    att = torch.empty((1,), dtype=torch.uint8, device=dev)
+    off_c = (ctypes.c_int32 * 2)(0, S)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    _lib.check(lib.nb_attn_bwd(P(do), P(q), P(k), P(v), P(saved.out), P(saved.out_resid), P(saved.lse), P(seg.buf),
+                               P(seg.folded), B, Hq, Hkv, L, S, D, saved.scale, W, code, P(g[0]), P(g[1]), P(g[2]),
+                               ctypes.cast(off_c, ctypes.c_void_p), 1, P(att), P(ws), wsb,
+                               ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)), "nb_attn_bwd")
+    assert torch.equal(g[0], a.dq) and torch.equal(g[1], a.dk) and torch.equal(g[2], a.dv)
