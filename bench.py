@@ -347,7 +347,7 @@ def chunks_main(args) -> int:
     dks = [torch.empty_like(c.k) for c in chunks]
     dvs = [torch.empty_like(c.v) for c in chunks]
     att = torch.empty((n,), dtype=torch.uint8, device=dev)
-    ws_bytes = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S2, D, _lib_bf16())
+    ws_bytes = lib.nb_attn_bwd_workspace_bytes_window(B, Hq, Hkv, L, S2, D, _lib_bf16(), W)
     ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
     Pn, In = ctypes.c_void_p * n, ctypes.c_int32 * n
     kp, vp = Pn(*[c.k.data_ptr() for c in chunks]), Pn(*[c.v.data_ptr() for c in chunks])

@@ -160,11 +160,12 @@ size_t nb_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, 
 
 /* The same plus, with a left window 0 <= window_left <= 4096 and D = 256, a
  * banded dS buffer (B * Hq * round_up(L, 32) rows of round_up(window_left + 96,
- * 32) elements of dtype; at most 2 GiB, else none).  Given a workspace of this size, nb_attn_bwd and nb_attn_bwd_main on
- * a windowed neighbourhood have the dK/dV pass store dS and form dQ = dS K
- * from it instead of recomputing S and dP (dK, dV unchanged bit for bit; dQ
- * within the usual tolerance).  Equal to nb_attn_bwd_workspace_bytes without a
- * window. */
+ * 32) elements of dtype; at most 2 GiB, else none).  Given a workspace of this
+ * size, nb_attn_bwd, nb_attn_bwd_main and nb_attn_bwd_chunks on a windowed
+ * neighbourhood have the dK/dV pass store dS and form dQ = dS K from it instead
+ * of recomputing S and dP (dK, dV unchanged bit for bit; dQ within the usual
+ * tolerance).  Equal to nb_attn_bwd_workspace_bytes without a window or at
+ * another D. */
 size_t nb_attn_bwd_workspace_bytes_window(int B, int Hq, int Hkv, int L, int S, int D, int dtype, int window_left);
 
 /*
@@ -257,7 +258,8 @@ int nb_attn_fwd_chunks(const void* q, const void* const* k_chunk, const void* co
  * query attends) and 0 on its rows outside [chunk_start, chunk_start +
  * chunk_len).  chunk_attended (device [n_chunk], or NULL) receives the
  * nb_owner_attended flags with the chunks as owners (folded_ids then required).
- * Workspace as for nb_attn_bwd. */
+ * Workspace as for nb_attn_bwd (nb_attn_bwd_workspace_bytes_window's size
+ * selects the stored-dS form here too). */
 int nb_attn_bwd_chunks(const void* dout, const void* q, const void* const* k_chunk, const void* const* v_chunk,
                        const int32_t* chunk_len, const int32_t* chunk_start, const int32_t* chunk_rows,
                        int n_chunk, const void* o, const void* o_resid, const float* lse, const int32_t* seg_buf,

@@ -339,9 +339,10 @@ def attn_fwd_chunks(q: torch.Tensor, chunks: List[KvChunk], seg: Segments, scale
     return out, ChunkSaved(q, list(chunks), out, resid, lse, seg, scale)
 
 
-def attn_bwd_chunks(saved: ChunkSaved, grad_out: torch.Tensor):
+def attn_bwd_chunks(saved: ChunkSaved, grad_out: torch.Tensor, stored_ds: bool = True):
     """Backward writing whole chunk-gradient buffers (zeros outside the used rows
-    and for keys no query attends); returns ``(dq, [dk_c], [dv_c], [attended_c])``."""
+    and for keys no query attends); returns ``(dq, [dk_c], [dv_c], [attended_c])``.
+    ``stored_ds`` as for :func:`attn_bwd`."""
     lib = _lib.load()
     q, chunks, out, resid, lse, seg, scale = saved
     _need(grad_out.shape == q.shape and grad_out.dtype == q.dtype and grad_out.is_contiguous(),
@@ -351,7 +352,8 @@ def attn_bwd_chunks(saved: ChunkSaved, grad_out: torch.Tensor):
     dks = [torch.empty_like(c.k) for c in chunks]
     dvs = [torch.empty_like(c.v) for c in chunks]
     att = torch.empty((n,), dtype=torch.uint8, device=q.device)
-    ws_bytes = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, _DTYPES[q.dtype])
+    ws_bytes = (lib.nb_attn_bwd_workspace_bytes_window(B, Hq, Hkv, L, S, D, _DTYPES[q.dtype], seg.window)
+                if stored_ds else lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, _DTYPES[q.dtype]))
     ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=q.device)
     P = ctypes.c_void_p * n
     dkp, dvp = P(*[t.data_ptr() for t in dks]), P(*[t.data_ptr() for t in dvs])

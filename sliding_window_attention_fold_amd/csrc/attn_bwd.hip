@@ -176,10 +176,13 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
     const int bh = b * p.Hkv + kvh;
     const int n16 = min(C::BK, p.S - j0) * RV;
     if constexpr (CH) {
+      const KvSpan<T> sk(p.kv, kDK, bh, j0, jmax, D), sv(p.kv, kDV, bh, j0, jmax, D);
       for (int x = tid; x < n16; x += C::NT) {
         const int j = j0 + x / RV, c = x % RV;
-        reinterpret_cast<uint4*>(kv_row<T>(p.kv, kDK, bh, j, D))[c] = uint4{0u, 0u, 0u, 0u};
-        reinterpret_cast<uint4*>(kv_row<T>(p.kv, kDV, bh, j, D))[c] = uint4{0u, 0u, 0u, 0u};
+        T* rk = sk.ok ? sk.row(j, D) : kv_row<T>(p.kv, kDK, bh, j, D);
+        T* rv = sv.ok ? sv.row(j, D) : kv_row<T>(p.kv, kDV, bh, j, D);
+        reinterpret_cast<uint4*>(rk)[c] = uint4{0u, 0u, 0u, 0u};
+        reinterpret_cast<uint4*>(rv)[c] = uint4{0u, 0u, 0u, 0u};
       }
     } else {
       const size_t base = ((size_t)bh * p.S + j0) * D;
@@ -228,7 +231,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   {
     const T* src;
     if constexpr (CH) {
-      src = kv_row<T>(p.kv, role_a ? kK : kV, b * p.Hkv + kvh, min(j, p.S - 1), D);
+      const KvSpan<const T> sp(p.kv, role_a ? kK : kV, b * p.Hkv + kvh, j0, jmax, D);
+      src = sp.ok ? sp.row(min(j, p.S - 1), D) : kv_row<T>(p.kv, role_a ? kK : kV, b * p.Hkv + kvh,
+                                                                  min(j, p.S - 1), D);
     } else {
       const size_t kr = ((size_t)b * p.Hkv + kvh) * p.S + min(j, p.S - 1);
       src = reinterpret_cast<const T*>(role_a ? p.kv.k[0] : p.kv.v[0]) + kr * D;
@@ -316,9 +321,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   // offset for the whole item and a constant offset per row.
   const int ds_nb = p.ds_w >> 5;                      // blocks per 32-row tile
   const int ds_ntq = (p.L + 31) >> 5;                 // 32-row tiles per head
-  const int ds_lane = (ln + 4 * g * 32) * (int)sizeof(T);
   auto store_ds = [&](const f32x16& ds, int it, const int* ks) {
 #if defined(__HIP_DEVICE_COMPILE__)
+    const int ds_lane = (ln + 4 * g * 32) * (int)sizeof(T);   // (formed here: nothing extra held in the loop)
     const int hh = it / n_t, tq = t_first + it % n_t, i0 = tq * C::BQ;
     int bs0 = max(0, ks[0] - kor);
     if (p.window >= 0) bs0 = max(bs0, off + i0 - p.window);
@@ -487,8 +492,10 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
 
   if (j < p.S) {
     T* dst;
-    if constexpr (CH)
-      dst = kv_row<T>(p.kv, role_a ? kDV : kDK, b * p.Hkv + kvh, j, D);
+    if constexpr (CH) {
+      const KvSpan<T> sp(p.kv, role_a ? kDV : kDK, b * p.Hkv + kvh, j0, jmax, D);
+      dst = sp.ok ? sp.row(j, D) : kv_row<T>(p.kv, role_a ? kDV : kDK, b * p.Hkv + kvh, j, D);
+    }
     else
       dst = reinterpret_cast<T*>(role_a ? p.kv.dv[0] : p.kv.dk[0]) + (((size_t)b * p.Hkv + kvh) * p.S + j) * D;
     const float sc = role_a ? 1.f : p.scale;
@@ -792,6 +799,9 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
 // from the buffer in the accumulator order the forward feeds P^T in.  A wave
 // reads the same 32-key blocks the dK/dV items wrote for its 32-row tile: from
 // the first row's band start rounded down to 32 up to the last row's position.
+// KV: kKvConcat (one neighbourhood buffer) or kKvPair (the chunk table: K tiles
+// through KvPair, and through the general lookup when the workgroup's key range
+// touches three or more chunks).
 template <typename T, int D>
 struct DqsCfg {
   static constexpr int NW = 4;
@@ -802,7 +812,7 @@ struct DqsCfg {
   static constexpr int OCC = (sizeof(T) == 2) ? 2 : 1;
 };
 
-template <typename T, int D>
+template <typename T, int D, int KV>
 __global__ __launch_bounds__(256, (DqsCfg<T, D>::OCC)) void dq_ds_kernel(BwdParams p) {
   typedef DqsCfg<T, D> C;
   typedef Tile<T, C::BN, D> TL;
@@ -852,7 +862,15 @@ __global__ __launch_bounds__(256, (DqsCfg<T, D>::OCC)) void dq_ds_kernel(BwdPara
                                ((size_t)(b * p.Hq + h) * ds_ntq + min(i0, p.L - 1) / 32) * ds_nb * 1024 + ln * 32;
   const TileDma<T, C::BN, D, C::NW> dma;
   const TileAccess<T, TL> acc(ln, lane);
-  auto load = [&](T* Ks, int j0) { dma.issue(Ks, kbase + (size_t)j0 * D, min(C::BN, p.S - j0)); };
+  const KvPair<T, C::BN> pair = KV == kKvConcat ? KvPair<T, C::BN>() : KvPair<T, C::BN>(p.kv, bh, kstart, kend, D);
+  auto load = [&](T* Ks, int j0) {
+    if constexpr (KV == kKvConcat) {
+      dma.issue(Ks, kbase + (size_t)j0 * D, min(C::BN, p.S - j0));
+    } else {
+      if (pair.ok) pair.load_k(dma, j0, Ks);   // uniform
+      else kv_tile_load<T, C::BN, D, C::NW, false>(dma, p.kv, bh, j0, min(C::BN, p.S - j0), Ks, nullptr);
+    }
+  };
   // the B-operand fragments of one tile (zeros outside the wave's blocks, for
   // keys past S and for rows past L)
   constexpr int NM = C::BN / 16;
@@ -1203,6 +1221,16 @@ static hipError_t launch_main_t(const BwdParams& p, hipStream_t s) {
   // passes take the concatenated neighbourhood)
   const bool concat = p.kv.n == 1 && p.kv.start[0] == 0 && p.kv.rows[0] == p.S;
   if constexpr (MODE == 3) {
+    if (!concat && p.dsbuf != nullptr) {   // dK/dV items storing dS, then dQ = dS K, both through the table
+      const long long n_kv1 = (long long)p.B * ((p.S + DkvCfg<T, D>::BK - 1) / DkvCfg<T, D>::BK) * p.Hkv;
+      dim3 grid1((unsigned)std::min<long long>(n_kv1, (long long)device_cu_count() * BwdShape<T, D>::OCC));
+      hipLaunchKernelGGL((bwd_kernel<T, D, 1, kKvPair>), grid1, dim3(BwdShape<T, D>::NT), 0, s, p);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      dim3 grid2((unsigned)((p.L + DqsCfg<T, D>::BM - 1) / DqsCfg<T, D>::BM) * p.Hq * p.B);
+      hipLaunchKernelGGL((dq_ds_kernel<T, D, kKvPair>), grid2, dim3(DqsCfg<T, D>::NT), 0, s, p);
+      return hipGetLastError();
+    }
     if (!concat) {
       hipLaunchKernelGGL((bwd_kernel<T, D, MODE, kKvPair>), grid, dim3(BwdShape<T, D>::NT), 0, s, p);
       const hipError_t e = hipGetLastError();
@@ -1220,7 +1248,7 @@ static hipError_t launch_main_t(const BwdParams& p, hipStream_t s) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       dim3 grid2((unsigned)((p.L + DqsCfg<T, D>::BM - 1) / DqsCfg<T, D>::BM) * p.Hq * p.B);
-      hipLaunchKernelGGL((dq_ds_kernel<T, D>), grid2, dim3(DqsCfg<T, D>::NT), 0, s, p);
+      hipLaunchKernelGGL((dq_ds_kernel<T, D, kKvConcat>), grid2, dim3(DqsCfg<T, D>::NT), 0, s, p);
       return hipGetLastError();
     }
   }

@@ -31,10 +31,37 @@ __device__ __forceinline__ T* kv_row(const KvChunks& c, int which, int bh, int j
   return reinterpret_cast<T*>(p) + r * D;
 }
 
+// Rows of neighbourhood keys [j0, j1] (uniform bounds) in buffer `which` with
+// uniform state when they lie in at most two chunks: key j's row is
+// (j < cut ? base0 : base1) + j * D, each base shifted by its chunk's first
+// key.  ok is false (kv_row then) when the keys touch three or more chunks.
+template <typename T>
+struct KvSpan {
+  T* base0;
+  T* base1;
+  int cut;
+  bool ok;
+
+  __device__ __forceinline__ KvSpan(const KvChunks& c, int which, int bh, int j0, int j1, int D) {
+    size_t r0, r1;
+    const int x0 = kv_locate(c, bh, j0, &r0);
+    const int x1 = kv_locate(c, bh, j1, &r1);
+    auto base = [&](int y) -> T* {
+      return reinterpret_cast<T*>(which == kK ? const_cast<void*>(c.k[y]) : which == kV ? const_cast<void*>(c.v[y])
+                                  : which == kDK ? c.dk[y] : c.dv[y]);
+    };
+    ok = x1 <= x0 + 1;
+    cut = x1 > x0 ? c.off[x1] : INT_MAX;
+    base0 = base(x0) + ((long long)r0 - j0) * D;
+    base1 = base(x1) + ((long long)r1 - j1) * D;
+  }
+  __device__ __forceinline__ T* row(int j, int D) const { return (j < cut ? base0 : base1) + (size_t)j * D; }
+};
+
 // Copies neighbourhood keys [j0, j0 + ROWS) of K and V into the tiles Ks, Vs
 // (rows at or beyond nv repeat row nv - 1): one buffer-resource copy per chunk
-// the tile touches (usually one).
-template <typename T, int ROWS, int D, int NW>
+// the tile touches (usually one).  WITH_V false: K alone (Vs unused).
+template <typename T, int ROWS, int D, int NW, bool WITH_V = true>
 __device__ __forceinline__ void kv_tile_load(const TileDma<T, ROWS, D, NW>& dma, const KvChunks& c, int bh, int j0,
                                              int nv, T* Ks, T* Vs) {
   int j = j0;
@@ -44,7 +71,7 @@ __device__ __forceinline__ void kv_tile_load(const TileDma<T, ROWS, D, NW>& dma,
     const int e = (x + 1 < c.n) ? min(c.off[x + 1], j0 + nv) : j0 + nv;
     const int r_hi = (e == j0 + nv) ? ROWS : e - j0;
     dma.issue_rows(Ks, reinterpret_cast<const T*>(c.k[x]) + row * D, j - j0, r_hi, nv);
-    dma.issue_rows(Vs, reinterpret_cast<const T*>(c.v[x]) + row * D, j - j0, r_hi, nv);
+    if constexpr (WITH_V) dma.issue_rows(Vs, reinterpret_cast<const T*>(c.v[x]) + row * D, j - j0, r_hi, nv);
     j = e;
   }
 }
@@ -108,6 +135,14 @@ struct KvPair {
       dma.issue_split(Ks, k0 + (size_t)j0 * D, k1 + (size_t)cut * D, cut - j0);
       dma.issue_split(Vs, v0 + (size_t)j0 * D, v1 + (size_t)cut * D, cut - j0);
     }
+  }
+
+  // The same tile of K alone.
+  template <int D, int NW>
+  __device__ __forceinline__ void load_k(const TileDma<T, ROWS, D, NW>& dma, int j0, T* Ks) const {
+    if (j0 + ROWS <= cut) dma.issue(Ks, k0 + (size_t)j0 * D, min(ROWS, cap - j0));
+    else if (j0 >= cut) dma.issue(Ks, k1 + (size_t)j0 * D, min(ROWS, cap - j0));
+    else dma.issue_split(Ks, k0 + (size_t)j0 * D, k1 + (size_t)cut * D, cut - j0);
   }
 };
 

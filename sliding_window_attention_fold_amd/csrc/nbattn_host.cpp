@@ -423,8 +423,8 @@ int nb_attn_bwd_chunks(const void* dout, const void* q, const void* const* k_chu
     if (st != NB_OK) return st;
   }
   hipStream_t s = (hipStream_t)stream;
-  const nb::BwdParams p = bwd_params(dout, q, kv, o, o_resid, lse, seg_buf, B, Hq, Hkv, L, S, scale, window_left,
-                                     dq, ws);
+  nb::BwdParams p = bwd_params(dout, q, kv, o, o_resid, lse, seg_buf, B, Hq, Hkv, L, S, scale, window_left, dq, ws);
+  enable_ds(p, ws, ws_bytes, B, Hq, Hkv, L, S, D, window_left, dtype);
   st = map_hip(nb::launch_kv_zero_outside(kv, B * Hkv, D * (dtype == NB_F32 ? 4 : 2), s));
   if (st != NB_OK) return st;
   st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdPrep, s));

@@ -53,6 +53,9 @@ CASES = [  # seed, B, Hq, Hkv, D, L, S, window, pad_tail, chunk lengths, dtype
     # the last chunk shorter than a key tile: the tile holding the boundary would run past it
     (8, 1, 2, 1, 128, 10, 160, -1, 0, [150, 10], torch.bfloat16),
     (9, 1, 2, 1, 256, 20, 163, 60, 0, [143, 20], torch.bfloat16),
+    # windowed at D = 256 (the stored-dS form): a dQ workgroup's keys over five chunks, and fp32
+    (10, 1, 2, 1, 256, 128, 250, 100, 5, [30, 40, 30, 20, 130], torch.bfloat16),
+    (11, 1, 2, 2, 256, 96, 200, 50, 0, [60, 44, 96], torch.float32),
 ]
 
 
@@ -73,7 +76,6 @@ def test_chunks_match_concatenated_bitwise(case):
     out, saved = nb.attn_fwd(q, k, v, seg)
     offs = np.concatenate([[0], np.cumsum(lens)]).tolist()
     owners = nb.OwnerTable(offs, list(range(len(lens))))
-    ref = nb.attn_bwd(saved, do, owners, stored_ds=False)   # the chunk path's dQ pass recomputes S and dP too
     # the same keys embedded at random rows of larger chunk buffers
     chunks = []
     for c, n in enumerate(lens):
@@ -86,15 +88,19 @@ def test_chunks_match_concatenated_bitwise(case):
     out_c, saved_c = nb.attn_fwd_chunks(q, chunks, seg)
     assert torch.equal(out_c, out)
     assert torch.equal(saved_c.lse, saved.lse)
-    dq, dks, dvs, att = nb.attn_bwd_chunks(saved_c, do)
-    assert torch.equal(dq, ref.dq)
-    for c, ch in enumerate(chunks):
-        lo, hi = ch.start, ch.start + ch.length
-        assert torch.equal(dks[c][:, :, lo:hi], ref.dk[:, :, offs[c]:offs[c + 1]])
-        assert torch.equal(dvs[c][:, :, lo:hi], ref.dv[:, :, offs[c]:offs[c + 1]])
-        assert not dks[c][:, :, :lo].any() and not dks[c][:, :, hi:].any()
-        assert not dvs[c][:, :, :lo].any() and not dvs[c][:, :, hi:].any()
-        assert att[c] == ref.attended[c]
+    # both backward forms (dQ from stored dS with a window at D = 256, else the
+    # recompute) against the same form over the concatenated neighbourhood
+    for stored in (False, True):
+        ref = nb.attn_bwd(saved, do, owners, stored_ds=stored)
+        dq, dks, dvs, att = nb.attn_bwd_chunks(saved_c, do, stored_ds=stored)
+        assert torch.equal(dq, ref.dq)
+        for c, ch in enumerate(chunks):
+            lo, hi = ch.start, ch.start + ch.length
+            assert torch.equal(dks[c][:, :, lo:hi], ref.dk[:, :, offs[c]:offs[c + 1]])
+            assert torch.equal(dvs[c][:, :, lo:hi], ref.dv[:, :, offs[c]:offs[c + 1]])
+            assert not dks[c][:, :, :lo].any() and not dks[c][:, :, hi:].any()
+            assert not dvs[c][:, :, :lo].any() and not dvs[c][:, :, hi:].any()
+            assert att[c] == ref.attended[c]
 
 
 @pytest.mark.parametrize("cfg", [1, 2])
