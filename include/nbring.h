@@ -96,13 +96,26 @@ int nb_ring_finalize(const float* out_acc, void* out, void* out_resid, int64_t R
  * and the global lse (the merged lse_acc): dq [B, Hq, L, D] receives the chunk's
  * dQ contribution (dtype; fp32 set or accumulated per flags), dk, dv
  * [B, Hkv, Lk, D] the chunk's dK/dV (its owner's share from this shard; 0 at
- * keys no query reaches).  Workspace: nb_attn_bwd_workspace_bytes(B, Hq, Hkv,
- * L, Lk, D, dtype).  Arguments as nb_ring_chunk_fwd otherwise; unknown flags,
- * or both dQ flags, are NB_ERR_INVALID_ARG. */
+ * keys no query reaches).  Workspace: at least nb_attn_bwd_workspace_bytes(B,
+ * Hq, Hkv, L, Lk, D, dtype); given nb_ring_chunk_bwd_workspace_bytes, the dK/dV
+ * pass stores dS and dQ is formed from it (dK, dV bit-identical to the
+ * recompute form, dQ within the usual tolerance).  Arguments as
+ * nb_ring_chunk_fwd otherwise; unknown flags, or both dQ flags, are
+ * NB_ERR_INVALID_ARG. */
 int nb_ring_chunk_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o,
                       const void* o_resid, const float* lse, const int32_t* seg_buf, int B, int Hq, int Hkv, int L,
                       int Lk, int D, int q_start, int k_start, float scale, int dtype, void* dq, void* dk, void* dv,
                       int flags, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace for nb_ring_chunk_bwd's stored-dS form: those of
+ * nb_attn_bwd_workspace_bytes plus, at D = 256, a banded dS buffer with room
+ * for bands as wide as the chunk (B * Hq * round_up(L, 32) rows of
+ * round_up(Lk + 96, 32) elements of dtype; at most 2 GiB, else none).  Equal to
+ * nb_attn_bwd_workspace_bytes at other head dims.  Without a window every row's
+ * band may span the chunk, so the dS round trip grows with the rows that reach
+ * it: on a 4096-token chunk at B = 1, Hq = 16 the shard's own (causal) chunk
+ * takes longer this way than with the recompute, a chunk few rows reach less. */
+size_t nb_ring_chunk_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int Lk, int D, int dtype);
 
 /* acc[x] += src[x] for n elements (fp32 acc, dtype src; 16-byte aligned, n a
  * multiple of 4): the chunks' dQ contributions summed in fp32.  init != 0:

@@ -36,6 +36,7 @@ SIGNATURES = {
     "nb_attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _F, _I, _P, _Z, _P]),
     "nb_attn_bwd_workspace_bytes": (_Z, [_I] * 7),
     "nb_attn_bwd_workspace_bytes_window": (_Z, [_I] * 8),
+    "nb_ring_chunk_bwd_workspace_bytes": (_Z, [_I] * 7),
     "nb_attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I,
                          _P, _P, _P, _P, _I, _P, _P, _Z, _P]),
     "nb_attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _Z, _P]),

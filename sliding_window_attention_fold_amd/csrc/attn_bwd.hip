@@ -935,7 +935,7 @@ __global__ __launch_bounds__(256, (DqsCfg<T, D>::OCC)) void dq_ds_kernel(BwdPara
     compute(K1, f1, j0 + C::BN);
   }
 
-  if (!in_range) return;
+  if (!in_range || (!w_any && p.dq_mode == kDqAddF32)) return;   // (no key: nothing to add)
   const size_t qrow = ((size_t)b * p.Hq + h) * p.L + i;
 #pragma unroll
   for (int d = 0; d < D / 32; ++d) {

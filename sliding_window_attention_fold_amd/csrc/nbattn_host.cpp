@@ -244,12 +244,18 @@ namespace {
 // below 256, where the dQ items that recompute S and dP measured faster (their
 // dK/dV steps have no spare registers for the stores' bookkeeping there either).
 constexpr int kMaxDsWindow = 4096;
-int ds_width(int window) { return (window + 96 + 31) / 32 * 32; }
-size_t ds_bytes(int B, int Hq, int L, int D, int window, int dtype) {
-  if (D != 256 || window < 0 || window > kMaxDsWindow || B < 1 || Hq < 1 || L < 1) return 0;
-  const size_t n = ((size_t)B * Hq * ((L + 31) / 32 * 32) * ds_width(window) * (dtype == NB_F32 ? 4 : 2) + 255) &
+// Keys per 32-row tile of the banded dS buffer when no row's band is wider
+// than `span` keys: the first row's band start rounded down to 32, then up to
+// the last row's position, 31 rows further.
+int ds_width(int span) { return (span + 96 + 31) / 32 * 32; }
+size_t ds_bytes_span(int B, int Hq, int L, int D, int span, int dtype) {
+  if (D != 256 || span < 0 || B < 1 || Hq < 1 || L < 1) return 0;
+  const size_t n = ((size_t)B * Hq * ((L + 31) / 32 * 32) * ds_width(span) * (dtype == NB_F32 ? 4 : 2) + 255) &
                    ~(size_t)255;
   return n < ((size_t)1 << 31) ? n : 0;   // buffer offsets stay in 31 bits
+}
+size_t ds_bytes(int B, int Hq, int L, int D, int window, int dtype) {
+  return window > kMaxDsWindow ? 0 : ds_bytes_span(B, Hq, L, D, window, dtype);
 }
 // Turns the stored-dS backward on when the workspace holds the buffer.
 void enable_ds(nb::BwdParams& p, void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int L, int S, int D,
@@ -268,6 +274,11 @@ extern "C" {
 size_t nb_attn_bwd_workspace_bytes_window(int B, int Hq, int Hkv, int L, int S, int D, int dtype, int window_left) {
   const size_t base = nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype);
   return base == 0 ? 0 : base + ds_bytes(B, Hq, L, D, window_left, dtype);
+}
+
+size_t nb_ring_chunk_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int Lk, int D, int dtype) {
+  const size_t base = nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, Lk, D, dtype);
+  return base == 0 ? 0 : base + ds_bytes_span(B, Hq, L, D, Lk, dtype);
 }
 
 }  // extern "C"
@@ -485,6 +496,14 @@ int nb_ring_chunk_bwd(const void* dout, const void* q, const void* k, const void
                                scale, -1, dq, ws, q_start - k_start, k_start);
   p.dq_mode = (flags & NB_RING_DQ_F32_SET) ? nb::kDqSetF32 : (flags & NB_RING_DQ_F32_ADD) ? nb::kDqAddF32
                                                                                             : nb::kDqStore;
+  // with room for a dS band as wide as the chunk: the stored-dS form
+  const size_t base = nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, Lk, D, dtype);
+  const size_t db = ds_bytes_span(B, Hq, L, D, Lk, dtype);
+  if (db != 0 && ws_bytes >= base + db) {
+    p.dsbuf = reinterpret_cast<char*>(ws) + base;
+    p.ds_w = ds_width(Lk);
+    p.ds_bytes = (int)db;
+  }
   st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, (flags & NB_RING_DELTA_READY) ? nb::kBwdOrders : nb::kBwdPrep,
                               s));
   if (st != NB_OK) return st;

@@ -128,18 +128,26 @@ def finalize(out_acc: torch.Tensor, dtype: torch.dtype, with_resid: bool = True)
     return out, resid
 
 
+def _ws_bytes(lib, B, Hq, Hkv, L, Lk, D, dt, stored_ds):
+    return (lib.nb_ring_chunk_bwd_workspace_bytes(B, Hq, Hkv, L, Lk, D, dt) if stored_ds
+            else lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, Lk, D, dt))
+
+
 def chunk_bwd(dout, q, k, v, o, o_resid, lse, segs: RingSegments, k_start: int, scale: Optional[float] = None,
               ws: Optional[torch.Tensor] = None, dq_acc: Optional[torch.Tensor] = None, dq_init: bool = False,
-              delta_ready: bool = False):
+              delta_ready: bool = False, stored_ds: bool = False):
     """One chunk's ``(dQ contribution, dK, dV)`` with the global out/lse
     (``_ffpa_varlen_backward_chunk``).  With ``dq_acc`` (fp32) the contribution
     is added to it (``dq_init``: written) and returned in its place;
-    ``delta_ready``: ``ws`` holds Delta from an earlier call."""
+    ``delta_ready``: ``ws`` holds Delta from an earlier call.  ``stored_ds``: a
+    workspace with room for dS (at D = 256 the library then stores dS and forms
+    dQ from it whenever ``ws`` is that large; without a window the band spans
+    the chunk, which pays only where few rows reach it)."""
     B, Hq, Hkv, L, Lk, D = _dims(q, k)
     scale = D ** -0.5 if scale is None else float(scale)
     lib = _lib.load()
     dt = _DTYPES[q.dtype]
-    need = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, Lk, D, dt)
+    need = _ws_bytes(lib, B, Hq, Hkv, L, Lk, D, dt, stored_ds)
     if ws is None or ws.numel() < need:
         if delta_ready:
             raise ValueError("delta_ready needs the workspace of the earlier call")
@@ -190,19 +198,18 @@ def ring_forward(q: torch.Tensor, k_chunks: Sequence[torch.Tensor], v_chunks: Se
 
 
 def ring_backward(dout, q, k_chunks, v_chunks, out, out_resid, lse, segs: RingSegments, chunk_starts,
-                  scale: Optional[float] = None):
+                  scale: Optional[float] = None, stored_ds: bool = False):
     """Every chunk's backward with the global out/lse: ``(dQ fp32, [dK_c], [dV_c])``."""
     B, Hq, L, D = q.shape
     dq_acc = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     dks: List[torch.Tensor] = []
     dvs: List[torch.Tensor] = []
     lib = _lib.load()
-    need = max(lib.nb_attn_bwd_workspace_bytes(B, Hq, k.shape[1], L, k.shape[2], D, _DTYPES[q.dtype])
-               for k in k_chunks)
+    need = max(_ws_bytes(lib, B, Hq, k.shape[1], L, k.shape[2], D, _DTYPES[q.dtype], stored_ds) for k in k_chunks)
     ws = torch.empty((need,), dtype=torch.uint8, device=q.device)
     for c, (k, v, ks) in enumerate(zip(k_chunks, v_chunks, chunk_starts)):
         _, dk, dv = chunk_bwd(dout, q, k, v, out, out_resid, lse, segs, ks, scale, ws, dq_acc=dq_acc,
-                              dq_init=c == 0, delta_ready=c > 0)
+                              dq_init=c == 0, delta_ready=c > 0, stored_ds=stored_ds)
         dks.append(dk)
         dvs.append(dv)
     return dq_acc, dks, dvs

@@ -62,6 +62,7 @@ CASES = [  # seed, B, Hq, Hkv, D, Lc, P, rank, doc lengths lo..hi, pad tail, dty
     (4, 1, 2, 1, 128, 64, 2, 1, 5, 40, 9, "f32"),
     (5, 2, 2, 2, 256, 70, 3, 1, 30, 90, 5, "f32"),
     (6, 1, 2, 1, 64, 100, 4, 3, 400, 400, 0, "bf16"),   # one document over the whole sequence
+    (7, 1, 4, 1, 256, 97, 4, 3, 5, 60, 11, "bf16"),     # stored dS: ragged chunks, short documents, padding
 ]
 
 
@@ -185,6 +186,13 @@ def test_chunk_backward_with_global_out(case):
     assert_close("dQ (neighbourhood)", dq.cpu().numpy(), dq_f, dt)
     for c, o in enumerate(order):
         assert_close(f"dK (neighbourhood) owner {o}", dks[c].float().cpu().numpy(), dk_f[:, :, o * Lc:(o + 1) * Lc], dt)
+    # the stored-dS form (a workspace with room for dS; taken at D = 256): dK, dV
+    # bit-identical to the recompute, dQ within tolerance of it and of the oracle
+    dq_s, dks_s, dvs_s = ring.ring_backward(do, q, kc, vc, out, resid, lse_acc, segs, starts, stored_ds=True)
+    for c in range(len(order)):
+        assert torch.equal(dks[c], dks_s[c]) and torch.equal(dvs[c], dvs_s[c])
+    assert_close("dQ stored vs recompute", dq_s.cpu().numpy(), dq.cpu().numpy(), dt)
+    assert_close("dQ stored", dq_s.cpu().numpy(), dq_ref, dt)
 
 
 def test_rejects_a_later_owner_chunk():
