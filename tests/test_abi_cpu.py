@@ -52,6 +52,35 @@ def test_segment_buffer_sizes():
     assert n >= lib.nb_segment_offset_kcov_lo(2, 8) + 2 + 2 * 16
 
 
+def _r256(n):
+    return (n + 255) // 256 * 256
+
+
+def test_backward_workspace_sizes():
+    """The stored-dS room: B * Hq * round_up(L, 32) rows of round_up(span + 96, 32)
+    elements (span = the window, or the chunk length for a ring chunk), 256-byte
+    rounded, only at D = 256, only under 2 GiB; a window above 4096 gets none."""
+    lib = _lib.load()
+    bf, f32 = _lib.NB_BF16, _lib.NB_F32
+    base = lib.nb_attn_bwd_workspace_bytes(2, 4, 2, 100, 300, 256, bf)
+    assert base > 0
+    win = lib.nb_attn_bwd_workspace_bytes_window
+    assert win(2, 4, 2, 100, 300, 256, bf, 40) == base + _r256(2 * 4 * 128 * 160 * 2)   # 40 + 96 -> 160
+    assert win(2, 4, 2, 100, 300, 256, f32, 40) == lib.nb_attn_bwd_workspace_bytes(2, 4, 2, 100, 300, 256, f32) \
+        + _r256(2 * 4 * 128 * 160 * 4)
+    assert win(2, 4, 2, 100, 300, 256, bf, 0) == base + _r256(2 * 4 * 128 * 96 * 2)
+    assert win(2, 4, 2, 100, 300, 256, bf, -1) == base                 # no window
+    assert win(2, 4, 2, 100, 300, 256, bf, 4097) == base               # window too wide
+    assert win(2, 4, 2, 100, 300, 128, bf, 40) == lib.nb_attn_bwd_workspace_bytes(2, 4, 2, 100, 300, 128, bf)
+    # over 2 GiB of dS: none (64 heads x 8192 rows x 4192 keys x 2 bytes)
+    assert win(1, 64, 8, 8192, 16384, 256, bf, 4096) == lib.nb_attn_bwd_workspace_bytes(1, 64, 8, 8192, 16384, 256, bf)
+    ring = lib.nb_ring_chunk_bwd_workspace_bytes
+    assert ring(1, 16, 8, 4096, 4096, 256, bf) == lib.nb_attn_bwd_workspace_bytes(1, 16, 8, 4096, 4096, 256, bf) \
+        + _r256(16 * 4096 * 4192 * 2)                                    # 4096 + 96 = 4192 keys per row
+    assert ring(1, 2, 1, 97, 300, 64, bf) == lib.nb_attn_bwd_workspace_bytes(1, 2, 1, 97, 300, 64, bf)
+    assert ring(0, 2, 1, 97, 300, 256, bf) == 0
+
+
 FAKE = 0x100000  # an aligned address that is never dereferenced: every call below fails preflight
 
 
