@@ -1114,11 +1114,30 @@ __device__ void work_order(const BwdParams& p, int modes, unsigned long long* ke
 // the serial sort overlaps the streaming), workgroups 1 .. gridDim.x - 1 form
 // Delta (kDeltaRowsPerWg rows each); a grid of one workgroup computes the
 // orders only.
+// Owner o is attended iff some real key of its range [off[o], off[o + 1]) lies
+// at or after its batch row's kcov_lo (the first key any segment covers): one
+// workgroup of NT threads per owner.
+template <int NT>
+__device__ __forceinline__ void owner_flag(const OwnerParams& p, int o) {
+  const int a = p.off[o], e = p.off[o + 1];
+  int found = 0;
+  for (int b = 0; b < p.B && !found; ++b) {
+    const int lo = max(a, p.kcov_lo[b]);
+    for (int jj = lo + (int)threadIdx.x; jj < e; jj += NT) {
+      if (p.folded[(size_t)b * p.S + jj] > 0) { found = 1; break; }
+    }
+    found = __syncthreads_or(found);
+  }
+  if (threadIdx.x == 0) p.attended[o] = found ? 1 : 0;
+}
+
 template <typename T, int D, int BK, int BQ, int BM>
 __global__ __launch_bounds__(kPrepNT) void bwd_prep_kernel(BwdParams p, int modes) {
   __shared__ unsigned long long keys[kOrderMax];
   __shared__ int bst[kOrderBandMax];
+  const int first_owner = gridDim.x - p.own.n_owner;   // the last n_owner workgroups
   if (blockIdx.x == 0) work_order<BK, BQ, BM>(p, modes, keys, bst);
+  else if ((int)blockIdx.x >= first_owner) owner_flag<kPrepNT>(p.own, blockIdx.x - first_owner);
   else delta_rows<T, D>(p, blockIdx.x - 1);
 }
 
@@ -1207,8 +1226,8 @@ static hipError_t launch_prep_t(const BwdParams& p, bool with_delta, int modes, 
   static_assert(CK::BK >= 32 && CQ::BM >= 32, "the work-order arrays are sized for tiles of >= 32");
   const long long rows = (long long)p.B * p.Hq * p.L;
   const unsigned n_delta = with_delta ? (unsigned)((rows + kDeltaRowsPerWg - 1) / kDeltaRowsPerWg) : 0u;
-  hipLaunchKernelGGL((bwd_prep_kernel<T, D, CK::BK, CK::BQ, CQ::BM>), dim3(n_delta + 1), dim3(kPrepNT), 0, s, p,
-                     modes);
+  hipLaunchKernelGGL((bwd_prep_kernel<T, D, CK::BK, CK::BQ, CQ::BM>), dim3(n_delta + 1 + p.own.n_owner),
+                     dim3(kPrepNT), 0, s, p, modes);
   return hipGetLastError();
 }
 
@@ -1294,19 +1313,7 @@ hipError_t launch_bwd(const BwdParams& p, int D, bool f32, int what, hipStream_t
 // attended[o] = 1 iff some batch row has a covered key in chunk o: a key j is
 // covered iff j >= kcov_lo[b] and folded[b, j] > 0 (every covered key is
 // attended by at least one real query row, see the segment builder).
-__global__ __launch_bounds__(256) void owner_flags_kernel(OwnerParams p) {
-  const int o = blockIdx.x;
-  const int a = p.off[o], e = p.off[o + 1];
-  int found = 0;
-  for (int b = 0; b < p.B && !found; ++b) {
-    const int lo = max(a, p.kcov_lo[b]);
-    for (int jj = lo + threadIdx.x; jj < e; jj += 256) {
-      if (p.folded[(size_t)b * p.S + jj] > 0) { found = 1; break; }
-    }
-    found = __syncthreads_or(found);
-  }
-  if (threadIdx.x == 0) p.attended[o] = found ? 1 : 0;
-}
+__global__ __launch_bounds__(256) void owner_flags_kernel(OwnerParams p) { owner_flag<256>(p, blockIdx.x); }
 
 // dK/dV rows of chunk buffers outside the neighbourhood ([0, start) and
 // [start + len, rows) of every (batch, kv head)): exact zeros, as for keys no

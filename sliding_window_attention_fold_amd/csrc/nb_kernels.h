@@ -80,6 +80,15 @@ struct FwdParams {
   float scale_log2;  // softmax scale * log2(e)
 };
 
+constexpr int kMaxOwners = 64;
+struct OwnerParams {
+  const int32_t* folded;
+  const int32_t* kcov_lo;
+  uint8_t* attended;
+  int B, S, n_owner;
+  int off[kMaxOwners + 1];
+};
+
 struct BwdParams {
   const void* q;
   KvChunks kv;       // K, V read and dK, dV written through the chunk table
@@ -107,16 +116,11 @@ struct BwdParams {
   int ds_bytes;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
+  // Optional (n_owner > 0): the owners' attended flags, computed by extra
+  // workgroups of the prep kernel (they depend on the segments alone).
+  OwnerParams own;
 };
 
-constexpr int kMaxOwners = 64;
-struct OwnerParams {
-  const int32_t* folded;
-  const int32_t* kcov_lo;
-  uint8_t* attended;
-  int B, S, n_owner;
-  int off[kMaxOwners + 1];
-};
 
 hipError_t launch_segment_build(const SegParams& p, hipStream_t s);
 hipError_t launch_attn_fwd(const FwdParams& p, int D, bool f32, hipStream_t s);

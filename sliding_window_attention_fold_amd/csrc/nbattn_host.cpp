@@ -317,6 +317,7 @@ nb::BwdParams bwd_params(const void* dout, const void* q, const nb::KvChunks& kv
   p.ds_bytes = 0;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
+  std::memset(&p.own, 0, sizeof(p.own));   // no owner flags unless an entry point asks
   return p;
 }
 
@@ -331,11 +332,12 @@ int owner_checks(const int32_t* folded_ids, int S, const int32_t* owner_off, int
   return NB_OK;
 }
 
-int launch_owner(const int32_t* seg_buf, const int32_t* folded_ids, int B, int L, int S, const int32_t* owner_off,
-                 int n_owner, uint8_t* owner_attended, hipStream_t s) {
-  if (n_owner == 0) return NB_OK;
+// The owner-flag arguments (checked by owner_checks; n_owner 0: none).
+nb::OwnerParams owner_params(const int32_t* seg_buf, const int32_t* folded_ids, int B, int L, int S,
+                             const int32_t* owner_off, int n_owner, uint8_t* owner_attended) {
   nb::OwnerParams op;
   std::memset(&op, 0, sizeof(op));
+  if (n_owner == 0) return op;
   op.folded = folded_ids;
   op.kcov_lo = seg_buf + nb::seg_layout(B, L, S).kcov_lo;
   op.attended = owner_attended;
@@ -343,7 +345,14 @@ int launch_owner(const int32_t* seg_buf, const int32_t* folded_ids, int B, int L
   op.S = S;
   op.n_owner = n_owner;
   for (int x = 0; x <= n_owner; ++x) op.off[x] = owner_off[x];
-  return map_hip(nb::launch_owner_flags(op, s));
+  return op;
+}
+
+int launch_owner(const int32_t* seg_buf, const int32_t* folded_ids, int B, int L, int S, const int32_t* owner_off,
+                 int n_owner, uint8_t* owner_attended, hipStream_t s) {
+  if (n_owner == 0) return NB_OK;
+  return map_hip(nb::launch_owner_flags(owner_params(seg_buf, folded_ids, B, L, S, owner_off, n_owner,
+                                                     owner_attended), s));
 }
 
 }  // namespace
@@ -436,13 +445,13 @@ int nb_attn_bwd_chunks(const void* dout, const void* q, const void* const* k_chu
   hipStream_t s = (hipStream_t)stream;
   nb::BwdParams p = bwd_params(dout, q, kv, o, o_resid, lse, seg_buf, B, Hq, Hkv, L, S, scale, window_left, dq, ws);
   enable_ds(p, ws, ws_bytes, B, Hq, Hkv, L, S, D, window_left, dtype);
+  if (chunk_attended != nullptr)   // the flags come from the prep kernel
+    p.own = owner_params(seg_buf, folded_ids, B, L, S, off, n_chunk, chunk_attended);
   st = map_hip(nb::launch_kv_zero_outside(kv, B * Hkv, D * (dtype == NB_F32 ? 4 : 2), s));
   if (st != NB_OK) return st;
   st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdPrep, s));
   if (st != NB_OK) return st;
-  st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdMain, s));
-  if (st != NB_OK || chunk_attended == nullptr) return st;
-  return launch_owner(seg_buf, folded_ids, B, L, S, off, n_chunk, chunk_attended, s);
+  return map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdMain, s));
 }
 
 int nb_attn_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o, const void* o_resid,
@@ -461,11 +470,10 @@ int nb_attn_bwd(const void* dout, const void* q, const void* k, const void* v, c
   nb::BwdParams p = bwd_params(dout, q, one_chunk(S, k, v, dk, dv), o, o_resid, lse, seg_buf, B, Hq, Hkv, L, S,
                                scale, window_left, dq, ws);
   enable_ds(p, ws, ws_bytes, B, Hq, Hkv, L, S, D, window_left, dtype);
+  p.own = owner_params(seg_buf, folded_ids, B, L, S, owner_off, n_owner, owner_attended);   // computed in prep
   st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdPrep, s));
   if (st != NB_OK) return st;
-  st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdMain, s));
-  if (st != NB_OK) return st;
-  return launch_owner(seg_buf, folded_ids, B, L, S, owner_off, n_owner, owner_attended, s);
+  return map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdMain, s));
 }
 
 int nb_ring_chunk_fwd(const void* q, const void* k, const void* v, void* out, float* lse, const int32_t* seg_buf,
