@@ -1131,14 +1131,24 @@ __device__ __forceinline__ void owner_flag(const OwnerParams& p, int o) {
   if (threadIdx.x == 0) p.attended[o] = found ? 1 : 0;
 }
 
-template <typename T, int D, int BK, int BQ, int BM>
+// OWN: the last p.own.n_owner workgroups compute the owner flags (a separate
+// instance, so the Delta workgroups of the other keep their short prologue).
+template <typename T, int D, int BK, int BQ, int BM, bool OWN>
 __global__ __launch_bounds__(kPrepNT) void bwd_prep_kernel(BwdParams p, int modes) {
   __shared__ unsigned long long keys[kOrderMax];
   __shared__ int bst[kOrderBandMax];
-  const int first_owner = gridDim.x - p.own.n_owner;   // the last n_owner workgroups
-  if (blockIdx.x == 0) work_order<BK, BQ, BM>(p, modes, keys, bst);
-  else if ((int)blockIdx.x >= first_owner) owner_flag<kPrepNT>(p.own, blockIdx.x - first_owner);
-  else delta_rows<T, D>(p, blockIdx.x - 1);
+  if (blockIdx.x == 0) {
+    work_order<BK, BQ, BM>(p, modes, keys, bst);
+    return;
+  }
+  if constexpr (OWN) {
+    const int first_owner = gridDim.x - p.own.n_owner;
+    if ((int)blockIdx.x >= first_owner) {
+      owner_flag<kPrepNT>(p.own, blockIdx.x - first_owner);
+      return;
+    }
+  }
+  delta_rows<T, D>(p, blockIdx.x - 1);
 }
 
 size_t dkdv_order_elems(int B, int S) { return (size_t)B * ((S + 31) / 32); }
@@ -1226,8 +1236,12 @@ static hipError_t launch_prep_t(const BwdParams& p, bool with_delta, int modes, 
   static_assert(CK::BK >= 32 && CQ::BM >= 32, "the work-order arrays are sized for tiles of >= 32");
   const long long rows = (long long)p.B * p.Hq * p.L;
   const unsigned n_delta = with_delta ? (unsigned)((rows + kDeltaRowsPerWg - 1) / kDeltaRowsPerWg) : 0u;
-  hipLaunchKernelGGL((bwd_prep_kernel<T, D, CK::BK, CK::BQ, CQ::BM>), dim3(n_delta + 1 + p.own.n_owner),
-                     dim3(kPrepNT), 0, s, p, modes);
+  if (p.own.n_owner > 0)
+    hipLaunchKernelGGL((bwd_prep_kernel<T, D, CK::BK, CK::BQ, CQ::BM, true>), dim3(n_delta + 1 + p.own.n_owner),
+                       dim3(kPrepNT), 0, s, p, modes);
+  else
+    hipLaunchKernelGGL((bwd_prep_kernel<T, D, CK::BK, CK::BQ, CQ::BM, false>), dim3(n_delta + 1), dim3(kPrepNT), 0,
+                       s, p, modes);
   return hipGetLastError();
 }
 
