@@ -277,6 +277,8 @@ STORED_DS_CASES = [  # seed, B, Hq, Hkv, L, S, window, doc lengths lo..hi, pad t
     (33, 1, 4, 1, 200, 515, 33, 20, 300, 0, "bf16"),  # GQA 4, keys not a multiple of 32
     (34, 2, 2, 2, 64, 64, 100, 10, 50, 3, "f32"),     # window wider than the neighbourhood
     (35, 1, 2, 1, 257, 1100, 700, 100, 900, 31, "bf16"),
+    (36, 1, 2, 1, 100, 5000, 4096, 200, 3000, 0, "bf16"),   # the widest window with a dS buffer
+    (37, 1, 2, 1, 64, 4300, 4097, 100, 2000, 5, "bf16"),    # one wider: the recompute form on the same calls
 ]
 
 
