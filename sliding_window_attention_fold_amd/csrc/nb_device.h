@@ -372,7 +372,7 @@ __device__ __forceinline__ void lds_mfma_pipeline(ReadFn&& rd, MmaFn&& mm) {
 // Wait until this wave's global reads (including copies into LDS) have landed.
 __device__ __forceinline__ void wait_global() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-// Waits until at most n (wave-uniform, 0 <= n <= 15; larger n waits for 15) of
+// Waits until at most n (wave-uniform, 0 <= n <= 31; larger n waits for 31) of
 // this wave's vector-memory operations are outstanding.  They complete in
 // issue order, so this waits for everything but the n most recent.
 __device__ __forceinline__ void wait_global_le(int n) {
