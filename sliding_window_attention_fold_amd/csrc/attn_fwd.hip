@@ -169,8 +169,9 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdP
       }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    // Move the reference (and rescale O) only when some row's maximum passed it
-    // by more than kRefLag; the wave decides together so the branch is uniform.
+    // Move the reference (and rescale O) when some row's maximum passed it by
+    // more than kRefLag (0: any growth); the wave decides together so the
+    // branch is uniform, and rows whose maximum did not grow scale by 1.
     if (__any(tmax > m_ref + kRefLag)) {
       const float m_new = fmaxf(m_ref, tmax);
       const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
