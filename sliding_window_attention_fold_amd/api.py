@@ -14,13 +14,14 @@ from __future__ import annotations
 
 import ctypes
 from dataclasses import dataclass, field
+from collections.abc import Mapping
 from typing import Dict, List, NamedTuple, Optional
 
 import torch
 
 from . import _lib
 
-__all__ = ["Segments", "OwnerTable", "Saved", "BwdResult", "segment_build", "attn_fwd", "attn_bwd",
+__all__ = ["Segments", "OwnerTable", "OwnerFlags", "Saved", "BwdResult", "segment_build", "attn_fwd", "attn_bwd",
            "NeighbourhoodAttention", "neighbourhood_attention", "KvChunk", "ChunkSaved", "attn_fwd_chunks",
            "attn_bwd_chunks", "ring_window_chunks"]
 
@@ -152,11 +153,42 @@ class Saved(NamedTuple):
     scale: float
 
 
+class OwnerFlags(Mapping):
+    """``owner -> attended`` read lazily from the device flags.
+
+    The backward only enqueues work; the flags stay on the device (``flags``,
+    uint8, one per owner of the table, in table order) until a value is read
+    here, and only that first read synchronises.  Owners outside the
+    neighbourhood (future or wrapped ring owners) are ``False`` without any
+    device read."""
+
+    def __init__(self, flags: torch.Tensor, owners: List[int], absent: List[int]):
+        self.flags = flags
+        self._index = {r: o for o, r in enumerate(owners)}
+        self._absent = [r for r in absent if r not in self._index]
+        self._host: Optional[List[int]] = None
+
+    def __getitem__(self, rank: int) -> bool:
+        if rank in self._index:
+            if self._host is None:
+                self._host = self.flags.tolist()
+            return bool(self._host[self._index[rank]])
+        if rank in self._absent:
+            return False
+        raise KeyError(rank)
+
+    def __iter__(self):
+        return iter(list(self._index) + self._absent)
+
+    def __len__(self) -> int:
+        return len(self._index) + len(self._absent)
+
+
 class BwdResult(NamedTuple):
     dq: torch.Tensor
     dk_by_owner: Dict[int, torch.Tensor]
     dv_by_owner: Dict[int, torch.Tensor]
-    attended: Dict[int, bool]
+    attended: OwnerFlags
     dk: torch.Tensor
     dv: torch.Tensor
 
@@ -221,12 +253,10 @@ def attn_bwd(saved: Saved, grad_out: torch.Tensor, owners: Optional[OwnerTable] 
                                _ptr(seg.folded), B, Hq, Hkv, L, S, D, scale, seg.window, _DTYPES[q.dtype],
                                _ptr(dq), _ptr(dk), _ptr(dv), ctypes.cast(off_c, ctypes.c_void_p), n_owner,
                                _ptr(att), _ptr(ws), ws_bytes, _stream_ptr(q.device)), "nb_attn_bwd")
-    att_host = att[:n_owner].tolist()
-    dk_by, dv_by, attended = {}, {}, {}
+    dk_by, dv_by, absent = {}, {}, []
     for o, rank in enumerate(owners.owners):
         dk_by[rank] = dk[:, :, off[o]:off[o + 1]]
         dv_by[rank] = dv[:, :, off[o]:off[o + 1]]
-        attended[rank] = bool(att_host[o])
     n_prior = owners.n_prior if owners.n_prior is not None else len(owners.owners) - 1
     for d in range(n_prior + 1):
         r = (owners.cp_rank - d) % owners.cp_size
@@ -234,8 +264,8 @@ def attn_bwd(saved: Saved, grad_out: torch.Tensor, owners: Optional[OwnerTable] 
             shape = (B, Hkv, L, D)  # a ring owner's chunk is one shard long
             dk_by[r] = torch.zeros(shape, dtype=k.dtype, device=k.device)
             dv_by[r] = torch.zeros(shape, dtype=v.dtype, device=v.device)
-            attended[r] = False
-    return BwdResult(dq, dk_by, dv_by, attended, dk, dv)
+            absent.append(r)
+    return BwdResult(dq, dk_by, dv_by, OwnerFlags(att[:n_owner], list(owners.owners), absent), dk, dv)
 
 
 class NeighbourhoodAttention(torch.autograd.Function):
@@ -341,8 +371,10 @@ def attn_fwd_chunks(q: torch.Tensor, chunks: List[KvChunk], seg: Segments, scale
 
 def attn_bwd_chunks(saved: ChunkSaved, grad_out: torch.Tensor, stored_ds: bool = True):
     """Backward writing whole chunk-gradient buffers (zeros outside the used rows
-    and for keys no query attends); returns ``(dq, [dk_c], [dv_c], [attended_c])``.
-    ``stored_ds`` as for :func:`attn_bwd`."""
+    and for keys no query attends); returns ``(dq, [dk_c], [dv_c], attended)``
+    where ``attended`` is an :class:`OwnerFlags` keyed by chunk index (read
+    lazily: the call itself never synchronises).  ``stored_ds`` as for
+    :func:`attn_bwd`."""
     lib = _lib.load()
     q, chunks, out, resid, lse, seg, scale = saved
     _need(grad_out.shape == q.shape and grad_out.dtype == q.dtype and grad_out.is_contiguous(),
@@ -364,5 +396,5 @@ def attn_bwd_chunks(saved: ChunkSaved, grad_out: torch.Tensor, stored_ds: bool =
                                       L, S, D, scale, seg.window, _DTYPES[q.dtype], _ptr(dq),
                                       ctypes.cast(dkp, ctypes.c_void_p), ctypes.cast(dvp, ctypes.c_void_p), _ptr(att),
                                       _ptr(ws), ws_bytes, _stream_ptr(q.device)), "nb_attn_bwd_chunks")
-    return dq, dks, dvs, [bool(x) for x in att.tolist()]
+    return dq, dks, dvs, OwnerFlags(att, list(range(n)), [])
 

@@ -327,3 +327,46 @@ def test_stored_ds_backward_edges(case):
                                ctypes.cast(off_c, ctypes.c_void_p), 1, P(att), P(ws), wsb,
                                ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)), "nb_attn_bwd")
     assert torch.equal(g[0], a.dq) and torch.equal(g[1], a.dk) and torch.equal(g[2], a.dv)
+
+
+def test_training_step_never_synchronises():
+    """segment_build -> attn_fwd -> attn_bwd, the autograd wrapper and the chunk-table
+    calls enqueue work only: under torch's sync debug mode "error" any device-to-host
+    read or stream synchronisation inside them raises (cp_local_ring page,
+    _cached_sliding_segments: the point of building segments once per step is to keep
+    host syncs out of the layers).  The owner flags stay on the device until read."""
+    w = SMALL["w2s"]
+    inp = workload_inputs(w, "bf16")
+    say("[nosync] w2s")
+    dev = torch.device("cuda:0")
+    ids = torch.from_numpy(inp.ids).to(dev)
+    q, k, v, do = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v, inp.do))
+    ql = q.clone().requires_grad_(True)
+    kl, vl = k.clone().requires_grad_(True), v.clone().requires_grad_(True)
+    off = inp.owner_off
+    k_chunks = [k[:, :, off[c]:off[c + 1]].contiguous() for c in range(len(off) - 1)]
+    v_chunks = [v[:, :, off[c]:off[c + 1]].contiguous() for c in range(len(off) - 1)]
+    table = nb.OwnerTable(off, inp.owners, inp.cp_rank, inp.cp_size)
+    torch.cuda.synchronize()
+    torch.cuda.set_sync_debug_mode("error")
+    try:
+        seg = nb.segment_build(ids, inp.L, inp.window)
+        _, saved = nb.attn_fwd(q, k, v, seg)
+        res = nb.attn_bwd(saved, do, table)
+        out = nb.neighbourhood_attention(ql, kl, vl, seg)
+        out.backward(do)
+        chunks = nb.ring_window_chunks(k_chunks, v_chunks, inp.window)
+        seg2 = nb.segment_build(ids[:, inp.S - sum(c.length for c in chunks):].contiguous(), inp.L, inp.window)
+        _, saved_c = nb.attn_fwd_chunks(q, chunks, seg2)
+        dq_c, dks, dvs, att_c = nb.attn_bwd_chunks(saved_c, do)
+    finally:
+        torch.cuda.set_sync_debug_mode("default")
+    torch.cuda.synchronize()
+    # the flags are read (and only now synchronised) after the step
+    ref = orc.key_attended(inp.folded, inp.L, inp.window)
+    for o, rank in enumerate(inp.owners):
+        assert res.attended[rank] == bool(ref[:, off[o]:off[o + 1]].any())
+    assert torch.equal(ql.grad, res.dq) and torch.equal(kl.grad, res.dk)
+    assert_close("dQ chunks", dq_c.float().cpu().numpy(), res.dq.float().cpu().numpy(), "bf16")
+    for c in range(len(chunks)):
+        assert att_c[c] == bool(dks[c].any() or dvs[c].any())
