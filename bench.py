@@ -43,6 +43,123 @@ KERNELS = {
 }
 
 
+RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # ~312: below it a step is HBM-bound
+PEAK_FLOP_PER_CLK = 256 * 4096          # 256 CUs x 4096 dense bf16 FLOP per clock per CU
+
+
+def stats(x) -> dict:
+    """Median, min, p90 and mean of per-iteration times (ms)."""
+    import numpy as np
+
+    x = np.asarray(x, dtype=np.float64)
+    return {"median": round(float(np.median(x)), 5), "min": round(float(x.min()), 5),
+            "p90": round(float(np.percentile(x, 90)), 5), "mean": round(float(x.mean()), 5)}
+
+
+def time_iters(stream, body, n_events, iters, scratch):
+    """Per-iteration times (ms) of `body(events)` [iters, n_events]: each iteration gets its own events on the
+    launch stream; with `scratch`, a write of the whole scratch buffer precedes every iteration (not timed)."""
+    import numpy as np
+    import torch
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_events + 1)] for _ in range(iters)]
+    torch.cuda.synchronize()
+    for s in range(iters):
+        if scratch is not None:
+            scratch.fill_(s & 0x7F)
+        body(evs[s])
+    torch.cuda.synchronize()
+    return np.array([[evs[s][i].elapsed_time(evs[s][i + 1]) for i in range(n_events)] for s in range(iters)])
+
+
+def accounting(lib, segbuf, B, Hq, Hkv, L, S, D, W, dev) -> dict:
+    """Exact allowed pairs per head and compulsory HBM bytes from the device segment buffer.
+
+    Every real row's band is [max(row_klo, p - W), p]; a key is covered if some band holds it.  Compulsory bytes
+    (bf16 tensors, fp32 LSE / Delta): forward reads Q and the covered K/V rows and writes O and LSE; the
+    backward reads Q, dO, O, LSE and the covered K/V rows and writes dQ and every row of dK/dV (zeros included).
+    Per kernel: the prep reads dO and O and writes Delta; bwd_main reads Q, dO, LSE, Delta and covered K/V and
+    writes dQ, dK, dV."""
+    import torch
+
+    off_klo = lib.nb_segment_offset_row_klo(B, L)
+    klo = segbuf[off_klo:off_klo + B * L].view(B, L).long()
+    pos = (S - L + torch.arange(L, device=dev)).view(1, L).expand(B, L)
+    lo = klo if W < 0 else torch.maximum(klo, pos - W)
+    real = lo <= pos
+    pairs = int(torch.clamp(pos - lo + 1, min=0).sum().item())
+    # covered keys: difference array over the bands of the real rows
+    diff = torch.zeros((B, S + 1), dtype=torch.int64, device=dev)
+    ones = real.long()
+    diff.scatter_add_(1, torch.where(real, lo, torch.full_like(lo, S)), ones)
+    diff.scatter_add_(1, torch.where(real, pos + 1, torch.full_like(lo, S)), -ones)
+    covered = int((torch.cumsum(diff, dim=1)[:, :S] > 0).sum().item())
+    e = 2
+    act = B * Hq * L * D * e          # one [B, Hq, L, D] tensor
+    kv_cov = covered * Hkv * D * e    # covered rows of K (or V)
+    kv_all = B * Hkv * S * D * e
+    row32 = B * Hq * L * 4            # LSE or Delta
+    by = {
+        "attn_fwd": act + 2 * kv_cov + act + row32,
+        "bwd_prep": 2 * act + row32,
+        "bwd_main": 2 * act + 2 * row32 + 2 * kv_cov + act + 2 * kv_all,
+        "owner_flags": 0,
+    }
+    step = (act + 2 * kv_cov + act + row32) + (3 * act + row32 + 2 * kv_cov + act + 2 * kv_all)
+    by["step"] = step
+    return {"pairs": pairs, "covered_keys": covered, "bytes": by, "ai": 14.0 * D * Hq * pairs / step}
+
+
+def sample_sclk(body, stream, seconds: float = 2.0):
+    """Median shader clock (MHz) that rocm-smi reports while `body` runs back to back for `seconds`; None if
+    the tool gives nothing readable.  The sampler is a child process; the GPU work goes on meanwhile."""
+    import subprocess
+    import threading
+
+    import torch
+
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["rocm-smi", "-g", "--json"], capture_output=True, text=True, timeout=20)
+            except Exception:
+                return
+            for key, val in re.findall(r'"([^"]*sclk[^"]*)"\s*:\s*"([^"]*)"', r.stdout, re.I):
+                m = re.search(r"(\d+(?:\.\d+)?)\s*mhz", val, re.I)
+                if m:
+                    samples.append(float(m.group(1)))
+
+    th = threading.Thread(target=sampler, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds or (not samples and time.perf_counter() - t0 < 4 * seconds):
+        for _ in range(8):
+            body()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=30)
+    if not samples:
+        return None
+    samples.sort()
+    return samples[len(samples) // 2]
+
+
+def cpu_model() -> str:
+    import subprocess
+
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return "unknown"
+
+
 def kernel_source_hash(fname: str) -> str:
     """First 16 hex digits of the sha256 over a kernel source and the local headers it includes (recursively,
     in include order): a profile taken from other code no longer matches."""
@@ -108,7 +225,7 @@ def cpu_baseline(w, dm, tensors, rows: int, kv_heads: int):
     M = orc.allow_mask(folded, w.L, w.window, rows=sel)[:, 0] & orc.real_rows(folded, w.L)[:, sel][:, :, None]
     pairs = int(M.sum())
     flops = 14.0 * w.D * nq * pairs
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"fp64 numpy oracle fwd+bwd, kv heads [0,{nkv}) of {w.Hkv} ({nq} of {w.Hq} q heads), "
                       f"query rows [0,{len(sel)}) of {w.L}, all {dm.S} keys; {pairs} allowed pairs per head; "
                       f"{dt:.1f} s"}
@@ -217,55 +334,73 @@ def main() -> int:
                                                      ctypes.c_void_p), n_owner, P(attended), sp),
     }
     names = list(calls)
+    fb = names[1:]   # fwd+bwd: everything but the segment build (built once per step, reused by every layer)
 
-    def step(events=None):
-        for i, n in enumerate(names):
+    def run(seq, events=None):
+        for i, n in enumerate(seq):
             if events is not None:
                 events[i].record(stream)
             st = calls[n]()
             if st != 0:
                 raise _lib.NbError(st, n)
         if events is not None:
-            events[len(names)].record(stream)
+            events[len(seq)].record(stream)
 
-    # exact useful pairs from the device segment buffer (accounting, outside the timed region)
-    step()
+    # exact useful pairs and compulsory bytes from the device segment buffer (accounting, outside the timed region)
+    run(names)
     torch.cuda.synchronize()
-    off_klo = lib.nb_segment_offset_row_klo(B, L)
-    klo = segbuf[off_klo:off_klo + B * L].view(B, L).long()
-    pos = (S - L + torch.arange(L, device=dev)).view(1, L)
-    band_lo = klo if W < 0 else torch.maximum(klo, pos - W)
-    pairs = int(torch.clamp(pos - band_lo + 1, min=0).sum().item())
+    acct = accounting(lib, segbuf, B, Hq, Hkv, L, S, D, W, dev)
+    pairs = acct["pairs"]
     useful = 14.0 * D * Hq * pairs
 
     for _ in range(args.warmup):
-        step()
+        run(names)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # Segment build alone (once per step in training, outside fwd+bwd).
+    seg_ms = time_iters(stream, lambda ev: run(["segment_build"], ev), 1, args.steps, None)[:, 0]
+    # Primary: every fwd+bwd iteration starts after a 512 MiB scratch write, so L2 and the MALL hold none of
+    # its inputs.  Each iteration is bracketed by its own events.
+    scratch = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
+    flushed = time_iters(stream, lambda ev: run(fb, ev), len(fb), args.steps, scratch)
+    # Warm: the same iterations back to back (inputs partly cached from the previous iteration).
+    warm = time_iters(stream, lambda ev: run(fb, ev), len(fb), args.steps, None)
+    # The K timed steps as one bracket (barrier + synchronise on both sides), back to back, segment build
+    # included: the whole hot path.
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for s in range(args.steps):
-        step(evs[s])
+    for _ in range(args.steps):
+        run(names)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
-    per = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
-           for i, n in enumerate(names)}
+    hot_path_ms = t_start.elapsed_time(t_end) / args.steps
+    sclk = sample_sclk(lambda: run(fb), stream)
+    del scratch
 
     if args.copy_mib > 0:
         calibration_copy(args.copy_mib, dev)
 
+    fb_f = flushed.sum(axis=1)
+    fb_w = warm.sum(axis=1)
+    ms_step = float(np.median(fb_f))
     tflops = useful / (ms_step * 1e-3) / 1e12
-    dom = max(KERNELS, key=lambda n: per[n])
-    dom_flops = KERNELS[dom][2] * D * Hq * pairs
-    achieved = dom_flops / (per[dom] * 1e-3) / 1e12
+    per_mean = {n: float(flushed[:, i].mean()) for i, n in enumerate(fb)}
+    dom = max(KERNELS, key=lambda n: per_mean[n])
+    dom_ms = per_mean[dom]
+    bound = "mfma" if acct["ai"] >= RIDGE_FLOP_PER_BYTE else "hbm"
     traffic = read_traffic(dom, f"config{args.config}")
+    if bound == "mfma":
+        dom_flops = KERNELS[dom][2] * D * Hq * pairs
+        achieved, peak, unit = dom_flops / (dom_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        algo = {"algorithmic_flop_per_launch": dom_flops}
+    else:
+        dom_bytes = acct["bytes"][dom]
+        achieved, peak, unit = dom_bytes / (dom_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+        algo = {"algorithmic_bytes_per_launch": dom_bytes}
     rec = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -285,14 +420,29 @@ def main() -> int:
             "pairs_per_head": pairs, "useful_flop_per_step": useful,
         },
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "ms_per_kernel": {n: round(per[n], 5) for n in names},
-        "fwd_bwd_ms": round(per["attn_fwd"] + per["bwd_prep"] + per["bwd_main"], 5),
+        "step": "fwd+bwd (nb_attn_fwd, nb_attn_bwd_prep, nb_attn_bwd_main, nb_owner_attended), each iteration "
+                "after a 512 MiB scratch write; value and ms_per_step from the median",
+        "fwd_bwd_ms": stats(fb_f),
+        "fwd_bwd_warm_ms": stats(fb_w),
+        "warm_tflops": round(useful / (float(np.median(fb_w)) * 1e-3) / 1e12, 3),
+        "segment_build_ms": stats(seg_ms),
+        "hot_path_back_to_back_ms": round(hot_path_ms, 5),
+        "hot_path_tflops": round(useful / (hot_path_ms * 1e-3) / 1e12, 3),
+        "ms_per_kernel": {n: stats(flushed[:, i]) for i, n in enumerate(fb)},
+        "ms_per_kernel_warm": {n: round(float(np.median(warm[:, i])), 5) for i, n in enumerate(fb)},
+        "compulsory_bytes_per_step": acct["bytes"]["step"],
+        "hbm_gbs_compulsory": round(acct["bytes"]["step"] / (ms_step * 1e-3) / 1e9, 1),
+        "arithmetic_intensity": round(acct["ai"], 1),
+        "sclk_mhz": sclk,
+        "pct_of_bf16_peak_at_sclk": (None if not sclk else
+                                     round(100.0 * tflops / (PEAK_FLOP_PER_CLK * sclk * 1e6 / 1e12), 2)),
         "wall_s_timed": round(wall, 4),
         "roofline": {
-            "kernel": dom, "bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-            "algorithmic_flop_per_launch": dom_flops,
-            "traffic_gbs": None if traffic is None else round(traffic / (per[dom] * 1e-3) / 1e9, 1),
+            "kernel": dom, "bound": bound, "achieved": round(achieved, 3), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
+            **algo,
+            "avg_launch_ms": round(dom_ms, 5),
+            "traffic_gbs": None if traffic is None else round(traffic / (dom_ms * 1e-3) / 1e9, 1),
         },
     }
     if not args.no_cpu_baseline:
