@@ -33,7 +33,9 @@
  *     W < 0: no window.
  *   - Errors are detected before anything is enqueued: a non-OK return leaves
  *     the stream untouched.  NB_ERR_LAUNCH reports a HIP launch failure.
- *   - Thread-safe and stateless; calls on one stream are ordered by the stream.
+ *   - Thread-safe and stateless (except nb_attn_bwd_noalloc, whose static
+ *     workspace calls on one GPU share); calls on one stream are ordered by the
+ *     stream.
  */
 #ifndef NBATTN_H
 #define NBATTN_H
@@ -225,6 +227,30 @@ int nb_attn_bwd_dkdv(const void* dout, const void* q, const void* k, const void*
                      void* ws, size_t ws_bytes, void* stream);
 int nb_owner_attended(const int32_t* seg_buf, const int32_t* folded_ids, int B, int L, int S,
                       const int32_t* owner_off, int n_owner, uint8_t* owner_attended, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): nb_attn_bwd
+ * with no workspace argument.  Its workspace (Delta, work orders, queue
+ * counters, deferred dQ list) lives in a static device array of the library,
+ * one per GPU, of nb_attn_bwd_noalloc_max_workspace_bytes() bytes (8 MiB),
+ * held until the process ends.  Nothing is allocated or freed by the call.
+ *   Arguments, layouts and results as nb_attn_bwd (the recompute form of the
+ *   dQ pass: no stored-dS buffer); dq, dk, dv are bit-identical to nb_attn_bwd
+ *   with a workspace of nb_attn_bwd_workspace_bytes.
+ *   NB_ERR_WORKSPACE when nb_attn_bwd_workspace_bytes(...) for these sizes
+ *   exceeds the static array (checked before anything is enqueued).
+ *   Every call on one GPU uses that GPU's one array: calls that overlap on one
+ *   GPU (on different streams, or from different threads) race and must be
+ *   ordered by the caller.  The array keeps the last call's contents; the call
+ *   rewrites everything it reads (the prep kernel sets the queue counters to 0).
+ */
+size_t nb_attn_bwd_noalloc_max_workspace_bytes(void);
+int nb_attn_bwd_noalloc(const void* dout, const void* q, const void* k, const void* v, const void* o,
+                        const void* o_resid, const float* lse, const int32_t* seg_buf, const int32_t* folded_ids,
+                        int B, int Hq, int Hkv, int L, int S, int D, float scale, int window_left, int dtype,
+                        void* dq, void* dk, void* dv, const int32_t* owner_off, int n_owner,
+                        uint8_t* owner_attended, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * Zero-copy neighbourhood: K/V straight from the owners' chunk buffers.

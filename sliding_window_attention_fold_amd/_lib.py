@@ -44,6 +44,9 @@ SIGNATURES = {
     "nb_attn_bwd_prep": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _Z, _P]),
     "nb_attn_bwd_main": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P, _Z, _P]),
     "nb_owner_attended": (_I, [_P, _P, _I, _I, _I, _P, _I, _P, _P]),
+    "nb_attn_bwd_noalloc_max_workspace_bytes": (_Z, []),
+    "nb_attn_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I,
+                                 _P, _P, _P, _P, _I, _P, _P]),
     "nb_attn_fwd_chunks": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _F,
                                 _I, _P, _Z, _P]),
     "nb_attn_bwd_chunks": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F,

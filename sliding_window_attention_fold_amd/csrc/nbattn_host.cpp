@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/nbattn.h"
 #include "../../include/nbring.h"
@@ -514,6 +515,73 @@ int nb_ring_chunk_bwd(const void* dout, const void* q, const void* k, const void
   }
   st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, (flags & NB_RING_DELTA_READY) ? nb::kBwdOrders : nb::kBwdPrep,
                               s));
+  if (st != NB_OK) return st;
+  return map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdMain, s));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The backward without a caller workspace (nb_attn_bwd_noalloc).  Its
+// workspace -- Delta, the work orders, the queue counters and the deferred dQ
+// list, laid out exactly as nb_attn_bwd's -- lives in this file-scope device
+// array, one copy per GPU, held until the process ends.  Host code never uses
+// the array's name as an address (on the host it is only a stand-in): each
+// device's address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and is what the kernels receive.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (resolved on the first call on that device).
+int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NB_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) return e == hipSuccess ? NB_ERR_DEVICE : map_hip(e);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return NB_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t nb_attn_bwd_noalloc_max_workspace_bytes(void) { return kNoAllocScratchBytes; }
+
+int nb_attn_bwd_noalloc(const void* dout, const void* q, const void* k, const void* v, const void* o,
+                        const void* o_resid, const float* lse, const int32_t* seg_buf, const int32_t* folded_ids,
+                        int B, int Hq, int Hkv, int L, int S, int D, float scale, int window_left, int dtype,
+                        void* dq, void* dk, void* dv, const int32_t* owner_off, int n_owner,
+                        uint8_t* owner_attended, void* stream) {
+  // the same checks as nb_attn_bwd, with the size limit of the static workspace
+  const void* ptrs[] = {dout, q, k, v, o, lse, seg_buf, dq, dk, dv};
+  int st = attn_common_checks(ptrs, 10, B, Hq, Hkv, L, S, D, scale, dtype);
+  if (st != NB_OK) return st;
+  if (o_resid != nullptr && !aligned16(o_resid)) return NB_ERR_INVALID_ARG;
+  const size_t need = nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, dtype);
+  if (need == 0 || need > kNoAllocScratchBytes) return NB_ERR_WORKSPACE;
+  st = owner_checks(folded_ids, S, owner_off, n_owner, owner_attended);
+  if (st != NB_OK) return st;
+  void* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st != NB_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // recompute form (no dS buffer); the prep kernel writes Delta and the work
+  // orders and sets the queue counters to zero, so nothing carried over from
+  // an earlier call is read
+  nb::BwdParams p = bwd_params(dout, q, one_chunk(S, k, v, dk, dv), o, o_resid, lse, seg_buf, B, Hq, Hkv, L, S,
+                               scale, window_left, dq, ws);
+  p.own = owner_params(seg_buf, folded_ids, B, L, S, owner_off, n_owner, owner_attended);
+  st = map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdPrep, s));
   if (st != NB_OK) return st;
   return map_hip(nb::launch_bwd(p, D, dtype == NB_F32, nb::kBwdMain, s));
 }

@@ -184,3 +184,24 @@ def test_exchange_preflight_rejects_bad_arguments():
     assert lib.nb_exchange_gather(FAKE, FAKE, 1, 1, 32, 8, P, _lib.NB_BF16, bad, None) == _lib.NB_ERR_INVALID_ARG
     assert lib.nb_exchange_gather(FAKE, FAKE, 300, 300, 32, 8, P, _lib.NB_BF16, ptrs, None) == \
         _lib.NB_ERR_INVALID_ARG                                      # B * C > 65535
+
+
+def test_noalloc_backward_rejects_sizes_beyond_its_static_workspace():
+    """nb_attn_bwd_noalloc: 8 MiB of static workspace; sizes whose workspace would
+    exceed it are refused with NB_ERR_WORKSPACE before any HIP call (the pointers
+    below are never dereferenced: the preflight returns first)."""
+    lib = _lib.load()
+    cap = lib.nb_attn_bwd_noalloc_max_workspace_bytes()
+    assert cap == 8 << 20
+    fake = ctypes.c_void_p(1 << 20)                      # non-null, 16-byte aligned, never used
+    def call(B, Hq, Hkv, L, S, D):
+        return lib.nb_attn_bwd_noalloc(fake, fake, fake, fake, fake, None, fake, fake, None, B, Hq, Hkv, L, S, D,
+                                       D ** -0.5, -1, _lib.NB_BF16, fake, fake, fake, None, 0, None, None)
+    # Delta alone: 64 heads x 40000 rows x 4 bytes > 8 MiB
+    assert lib.nb_attn_bwd_workspace_bytes(1, 64, 8, 40000, 40000, 128, _lib.NB_BF16) > cap
+    assert call(1, 64, 8, 40000, 40000, 128) == _lib.NB_ERR_WORKSPACE
+    # the other checks come first, as for nb_attn_bwd
+    assert call(1, 6, 4, 100, 200, 128) == _lib.NB_ERR_INVALID_ARG      # Hq % Hkv != 0
+    assert call(1, 8, 2, 100, 200, 96) == _lib.NB_ERR_UNSUPPORTED       # head dim
+    # the largest workload here fits (config 4: 32 heads x 8192 rows, 65536 keys)
+    assert lib.nb_attn_bwd_workspace_bytes(1, 32, 8, 8192, 65536, 128, _lib.NB_BF16) <= cap
