@@ -110,37 +110,64 @@ def accounting(lib, segbuf, B, Hq, Hkv, L, S, D, W, dev) -> dict:
     return {"pairs": pairs, "covered_keys": covered, "bytes": by, "ai": 14.0 * D * Hq * pairs / step}
 
 
-def sample_sclk(body, stream, seconds: float = 2.0):
-    """Median shader clock (MHz) that rocm-smi reports while `body` runs back to back for `seconds`; None if
-    the tool gives nothing readable.  The sampler is a child process; the GPU work goes on meanwhile."""
-    import subprocess
+def _sclk_path(index: int = 0):
+    """sysfs DPM table of the GPU torch calls cuda:index (matched by PCI domain/bus/device), or None."""
+    import glob
+
+    import torch
+
+    pr = torch.cuda.get_device_properties(index)
+    want = (int(pr.pci_domain_id), int(pr.pci_bus_id), int(pr.pci_device_id))
+    for path in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
+        addr = os.path.basename(os.path.realpath(os.path.dirname(path)))      # e.g. 0000:75:00.0
+        m = re.match(r"([0-9a-fA-F]+):([0-9a-fA-F]+):([0-9a-fA-F]+)\.", addr)
+        if m and tuple(int(x, 16) for x in m.groups()) == want:
+            return path
+    return None
+
+
+def _read_sclk(path):
+    """Current shader clock (MHz): the starred level of the DPM table."""
+    try:
+        with open(path) as fh:
+            for line in fh:
+                if "*" in line:
+                    m = re.search(r"(\d+(?:\.\d+)?)\s*mhz", line, re.I)
+                    return float(m.group(1)) if m else None
+    except OSError:
+        return None
+    return None
+
+
+def sample_sclk(body, stream, seconds: float = 1.5):
+    """Median shader clock (MHz) read from the GPU's sysfs DPM table every few ms while `body` runs back to
+    back for `seconds` (a thread reading a file: no child process); None where the table is not readable."""
     import threading
 
     import torch
 
+    path = _sclk_path(torch.cuda.current_device())
+    if path is None or _read_sclk(path) is None:
+        return None
     samples = []
     stop = threading.Event()
 
     def sampler():
         while not stop.is_set():
-            try:
-                r = subprocess.run(["rocm-smi", "-g", "--json"], capture_output=True, text=True, timeout=20)
-            except Exception:
-                return
-            for key, val in re.findall(r'"([^"]*sclk[^"]*)"\s*:\s*"([^"]*)"', r.stdout, re.I):
-                m = re.search(r"(\d+(?:\.\d+)?)\s*mhz", val, re.I)
-                if m:
-                    samples.append(float(m.group(1)))
+            v = _read_sclk(path)
+            if v is not None:
+                samples.append(v)
+            time.sleep(0.005)
 
     th = threading.Thread(target=sampler, daemon=True)
     t0 = time.perf_counter()
     th.start()
-    while time.perf_counter() - t0 < seconds or (not samples and time.perf_counter() - t0 < 4 * seconds):
+    while time.perf_counter() - t0 < seconds:
         for _ in range(8):
             body()
         torch.cuda.synchronize()
     stop.set()
-    th.join(timeout=30)
+    th.join(timeout=5)
     if not samples:
         return None
     samples.sort()
@@ -148,14 +175,13 @@ def sample_sclk(body, stream, seconds: float = 2.0):
 
 
 def cpu_model() -> str:
-    import subprocess
-
+    """The host CPU's model name (as lscpu prints it), from /proc/cpuinfo."""
     try:
-        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
-        for line in out.splitlines():
-            if line.lower().startswith("model name"):
-                return line.split(":", 1)[1].strip()
-    except Exception:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
         pass
     return "unknown"
 
