@@ -288,6 +288,8 @@ def main() -> int:
                          "ring: the global-layer ring (per-chunk attention, online merges)")
     ap.add_argument("--ring-config", type=int, default=2,
                     help="ring workload whose world the global-layer ring runs on (default 2)")
+    ap.add_argument("--ring-head-dim", type=int, default=512,
+                    help="head dim of the global-layer ring (default 512, the global layers'; 64/128/256 also run)")
     ap.add_argument("--kv", choices=["concat", "chunks"], default="concat",
                     help="concat: K/V as one neighbourhood buffer (default); chunks: the window-trimmed owner "
                          "chunks read in place (ring workloads)")
@@ -625,7 +627,9 @@ def ring_main(args) -> int:
     lib = _lib.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    w = wl.get(args.ring_config)
+    import dataclasses
+
+    w = dataclasses.replace(wl.get(args.ring_config), D=args.ring_head_dim)
     if w.mode != "ring":
         print("--part ring needs a ring workload", file=sys.stderr)
         return 2
@@ -657,7 +661,9 @@ def ring_main(args) -> int:
     dq_acc = torch.empty((B, Hq, Lc, D), dtype=torch.float32, device=dev)
     dks = [torch.empty_like(t) for t in kc]
     dvs = [torch.empty_like(t) for t in vc]
-    ws_bytes = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, Lc, Lc, D, bf)
+    # (D = 512 runs only the stored-dS backward, whose workspace holds the chunk-wide dS band)
+    ws_bytes = (lib.nb_ring_chunk_bwd_workspace_bytes(B, Hq, Hkv, Lc, Lc, D, bf) if D >= 512
+                else lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, Lc, Lc, D, bf))
     ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -733,7 +739,7 @@ def ring_main(args) -> int:
     ln, st, rw = In(*([Lc] * (r + 1))), In(*([0] * (r + 1))), In(*([Lc] * (r + 1)))
     cv = lambda a: ctypes.cast(a, ctypes.c_void_p)  # noqa: E731
     lse1 = torch.empty((B, Hq, Lc), dtype=torch.float32, device=dev)
-    ws1_bytes = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, Lc, S, D, bf)
+    ws1_bytes = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, Lc, S, D, bf) if D <= 256 else 1
     ws1 = torch.empty((ws1_bytes,), dtype=torch.uint8, device=dev)
     seg1 = torch.empty((lib.nb_segment_buffer_elems(B, Lc, S),), dtype=torch.int32, device=dev)
     fold1 = torch.empty((B, S), dtype=torch.int32, device=dev)
@@ -751,15 +757,17 @@ def ring_main(args) -> int:
             if rc != 0:
                 raise _lib.NbError(rc, nm)
 
-    one_pass()
-    torch.cuda.synchronize()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(args.steps):
+    one_ms = None
+    if D <= 256:   # the chunk-table calls take head dims up to 256
         one_pass()
-    c1.record(stream)
-    torch.cuda.synchronize()
-    one_ms = c0.elapsed_time(c1) / args.steps
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(args.steps):
+            one_pass()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        one_ms = c0.elapsed_time(c1) / args.steps
 
     rec = {
         "metric": "global-layer ring fwd+bwd useful TFLOP/s per shard; % of bf16 MFMA peak (MI355X)",
@@ -772,7 +780,7 @@ def ring_main(args) -> int:
                    "doc_lengths": list(w.doc_len), "pairs_per_head": pairs, "useful_flop_per_step": useful},
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "ms_per_call": {nm: round(v_, 5) for nm, v_ in per.items()},
-        "one_pass_ms": round(one_ms, 5),
+        "one_pass_ms": None if one_ms is None else round(one_ms, 5),
         "roofline": {"kernel": "per-chunk backward (prep + main, all chunks)", "bound": "mfma",
                      "achieved": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(bwd_flop / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),

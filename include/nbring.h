@@ -31,7 +31,11 @@
  *
  * Conventions are those of nbattn.h (device pointers owned by the caller, work
  * enqueued on `stream`, checks before any launch, NB_* status codes, NB_BF16 /
- * NB_F32 for `dtype`, head dim 64 / 128 / 256).
+ * NB_F32 for `dtype`, head dim 64 / 128 / 256, and 512 -- the global layers'
+ * head dim, which the cp_attention page's FFPA path runs -- on the chunk
+ * attention calls).  At D = 512 each 32-row query group of the forward is
+ * split over two waves, one per half of the head dim, and the backward always
+ * takes the stored-dS form (see nb_ring_chunk_bwd_workspace_bytes).
  */
 #ifndef NBRING_H
 #define NBRING_H
@@ -59,7 +63,7 @@ int nb_ring_chunk_fwd(const void* q, const void* k, const void* v, void* out, fl
  * exp(lse_x - lse).  A row whose lse_step is -inf is left untouched (nothing to
  * merge), so the rows neither side covers keep out 0, lse -inf.  out_acc,
  * lse_acc fp32; out_step dtype, lse_step fp32; out_acc and out_step 16-byte
- * aligned; D a power of two in [4, 256].  init != 0: nothing is merged yet --
+ * aligned; D a power of two in [4, 1024].  init != 0: nothing is merged yet --
  * the accumulators are set to the step on every row (their contents ignored). */
 int nb_ring_merge(float* out_acc, float* lse_acc, const void* out_step, const float* lse_step, int64_t R, int D,
                   int dtype, int init, void* stream);
@@ -99,16 +103,17 @@ int nb_ring_finalize(const float* out_acc, void* out, void* out_resid, int64_t R
  * keys no query reaches).  Workspace: at least nb_attn_bwd_workspace_bytes(B,
  * Hq, Hkv, L, Lk, D, dtype); given nb_ring_chunk_bwd_workspace_bytes, the dK/dV
  * pass stores dS and dQ is formed from it (dK, dV bit-identical to the
- * recompute form, dQ within the usual tolerance).  Arguments as
- * nb_ring_chunk_fwd otherwise; unknown flags, or both dQ flags, are
- * NB_ERR_INVALID_ARG. */
+ * recompute form, dQ within the usual tolerance).  At D = 512 that workspace
+ * is required (NB_ERR_WORKSPACE below it; NB_ERR_UNSUPPORTED when the dS band
+ * would exceed 2 GiB).  Arguments as nb_ring_chunk_fwd otherwise; unknown
+ * flags, or both dQ flags, are NB_ERR_INVALID_ARG. */
 int nb_ring_chunk_bwd(const void* dout, const void* q, const void* k, const void* v, const void* o,
                       const void* o_resid, const float* lse, const int32_t* seg_buf, int B, int Hq, int Hkv, int L,
                       int Lk, int D, int q_start, int k_start, float scale, int dtype, void* dq, void* dk, void* dv,
                       int flags, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace for nb_ring_chunk_bwd's stored-dS form: those of
- * nb_attn_bwd_workspace_bytes plus, at D = 256, a banded dS buffer with room
+ * nb_attn_bwd_workspace_bytes plus, at D = 256 and 512, a banded dS buffer with room
  * for bands as wide as the chunk (B * Hq * round_up(L, 32) rows of
  * round_up(Lk + 96, 32) elements of dtype; at most 2 GiB, else none).  Equal to
  * nb_attn_bwd_workspace_bytes at other head dims.  Without a window every row's

@@ -47,10 +47,13 @@ namespace nb {
 // four waves per workgroup, ran the backward 1.5x slower).
 // Workgroup shape: eight waves (four groups of 32 keys or 32 query rows, two
 // roles each); the LDS of one workgroup is 160 KB / OCC at most.
+// At D = 512 (the global layers) a wave holding 32 keys' K or V rows over all
+// 512 dims plus half of their gradient's columns needs ~300 registers: four
+// waves per workgroup (one per SIMD, 512 registers each).
 template <typename T, int D>
 struct BwdShape {
   static constexpr int OCC = 1;
-  static constexpr int NT = 512;
+  static constexpr int NT = D >= 512 ? 256 : 512;
   static constexpr int LDS_BUDGET = 160 * 1024 / OCC;
 };
 
@@ -58,7 +61,13 @@ template <typename T, int D>
 struct DkvCfg {
   static constexpr int NT = BwdShape<T, D>::NT;
   static constexpr int NW = NT / 64;
-  static constexpr int NKG = NW / 2;   // key groups of 32 keys
+  // Column halves of the gradient accumulators: at D = 512 each role runs on
+  // two waves, which form the same S (or dP, dS) and keep one half of dV^T
+  // (dK^T) each -- the S / dP products are done twice (1.5x the dK/dV pass's
+  // matrix work) but no partial sums cross between waves.
+  static constexpr int HS = D >= 512 ? 2 : 1;
+  static constexpr int DA = D / HS;      // columns of one wave's accumulator
+  static constexpr int NKG = NW / (2 * HS);   // key groups of 32 keys
   static constexpr int BK = 32 * NKG;  // keys per workgroup
   static constexpr int BQ = 32;        // query rows per step
   // operand fragments read ahead of their MFMA; 0 = plain loop (D = 256 and the
@@ -77,8 +86,10 @@ struct DkvCfg {
   //  - in step, three slots (copies two steps ahead), two hand-over buffers,
   //    one barrier per step;
   //  - in step, two slots, one hand-over buffer, two barriers per step.
-  static constexpr bool SKEW = D > 128 && fits(3, 2);
-  static constexpr int STAGES = SKEW ? (fits(4, 2) ? 4 : 3) : fits(3, 2) ? 3 : 2;
+  //  - one slot (float32 at D = 512, whose Q + dO tiles take 128 KB): the
+  //    next step's copies wait for the end of the current step.
+  static constexpr bool SKEW = D > 128 && HS == 1 && fits(3, 2);
+  static constexpr int STAGES = SKEW ? (fits(4, 2) ? 4 : 3) : fits(3, 2) ? 3 : fits(2, 1) ? 2 : 1;
   static constexpr int NPEX = STAGES >= 3 ? 2 : 1;
 };
 
@@ -129,7 +140,10 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   const int n_kt = (p.S + C::BK - 1) / C::BK;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
   const int kg = w % C::NKG;                      // key group
-  const bool role_a = w < C::NKG;                 // A: S, P, dV   B: dP, dS, dK
+  const int wr = w / C::NKG;                      // role and accumulator half
+  const bool role_a = wr < C::HS;                 // A: S, P, dV   B: dP, dS, dK
+  const int hf = wr % C::HS;                      // the half of dV^T / dK^T this wave keeps
+  constexpr int NDA = C::DA / 32;                 // 32-wide column blocks of the accumulator
   const int off = p.q_off;                        // row i sits at key position off + i
   const int kor = p.k_origin;                     // row_klo values count keys from here
   const TileAccess<T, TL> acc(ln, lane);
@@ -222,7 +236,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   };
   // prologue: the copies of the first steps (all that run ahead of step 0)
 #pragma unroll
-  for (int x = 0; x < (C::SKEW ? NS - 2 : NS - 1); ++x)
+  for (int x = 0; x < (NS == 1 ? 1 : C::SKEW ? NS - 2 : NS - 1); ++x)
     if (x < n_iter) load_slot(x, x);
 
   // this lane's key row of K (role A) or V (role B): the B operand of S = Q K^T
@@ -241,9 +255,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) kv[kk] = load_frag<T>(src + 16 * kk + 8 * g);
   }
-  f32x16 gacc[D / 32];   // dV^T (role A) or dK^T (role B) of the group's keys
+  f32x16 gacc[NDA];   // dV^T (role A) or dK^T (role B) of the group's keys, columns of half hf
 #pragma unroll
-  for (int d = 0; d < D / 32; ++d) gacc[d] = f32x16{};
+  for (int d = 0; d < NDA; ++d) gacc[d] = f32x16{};
 
   // One step's facts from its slot's band starts (uniform over the workgroup):
   // the tile's rows, whether the group's keys meet their bands at all, and
@@ -300,9 +314,11 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
         }
       }
     }
+    if (hf == 0) {   // (at D = 512 the other role-A wave holds the same P)
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd)
-      px[kg][qd][lane] = f32x4{sacc[4 * qd], sacc[4 * qd + 1], sacc[4 * qd + 2], sacc[4 * qd + 3]};
+      for (int qd = 0; qd < 4; ++qd)
+        px[kg][qd][lane] = f32x4{sacc[4 * qd], sacc[4 * qd + 1], sacc[4 * qd + 2], sacc[4 * qd + 3]};
+    }
   };
   // role B: dP -> dS = P (dP - Delta) in place, P from role A
   auto to_ds = [&](f32x16& sacc, const auto& px, const float* ds) {
@@ -331,7 +347,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
     const int blk = ((b * p.Hq + kvh * grp + hh) * ds_ntq + tq) * ds_nb + ((jw - (bs0 & ~31)) >> 5);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(p.dsbuf, (short)0, p.ds_bytes, kBufferWord3);
     const int nrows = p.L - i0;
-    if (j < p.S) {
+    if (j < p.S && hf == 0) {   // (at D = 512 the other role-B wave holds the same dS)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         if (acc_row(r, g) < nrows) {
@@ -351,18 +367,19 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   };
   // gacc += src^T (P or dS): dV^T = dO^T P (role A) or dK^T = Q^T dS (role B)
   auto accumulate = [&](const T* src, const f32x16& sacc) {
+    const int d0 = hf * NDA;   // first column block of this wave's half
     if constexpr (C::AHEAD > 0) {
       const F sf[2] = {acc_to_frag<T>(sacc, 0), acc_to_frag<T>(sacc, 1)};
-      constexpr int ND = D / 32;
+      constexpr int ND = NDA;
       lds_mfma_pipeline<2 * ND, C::AHEAD, F>(
-          [&](int x) { return acc.col(src, x % ND, x / ND); },
+          [&](int x) { return acc.col(src, d0 + x % ND, x / ND); },
           [&](int x, const F& a) { gacc[x % ND] = mma(a, sf[x / ND], gacc[x % ND]); });
     } else {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const F sf = acc_to_frag<T>(sacc, m);
 #pragma unroll
-        for (int d = 0; d < D / 32; ++d) gacc[d] = mma(acc.col(src, d, m), sf, gacc[d]);
+        for (int d = 0; d < NDA; ++d) gacc[d] = mma(acc.col(src, d0 + d, m), sf, gacc[d]);
       }
     }
   };
@@ -459,6 +476,32 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
       for (int x = 0; x < NS; ++x)
         if (it + x < n_iter) stage(it + x, x);
     }
+  } else if constexpr (NS == 1) {
+    // One slot: step it's copies go out once every wave is done with step
+    // it - 1; P crosses at a barrier inside the step.
+    auto stage = [&](int it) {
+      if (it > 0) {
+        __syncthreads();   // step it - 1 is done with the slot
+        load_slot(0, it);
+      }
+      wait_global();
+      __syncthreads();
+      const StepInfo si = info(sm.klo[0], it);
+      f32x16 sacc = f32x16{};
+      if (si.active) {
+        rows_x_kv(role_a ? sm.Q[0] : sm.G[0], sacc);
+        if (role_a) to_p(sacc, sm.lse[0], sm.klo[0], si, pex[0]);
+      }
+      __syncthreads();   // the hand-over
+      if (si.active) {
+        if (!role_a) {
+          to_ds(sacc, pex[0], sm.dl[0]);
+          if (DS && p.dsbuf) store_ds(sacc, it, sm.klo[0]);
+        }
+        accumulate(role_a ? sm.G[0] : sm.Q[0], sacc);
+      }
+    };
+    for (int it = 0; it < n_iter; ++it) stage(it);
   } else {
     // Two slots, role B in step with role A: copies for step it + 1 go out
     // after the barrier at the top of step it (which also makes step it's
@@ -499,8 +542,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
     else
       dst = reinterpret_cast<T*>(role_a ? p.kv.dv[0] : p.kv.dk[0]) + (((size_t)b * p.Hkv + kvh) * p.S + j) * D;
     const float sc = role_a ? 1.f : p.scale;
+    dst += hf * C::DA;
 #pragma unroll
-    for (int d = 0; d < D / 32; ++d) {
+    for (int d = 0; d < NDA; ++d) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         store_quad<T>(dst + 32 * d + 8 * rq + 4 * g, gacc[d][4 * rq] * sc, gacc[d][4 * rq + 1] * sc,
@@ -807,9 +851,11 @@ struct DqsCfg {
   static constexpr int NW = 4;
   static constexpr int NT = 64 * NW;
   static constexpr int BM = 32 * NW;
-  static constexpr int BN = 64;   // keys per tile (no Q fragments to hold: room for 64 at D = 256)
+  // keys per tile (no Q fragments to hold: room for 64 at D = 256; 32 for a
+  // float32 tile at D = 512, so two of them fit the LDS)
+  static constexpr int BN = (sizeof(T) * D > 1024) ? 32 : 64;
   static constexpr int AHEAD = (D <= 128) ? 3 : 2;   // as the forward's P V half
-  static constexpr int OCC = (sizeof(T) == 2) ? 2 : 1;
+  static constexpr int OCC = (sizeof(T) == 2 && D <= 256) ? 2 : 1;
 };
 
 template <typename T, int D, int KV>
@@ -1157,6 +1203,26 @@ size_t dq_cross_elems(int B, int Hq, int L) { return (size_t)B * Hq * ((L + 31) 
 
 // ---------------------------------------------------------------- backward kernel
 
+template <typename T, int D>
+union BwdSmemBoth {
+  DkvSmem<T, D> kv;
+  DqSmem<T, D> q;
+};
+template <typename T, int D>
+struct BwdSmemKvOnly {
+  DkvSmem<T, D> kv;
+};
+template <typename T, int D>
+struct BwdSmemQOnly {
+  DqSmem<T, D> q;
+};
+template <typename T, int D, int MODE>
+struct BwdSmemFor {
+  typedef typename std::conditional<MODE == 1, BwdSmemKvOnly<T, D>,
+                                    typename std::conditional<MODE == 2, BwdSmemQOnly<T, D>,
+                                                              BwdSmemBoth<T, D>>::type>::type type;
+};
+
 // A persistent grid (one workgroup per CU) drains the items of the selected
 // passes (MODE bit 0: dK/dV, bit 1: dQ) from kNumQueues queues; workgroup w
 // serves queue w % NQ, which holds the flat items f = q, q + NQ, ...  The flat
@@ -1170,11 +1236,12 @@ template <typename T, int D, int MODE, int KV>
 __global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void bwd_kernel(BwdParams p) {
   static_assert(DkvCfg<T, D>::NT == BwdShape<T, D>::NT && DqCfg<T, D>::NT == BwdShape<T, D>::NT,
                 "one block shape for both passes");
-  __shared__ union BwdSmem {
-    DkvSmem<T, D> kv;
-    DqSmem<T, D> q;
-  } sm;
-  auto dkdv = [&](int f) { dkdv_item<T, D, KV != kKvConcat, MODE == 1>(p, sm.kv, f); };
+  // (a pass that runs alone needs only its own LDS: at D = 512 the dK/dV pass
+  // runs alone, and a float32 dQ item's tiles would not fit beside nothing)
+  __shared__ typename BwdSmemFor<T, D, MODE>::type sm;
+  auto dkdv = [&](int f) {
+    if constexpr (MODE != 2) dkdv_item<T, D, KV != kKvConcat, MODE == 1>(p, sm.kv, f);
+  };
   const int n_kv = (MODE & 1) ? p.B * ((p.S + DkvCfg<T, D>::BK - 1) / DkvCfg<T, D>::BK) * p.Hkv : 0;
   const int n_q = (MODE & 2) ? p.B * ((p.L + DqCfg<T, D>::BM - 1) / DqCfg<T, D>::BM) * p.Hq : 0;
   const int total = n_kv + n_q;
@@ -1292,6 +1359,30 @@ static hipError_t launch_main_t(const BwdParams& p, hipStream_t s) {
 template <typename T, int D>
 static hipError_t launch_t(const BwdParams& p, int what, hipStream_t s) {
   hipError_t e = hipSuccess;
+  if constexpr (D >= 512) {
+    // The global layers' head dim: the dK/dV items store dS and dQ = dS K runs
+    // as its own GEMM (a dQ item recomputing S and dP would not fit a wave);
+    // one concatenated K/V buffer.
+    const bool concat = p.kv.n == 1 && p.kv.start[0] == 0 && p.kv.rows[0] == p.S;
+    switch (what) {
+      case kBwdPrep:
+        return launch_prep_t<T, D>(p, true, 3, s);
+      case kBwdOrders:
+        return launch_prep_t<T, D>(p, false, 3, s);
+      case kBwdMain: {
+        if (p.dsbuf == nullptr || !concat) return hipErrorInvalidValue;
+        const long long n_kv = (long long)p.B * ((p.S + DkvCfg<T, D>::BK - 1) / DkvCfg<T, D>::BK) * p.Hkv;
+        dim3 grid1((unsigned)std::min<long long>(n_kv, (long long)device_cu_count() * BwdShape<T, D>::OCC));
+        hipLaunchKernelGGL((bwd_kernel<T, D, 1, kKvConcat>), grid1, dim3(BwdShape<T, D>::NT), 0, s, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        dim3 grid2((unsigned)((p.L + DqsCfg<T, D>::BM - 1) / DqsCfg<T, D>::BM) * p.Hq * p.B);
+        hipLaunchKernelGGL((dq_ds_kernel<T, D, kKvConcat>), grid2, dim3(DqsCfg<T, D>::NT), 0, s, p);
+        return hipGetLastError();
+      }
+    }
+    return hipErrorInvalidValue;
+  } else {
   switch (what) {
     case kBwdPrep:   // Delta + work orders of both passes
       return launch_prep_t<T, D>(p, true, 3, s);
@@ -1307,6 +1398,7 @@ static hipError_t launch_t(const BwdParams& p, int what, hipStream_t s) {
       return e != hipSuccess ? e : launch_main_t<T, D, 1>(p, s);
   }
   return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_bwd(const BwdParams& p, int D, bool f32, int what, hipStream_t s) {
@@ -1314,10 +1406,12 @@ hipError_t launch_bwd(const BwdParams& p, int D, bool f32, int what, hipStream_t
     if (D == 64) return launch_t<float, 64>(p, what, s);
     if (D == 128) return launch_t<float, 128>(p, what, s);
     if (D == 256) return launch_t<float, 256>(p, what, s);
+    if (D == 512) return launch_t<float, 512>(p, what, s);
   } else {
     if (D == 64) return launch_t<bf16, 64>(p, what, s);
     if (D == 128) return launch_t<bf16, 128>(p, what, s);
     if (D == 256) return launch_t<bf16, 256>(p, what, s);
+    if (D == 512) return launch_t<bf16, 512>(p, what, s);
   }
   return hipErrorInvalidValue;
 }

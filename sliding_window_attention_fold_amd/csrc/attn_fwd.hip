@@ -27,22 +27,59 @@
 
 namespace nb {
 
-// Two workgroups share a CU (bf16): while one runs its softmax on the vector
-// units, the other keeps the matrix cores busy, which a single wave per SIMD
-// cannot do on its own.  That needs <= 256 registers per wave and <= 80 KB of
-// LDS per workgroup, hence 32-key tiles at D = 256.  The float32 debug path
+// Two workgroups share a CU (bf16, D <= 256): while one runs its softmax on the
+// vector units, the other keeps the matrix cores busy, which a single wave per
+// SIMD cannot do on its own.  That needs <= 256 registers per wave and <= 80 KB
+// of LDS per workgroup, hence 32-key tiles at D = 256.  The float32 debug path
 // keeps one workgroup per CU.
+//
+// Head-dim split (D = 512, the global layers): a wave holding a 32-row group's
+// Q fragments and O accumulator over all 512 dims would need ~400 registers,
+// so two waves share each 32-row group, one per half of D.  Each forms the
+// partial scores of its half, the two halves meet in LDS (every wave adds the
+// two partials in the same order, so both hold bit-identical scores and run
+// the same softmax), and each accumulates O over its own half.  bf16: eight
+// waves (four row groups x two halves) with double-buffered K/V tiles, exactly
+// 160 KB of LDS with the exchange; float32: four waves (two row groups) and one
+// K/V tile pair (a float32 tile pair is 128 KB).
 template <typename T, int D>
 struct FwdCfg {
-  static constexpr int NW = 4;
+  static constexpr int DS = D >= 512 ? 2 : 1;        // waves per 32-row group (halves of D)
+  static constexpr int DW = D / DS;                  // head dims of one wave's Q fragments and O
+  static constexpr int NRG = (DS == 1 || sizeof(T) == 2) ? 4 : 2;   // 32-row groups per workgroup
+  static constexpr int NW = NRG * DS;
   static constexpr int NT = 64 * NW;
-  static constexpr int BM = 32 * NW;
+  static constexpr int BM = 32 * NRG;
   static constexpr int BN = (D <= 128) ? 64 : 32;  // keys per tile
-  static constexpr int OCC = (sizeof(T) == 2) ? 2 : 1;  // workgroups per CU
-  // operand fragments read ahead of their MFMA (fewer at D = 256, where the
-  // Q fragments and O accumulators leave little room)
-  static constexpr int AHEAD_S = (D <= 128) ? 4 : 2;
-  static constexpr int AHEAD_PV = (D <= 128) ? 3 : 2;
+  static constexpr int OCC = (sizeof(T) == 2 && D <= 256) ? 2 : 1;  // workgroups per CU
+  static constexpr int NBUF = (sizeof(T) * D > 1024) ? 1 : 2;      // K/V tile pairs in LDS
+  // operand fragments read ahead of their MFMA (fewer at 256 dims per wave,
+  // where the Q fragments and O accumulators leave little room)
+  static constexpr int AHEAD_S = (DW <= 128) ? 4 : 2;
+  static constexpr int AHEAD_PV = (DW <= 128) ? 3 : 2;
+};
+
+// LDS of the forward: the K/V tile pairs and the key-range reduction; with the
+// head-dim split also the partial scores, [wave][32-key block][value quad][lane]
+// (the reduction, done before the first tile, shares their space).
+template <typename T, int D, bool SPLIT = (FwdCfg<T, D>::DS > 1)>
+struct FwdSmem;
+template <typename T, int D>
+struct FwdSmem<T, D, false> {
+  typedef FwdCfg<T, D> C;
+  __attribute__((aligned(1024))) T K[C::NBUF][Tile<T, C::BN, D>::ELEMS];
+  __attribute__((aligned(1024))) T V[C::NBUF][Tile<T, C::BN, D>::ELEMS];
+  int red[C::NW][2];
+};
+template <typename T, int D>
+struct FwdSmem<T, D, true> {
+  typedef FwdCfg<T, D> C;
+  __attribute__((aligned(1024))) T K[C::NBUF][Tile<T, C::BN, D>::ELEMS];
+  __attribute__((aligned(1024))) T V[C::NBUF][Tile<T, C::BN, D>::ELEMS];
+  union {
+    f32x4 xs[C::NW][C::BN / 32][4][64];
+    int red[C::NW][2];
+  };
 };
 
 // KV selects how K/V rows are found: kKvConcat, one concatenated buffer
@@ -53,16 +90,18 @@ struct FwdCfg {
 // kKvPair, then kKvAny over the same grid when the chunk lengths allow such
 // ranges, so the common loop carries none of the general lookup's registers.
 template <typename T, int D, int KV>
-__global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__((FwdCfg<T, D>::NT), (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdParams p) {
   typedef FwdCfg<T, D> C;
   typedef Tile<T, C::BN, D> TL;
   typedef typename Frag<T>::type F;
-  // two K/V tile pairs: one is being filled by DMA while the other is read
-  __shared__ __attribute__((aligned(1024))) T K0[TL::ELEMS];
-  __shared__ __attribute__((aligned(1024))) T V0[TL::ELEMS];
-  __shared__ __attribute__((aligned(1024))) T K1[TL::ELEMS];
-  __shared__ __attribute__((aligned(1024))) T V1[TL::ELEMS];
-  __shared__ int red[4][2];
+  // two K/V tile pairs (one is being filled by DMA while the other is read),
+  // or one where a float32 pair fills most of the LDS
+  __shared__ FwdSmem<T, D> sm;
+  T* const K0 = sm.K[0];
+  T* const V0 = sm.V[0];
+  T* const K1 = sm.K[C::NBUF - 1];
+  T* const V1 = sm.V[C::NBUF - 1];
+  int (*red)[2] = sm.red;
 
   // Work order: the kv group (batch row, kv head) varies fastest, so with the
   // round-robin dispatch over 8 XCDs every group stays on one XCD and the K/V
@@ -74,7 +113,9 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdP
   const int b = gid / p.Hkv, kvh = gid % p.Hkv;
   const int h = kvh * grp + rest % grp, qt = rest / grp;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
-  const int i = qt * C::BM + 32 * w + ln;
+  const int rg = C::DS > 1 ? w % C::NRG : w;   // 32-row group
+  const int hf = C::DS > 1 ? w / C::NRG : 0;   // half of D (head-dim split)
+  const int i = qt * C::BM + 32 * rg + ln;
   const bool in_range = i < p.L;
   const int pq = p.q_off + i;               // the row's key position
   const int pos = min(pq, p.S - 1);         // its band's last key
@@ -124,12 +165,12 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdP
   };
   if (kstart < kend) load(K0, V0, kstart);
 
-  F qf[D / 16];
+  F qf[C::DW / 16];
   {
     // rows past L read row L-1 (in bounds) and are zeroed
-    const T* qp = reinterpret_cast<const T*>(p.q) + (((size_t)b * p.Hq + h) * p.L + min(i, p.L - 1)) * D;
+    const T* qp = reinterpret_cast<const T*>(p.q) + (((size_t)b * p.Hq + h) * p.L + min(i, p.L - 1)) * D + hf * C::DW;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
+    for (int kk = 0; kk < C::DW / 16; ++kk) {
       qf[kk] = load_frag<T>(qp + 16 * kk + 8 * g);
       if (!in_range) qf[kk] = zero_frag<T>();
     }
@@ -137,26 +178,57 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdP
 
   const TileAccess<T, TL> acc(ln, lane);  // K rows: this lane reads key row 32*sb + ln
 
-  f32x16 oacc[D / 32];
+  f32x16 oacc[C::DW / 32];
 #pragma unroll
-  for (int d = 0; d < D / 32; ++d) oacc[d] = f32x16{};
+  for (int d = 0; d < C::DW / 32; ++d) oacc[d] = f32x16{};
   // m_ref: exponent reference of the row (log2 units, scaled scores); l_run: the
   // row's sum of 2^(s - m_ref) over this lane's keys (the other half is in lane^32).
   float m_ref = -INFINITY, l_run = 0.f;
 
   auto compute = [&](const T* Ks, const T* Vs, int j0) __attribute__((always_inline)) {
-    if (j0 >= w_hi || j0 + C::BN <= w_lo) return;
+    constexpr int NSB = C::BN / 32;
+    const bool active = !(j0 >= w_hi || j0 + C::BN <= w_lo);
+    if constexpr (C::DS == 1) {
+      if (!active) return;
+    }
     const bool full = w_all_real && j0 >= w_bs_max && j0 + C::BN - 1 <= w_p_min;
-    f32x16 sacc[C::BN / 32];
-    constexpr int NK = D / 16;
+    f32x16 sacc[NSB];
+    constexpr int NK = C::DW / 16;   // contraction steps of this wave's dims
 #pragma unroll
-    for (int sb = 0; sb < C::BN / 32; ++sb) sacc[sb] = f32x16{};
-    lds_mfma_pipeline<C::BN / 32 * NK, C::AHEAD_S, F>(
-        [&](int x) { return acc.row(Ks, x / NK, x % NK); },
-        [&](int x, const F& a) { sacc[x / NK] = mma(a, qf[x % NK], sacc[x / NK]); });
+    for (int sb = 0; sb < NSB; ++sb) sacc[sb] = f32x16{};
+    if (active) {
+      lds_mfma_pipeline<NSB * NK, C::AHEAD_S, F>(
+          [&](int x) { return acc.row(Ks, x / NK, x % NK + hf * NK); },
+          [&](int x, const F& a) { sacc[x / NK] = mma(a, qf[x % NK], sacc[x / NK]); });
+    }
+    if constexpr (C::DS > 1) {
+      // the two halves' partial scores meet in LDS; every wave of the workgroup
+      // reaches the barrier, active or not
+      if (active) {
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            sm.xs[w][sb][qd][lane] = f32x4{sacc[sb][4 * qd], sacc[sb][4 * qd + 1], sacc[sb][4 * qd + 2],
+                                           sacc[sb][4 * qd + 3]};
+      }
+      __syncthreads();
+      if (!active) return;
+      const int partner = hf ? w - C::NRG : w + C::NRG;
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x4 o = sm.xs[partner][sb][qd][lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)   // half 0's partial first, in both waves
+            sacc[sb][4 * qd + e] = hf ? o[e] + sacc[sb][4 * qd + e] : sacc[sb][4 * qd + e] + o[e];
+        }
+      }
+    }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int sb = 0; sb < C::BN / 32; ++sb) {
+    for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float x = sacc[sb][r] * p.scale_log2;
@@ -177,12 +249,12 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdP
       const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int d = 0; d < D / 32; ++d) oacc[d] *= alpha;
+      for (int d = 0; d < C::DW / 32; ++d) oacc[d] *= alpha;
       m_ref = m_new;
     }
     const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
 #pragma unroll
-    for (int sb = 0; sb < C::BN / 32; ++sb) {
+    for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float e = fast_exp2(sacc[sb][r] - m_use);
@@ -193,35 +265,47 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdP
     F pf[C::BN / 16];
 #pragma unroll
     for (int m = 0; m < C::BN / 16; ++m) pf[m] = acc_to_frag<T>(sacc[m >> 1], m & 1);
-    constexpr int ND = D / 32;
+    constexpr int ND = C::DW / 32;
     lds_mfma_pipeline<C::BN / 16 * ND, C::AHEAD_PV, F>(
-        [&](int x) { return acc.col(Vs, x % ND, x / ND); },
+        [&](int x) { return acc.col(Vs, x % ND + hf * ND, x / ND); },
         [&](int x, const F& a) { oacc[x % ND] = mma(a, pf[x / ND], oacc[x % ND]); });
   };
 
-  // Double-buffered key loop: the DMA of the next tile is issued right after
-  // the barrier that frees its buffer, then the current tile is computed.
-  for (int j0 = kstart; j0 < kend; j0 += 2 * C::BN) {
-    wait_global();
-    __syncthreads();
-    if (j0 + C::BN < kend) load(K1, V1, j0 + C::BN);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(K0, V0, j0);
-    if (j0 + C::BN >= kend) break;
-    wait_global();
-    __syncthreads();
-    if (j0 + 2 * C::BN < kend) load(K0, V0, j0 + 2 * C::BN);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(K1, V1, j0 + C::BN);
+  if constexpr (C::NBUF == 2) {
+    // Double-buffered key loop: the DMA of the next tile is issued right after
+    // the barrier that frees its buffer, then the current tile is computed.
+    for (int j0 = kstart; j0 < kend; j0 += 2 * C::BN) {
+      wait_global();
+      __syncthreads();
+      if (j0 + C::BN < kend) load(K1, V1, j0 + C::BN);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(K0, V0, j0);
+      if (j0 + C::BN >= kend) break;
+      wait_global();
+      __syncthreads();
+      if (j0 + 2 * C::BN < kend) load(K0, V0, j0 + 2 * C::BN);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(K1, V1, j0 + C::BN);
+    }
+  } else {
+    // One tile pair: the next tile's copy waits until every wave is done
+    // with the current one.
+    for (int j0 = kstart; j0 < kend; j0 += C::BN) {
+      wait_global();
+      __syncthreads();
+      compute(K0, V0, j0);
+      __syncthreads();
+      if (j0 + C::BN < kend) load(K0, V0, j0 + C::BN);
+    }
   }
 
   const float l = l_run + __shfl_xor(l_run, 32);
   if (!in_range) return;
   const float inv = real ? 1.f / l : 0.f;
-  T* op = reinterpret_cast<T*>(p.o) + qrow * D;
-  T* olp = p.o_lo ? reinterpret_cast<T*>(p.o_lo) + qrow * D : nullptr;
+  T* op = reinterpret_cast<T*>(p.o) + qrow * D + hf * C::DW;
+  T* olp = p.o_lo ? reinterpret_cast<T*>(p.o_lo) + qrow * D + hf * C::DW : nullptr;
 #pragma unroll
-  for (int d = 0; d < D / 32; ++d) {
+  for (int d = 0; d < C::DW / 32; ++d) {
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       const int dd = 32 * d + 8 * rq + 4 * g;
@@ -229,7 +313,7 @@ __global__ __launch_bounds__(256, (FwdCfg<T, D>::OCC)) void attn_fwd_kernel(FwdP
                           oacc[d][4 * rq + 2] * inv, oacc[d][4 * rq + 3] * inv);
     }
   }
-  if (g == 0) p.lse[qrow] = real ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
+  if (g == 0 && hf == 0) p.lse[qrow] = real ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
 }
 
 // The concatenated neighbourhood: one chunk of S rows starting at row 0.
@@ -239,15 +323,21 @@ template <typename T, int D>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   typedef FwdCfg<T, D> C;
   dim3 grid((unsigned)((p.L + C::BM - 1) / C::BM) * p.Hq * p.B);
-  if (kv_concatenated(p.kv, p.S)) {
+  if constexpr (D >= 512) {   // the global layers' head dim: one concatenated K/V buffer only
+    if (!kv_concatenated(p.kv, p.S)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attn_fwd_kernel<T, D, kKvConcat>), grid, dim3(C::NT), 0, s, p);
     return hipGetLastError();
+  } else {
+    if (kv_concatenated(p.kv, p.S)) {
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D, kKvConcat>), grid, dim3(C::NT), 0, s, p);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, kKvPair>), grid, dim3(C::NT), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !kv_may_need_general(p.kv, p.window, C::BM, C::BN)) return e;
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, kKvAny>), grid, dim3(C::NT), 0, s, p);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, kKvPair>), grid, dim3(C::NT), 0, s, p);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !kv_may_need_general(p.kv, p.window, C::BM, C::BN)) return e;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, kKvAny>), grid, dim3(C::NT), 0, s, p);
-  return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd(const FwdParams& p, int D, bool f32, hipStream_t s) {
@@ -255,10 +345,12 @@ hipError_t launch_attn_fwd(const FwdParams& p, int D, bool f32, hipStream_t s) {
     if (D == 64) return launch_fwd_t<float, 64>(p, s);
     if (D == 128) return launch_fwd_t<float, 128>(p, s);
     if (D == 256) return launch_fwd_t<float, 256>(p, s);
+    if (D == 512) return launch_fwd_t<float, 512>(p, s);
   } else {
     if (D == 64) return launch_fwd_t<bf16, 64>(p, s);
     if (D == 128) return launch_fwd_t<bf16, 128>(p, s);
     if (D == 256) return launch_fwd_t<bf16, 256>(p, s);
+    if (D == 512) return launch_fwd_t<bf16, 512>(p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -38,15 +38,17 @@ int map_hip(hipError_t e) {
   return NB_ERR_LAUNCH;
 }
 
+// allow512: head dim 512 (the global layers) is accepted -- by the ring chunk
+// entry points only, whose backward takes the stored-dS form it requires.
 int attn_common_checks(const void* const* ptrs, int nptrs, int B, int Hq, int Hkv, int L, int S, int D,
-                       float scale, int dtype) {
+                       float scale, int dtype, bool allow512 = false) {
   for (int x = 0; x < nptrs; ++x)
     if (ptrs[x] == nullptr || !aligned16(ptrs[x])) return NB_ERR_INVALID_ARG;
   if (!dims_ok(B, L, S)) return NB_ERR_INVALID_ARG;
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Hq > 65535) return NB_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !std::isfinite(scale)) return NB_ERR_INVALID_ARG;
   if (dtype != NB_BF16 && dtype != NB_F32) return NB_ERR_UNSUPPORTED;
-  if (D != 64 && D != 128 && D != 256) return NB_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128 && D != 256 && !(allow512 && D == 512)) return NB_ERR_UNSUPPORTED;
   if ((int64_t)B * Hq * L >= kMaxIndex * 2 || (int64_t)B * Hkv * S >= kMaxIndex * 2) return NB_ERR_INVALID_ARG;
   return NB_OK;
 }
@@ -106,7 +108,8 @@ const char* nb_status_string(int status) {
   switch (status) {
     case NB_OK: return "ok";
     case NB_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or shape)";
-    case NB_ERR_UNSUPPORTED: return "unsupported (head dim not in {64,128,256}, unknown dtype, or dropout)";
+    case NB_ERR_UNSUPPORTED:
+      return "unsupported (head dim not in {64,128,256} -- 512 on the ring chunk calls --, unknown dtype, or dropout)";
     case NB_ERR_WORKSPACE: return "workspace or segment buffer too small";
     case NB_ERR_LAUNCH: return "HIP kernel launch failed";
     case NB_ERR_DEVICE: return "no usable gfx950 device";
@@ -250,13 +253,13 @@ constexpr int kMaxDsWindow = 4096;
 // the last row's position, 31 rows further.
 int ds_width(int span) { return (span + 96 + 31) / 32 * 32; }
 size_t ds_bytes_span(int B, int Hq, int L, int D, int span, int dtype) {
-  if (D != 256 || span < 0 || B < 1 || Hq < 1 || L < 1) return 0;
+  if ((D != 256 && D != 512) || span < 0 || B < 1 || Hq < 1 || L < 1) return 0;
   const size_t n = ((size_t)B * Hq * ((L + 31) / 32 * 32) * ds_width(span) * (dtype == NB_F32 ? 4 : 2) + 255) &
                    ~(size_t)255;
   return n < ((size_t)1 << 31) ? n : 0;   // buffer offsets stay in 31 bits
 }
 size_t ds_bytes(int B, int Hq, int L, int D, int window, int dtype) {
-  return window > kMaxDsWindow ? 0 : ds_bytes_span(B, Hq, L, D, window, dtype);
+  return (window > kMaxDsWindow || D != 256) ? 0 : ds_bytes_span(B, Hq, L, D, window, dtype);
 }
 // Turns the stored-dS backward on when the workspace holds the buffer.
 void enable_ds(nb::BwdParams& p, void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int L, int S, int D,
@@ -481,7 +484,7 @@ int nb_ring_chunk_fwd(const void* q, const void* k, const void* v, void* out, fl
                       int B, int Hq, int Hkv, int L, int Lk, int D, int q_start, int k_start, float scale, int dtype,
                       void* stream) {
   const void* ptrs[] = {q, k, v, out, lse, seg_buf};
-  int st = attn_common_checks(ptrs, 6, B, Hq, Hkv, L, Lk, D, scale, dtype);
+  int st = attn_common_checks(ptrs, 6, B, Hq, Hkv, L, Lk, D, scale, dtype, true);
   if (st != NB_OK) return st;
   if (k_start < 0 || k_start > q_start || (int64_t)q_start + L >= kMaxIndex) return NB_ERR_INVALID_ARG;
   return attn_fwd_kv(q, one_chunk(Lk, k, v, nullptr, nullptr), out, nullptr, lse, seg_buf, B, Hq, Hkv, L, Lk, D,
@@ -493,7 +496,7 @@ int nb_ring_chunk_bwd(const void* dout, const void* q, const void* k, const void
                       int Lk, int D, int q_start, int k_start, float scale, int dtype, void* dq, void* dk, void* dv,
                       int flags, void* ws, size_t ws_bytes, void* stream) {
   const void* ptrs[] = {dout, q, k, v, o, lse, seg_buf, dq, dk, dv, ws};
-  int st = attn_common_checks(ptrs, 11, B, Hq, Hkv, L, Lk, D, scale, dtype);
+  int st = attn_common_checks(ptrs, 11, B, Hq, Hkv, L, Lk, D, scale, dtype, true);
   if (st != NB_OK) return st;
   if (o_resid != nullptr && !aligned16(o_resid)) return NB_ERR_INVALID_ARG;
   if (k_start < 0 || k_start > q_start || (int64_t)q_start + L >= kMaxIndex) return NB_ERR_INVALID_ARG;
@@ -505,9 +508,12 @@ int nb_ring_chunk_bwd(const void* dout, const void* q, const void* k, const void
                                scale, -1, dq, ws, q_start - k_start, k_start);
   p.dq_mode = (flags & NB_RING_DQ_F32_SET) ? nb::kDqSetF32 : (flags & NB_RING_DQ_F32_ADD) ? nb::kDqAddF32
                                                                                             : nb::kDqStore;
-  // with room for a dS band as wide as the chunk: the stored-dS form
+  // with room for a dS band as wide as the chunk: the stored-dS form (the
+  // only form at D = 512, where a dQ pass recomputing S and dP does not fit)
   const size_t base = nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, Lk, D, dtype);
   const size_t db = ds_bytes_span(B, Hq, L, D, Lk, dtype);
+  if (D == 512 && db == 0) return NB_ERR_UNSUPPORTED;          // dS band over 2 GiB
+  if (D == 512 && ws_bytes < base + db) return NB_ERR_WORKSPACE;
   if (db != 0 && ws_bytes >= base + db) {
     p.dsbuf = reinterpret_cast<char*>(ws) + base;
     p.ds_w = ds_width(Lk);

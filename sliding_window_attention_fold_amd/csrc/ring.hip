@@ -38,18 +38,26 @@ __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
 }
 
 // One row's merge, by the D / 4 lanes that hold it (lane part c: values 4c..4c+3).
+// A row may span several waves (D > 256), so every lane reads the row's two
+// LSEs, then the whole workgroup meets at a barrier, and only then does the
+// row's lane 0 overwrite lse_acc: no lane can read the new value.  Lanes
+// without a row (`row` < 0) take part in the barrier only.
 template <typename T>
 __device__ __forceinline__ void merge_row(float* out_acc, float* lse_acc, const T* out_step, const float* lse_step,
-                                          size_t row, int D, int c) {
-  const float b = lse_step[row];
-  if (b == -INFINITY) return;          // the chunk gave this row nothing
-  const float a = lse_acc[row];
-  const float m = fmaxf(a, b);         // finite: b is
+                                          int64_t row, int D, int c) {
+  float a = -INFINITY, b = -INFINITY;
+  if (row >= 0) {
+    b = lse_step[row];
+    a = lse_acc[row];
+  }
+  __syncthreads();
+  if (row < 0 || b == -INFINITY) return;   // no row, or the chunk gave this row nothing
+  const float m = fmaxf(a, b);             // finite: b is
   const float lse = m + logf(expf(a - m) + expf(b - m));
   const float wa = expf(a - lse), wb = expf(b - lse);
-  float* o = out_acc + row * D + 4 * c;
+  float* o = out_acc + (size_t)row * D + 4 * c;
   const f32x4 x = *reinterpret_cast<const f32x4*>(o);
-  const f32x4 y = load4<T>(out_step + row * D + 4 * c);
+  const f32x4 y = load4<T>(out_step + (size_t)row * D + 4 * c);
   *reinterpret_cast<f32x4*>(o) = f32x4{wa * x[0] + wb * y[0], wa * x[1] + wb * y[1], wa * x[2] + wb * y[2],
                                        wa * x[3] + wb * y[3]};
   if (c == 0) lse_acc[row] = lse;
@@ -61,14 +69,14 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(float* out_acc, float* 
                                                          const float* lse_step, int64_t R, int D, int init) {
   const int tpr = D / 4, rpb = kThreads / tpr;
   const int64_t row = (int64_t)blockIdx.x * rpb + threadIdx.x / tpr;
-  if (row >= R) return;
   const int c = threadIdx.x % tpr;
   if (init) {
+    if (row >= R) return;
     *reinterpret_cast<f32x4*>(out_acc + (size_t)row * D + 4 * c) = load4<T>(out_step + (size_t)row * D + 4 * c);
     if (c == 0) lse_acc[row] = lse_step[row];
     return;
   }
-  merge_row<T>(out_acc, lse_acc, out_step, lse_step, (size_t)row, D, c);
+  merge_row<T>(out_acc, lse_acc, out_step, lse_step, row < R ? row : -1, D, c);
 }
 
 template <typename T>
@@ -78,13 +86,16 @@ __global__ __launch_bounds__(kThreads) void merge_live_kernel(float* out_acc, fl
                                                               int D) {
   const int tpr = D / 4, rpb = kThreads / tpr;
   const int64_t t = (int64_t)blockIdx.x * rpb + threadIdx.x / tpr;   // (live row, head), head fastest
-  if (t >= tasks) return;
-  const int64_t x = t / H;
-  if (x >= *n_live) return;
-  const int h = (int)(t % H);
-  const int flat = live_index[x];
-  const int b = flat / L, i = flat % L;
-  const size_t row = ((size_t)b * H + h) * L + i;
+  int64_t row = -1;
+  if (t < tasks) {
+    const int64_t x = t / H;
+    if (x < *n_live) {
+      const int h = (int)(t % H);
+      const int flat = live_index[x];
+      const int b = flat / L, i = flat % L;
+      row = ((int64_t)b * H + h) * L + i;
+    }
+  }
   merge_row<T>(out_acc, lse_acc, out_step, lse_step, row, D, threadIdx.x % tpr);
 }
 
@@ -143,8 +154,9 @@ __global__ __launch_bounds__(kThreads) void grad_add_kernel(float* acc, const T*
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-// a row's lanes sit in one wave (they read lse_acc before lane 0 rewrites it)
-bool row_width_ok(int D) { return D >= 4 && D <= 256 && (D & (D - 1)) == 0; }
+// a row's D / 4 lanes sit in one workgroup (the merge's barrier orders the
+// reads of lse_acc before its rewrite)
+bool row_width_ok(int D) { return D >= 4 && D <= 4 * kThreads && (D & (D - 1)) == 0; }
 constexpr int64_t kMaxGrid = (int64_t)1 << 31;
 
 int status(hipError_t e) { return e == hipSuccess ? NB_OK : NB_ERR_LAUNCH; }

@@ -129,7 +129,8 @@ def finalize(out_acc: torch.Tensor, dtype: torch.dtype, with_resid: bool = True)
 
 
 def _ws_bytes(lib, B, Hq, Hkv, L, Lk, D, dt, stored_ds):
-    return (lib.nb_ring_chunk_bwd_workspace_bytes(B, Hq, Hkv, L, Lk, D, dt) if stored_ds
+    # D = 512 has only the stored-dS form
+    return (lib.nb_ring_chunk_bwd_workspace_bytes(B, Hq, Hkv, L, Lk, D, dt) if stored_ds or D >= 512
             else lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, Lk, D, dt))
 
 
@@ -142,7 +143,8 @@ def chunk_bwd(dout, q, k, v, o, o_resid, lse, segs: RingSegments, k_start: int, 
     ``delta_ready``: ``ws`` holds Delta from an earlier call.  ``stored_ds``: a
     workspace with room for dS (at D = 256 the library then stores dS and forms
     dQ from it whenever ``ws`` is that large; without a window the band spans
-    the chunk, which pays only where few rows reach it)."""
+    the chunk, which pays only where few rows reach it).  At D = 512 the
+    stored-dS form is the only one and its workspace is always given."""
     B, Hq, Hkv, L, Lk, D = _dims(q, k)
     scale = D ** -0.5 if scale is None else float(scale)
     lib = _lib.load()

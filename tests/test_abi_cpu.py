@@ -205,3 +205,23 @@ def test_noalloc_backward_rejects_sizes_beyond_its_static_workspace():
     assert call(1, 8, 2, 100, 200, 96) == _lib.NB_ERR_UNSUPPORTED       # head dim
     # the largest workload here fits (config 4: 32 heads x 8192 rows, 65536 keys)
     assert lib.nb_attn_bwd_workspace_bytes(1, 32, 8, 8192, 65536, 128, _lib.NB_BF16) <= cap
+
+
+def test_head_dim_512_only_on_the_ring_chunk_calls():
+    """The global layers' head dim (512) is taken by nb_ring_chunk_fwd / _bwd only; their
+    backward's stored-dS workspace is then required (dQ = dS K is the only dQ pass at 512)."""
+    lib = _lib.load()
+    bf = _lib.NB_BF16
+    assert _fwd(D=512) == _lib.NB_ERR_UNSUPPORTED
+    assert _bwd([0, 16], 1, D=512) == _lib.NB_ERR_UNSUPPORTED
+    ring = lib.nb_ring_chunk_bwd_workspace_bytes
+    need = ring(1, 2, 1, 40, 64, 512, bf)
+    assert need == lib.nb_attn_bwd_workspace_bytes(1, 2, 1, 40, 64, 512, bf) + _r256(2 * 64 * 160 * 2)
+    def rbwd(ws_bytes, D=512):
+        return lib.nb_ring_chunk_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 2, 1, 40, 64, D, 128, 64,
+                                     D ** -0.5, bf, FAKE, FAKE, FAKE, 0, FAKE, ws_bytes, None)
+    assert rbwd(need - 1) == _lib.NB_ERR_WORKSPACE          # refused before any launch
+    assert rbwd(need, D=1024) == _lib.NB_ERR_UNSUPPORTED
+    # a dS band over 2 GiB (32 heads x 8192 rows x 8288 keys x 2 bytes): unsupported at 512
+    assert lib.nb_ring_chunk_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 32, 8, 8192, 8192, 512, 8192, 0,
+                                 512 ** -0.5, bf, FAKE, FAKE, FAKE, 0, FAKE, 1 << 40, None) == _lib.NB_ERR_UNSUPPORTED

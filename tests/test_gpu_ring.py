@@ -5,8 +5,8 @@ Per-chunk forward (own chunk causal, earlier owners' chunks non-causal) and
 backward with the global out/lse, the -inf-safe merge and its live-row form
 (the live-row list bit-exact), the final rounding, and the whole ring of a
 rank against one softmax over its causal neighbourhood; bf16 and float32, head
-dims 64 / 128 / 256, padding tails, several batch rows, GQA.  Tolerances as in
-gpu_cases (bf16 2e-2, float32 1e-4; -inf LSE exactly).
+dims 64 / 128 / 256 / 512, padding tails, several batch rows, GQA.  Tolerances as
+in gpu_cases (bf16 2e-2, float32 1e-4; -inf LSE exactly).
 """
 import numpy as np
 import pytest
@@ -63,6 +63,11 @@ CASES = [  # seed, B, Hq, Hkv, D, Lc, P, rank, doc lengths lo..hi, pad tail, dty
     (5, 2, 2, 2, 256, 70, 3, 1, 30, 90, 5, "f32"),
     (6, 1, 2, 1, 64, 100, 4, 3, 400, 400, 0, "bf16"),   # one document over the whole sequence
     (7, 1, 4, 1, 256, 97, 4, 3, 5, 60, 11, "bf16"),     # stored dS: ragged chunks, short documents, padding
+    # the global layers' head dim: the forward's head-dim split and the stored-dS backward
+    (8, 1, 2, 1, 512, 96, 3, 2, 10, 120, 0, "bf16"),
+    (9, 1, 4, 1, 512, 130, 4, 3, 30, 300, 13, "bf16"),   # GQA 4, ragged chunks, padding tail
+    (10, 2, 4, 2, 512, 70, 3, 1, 5, 60, 7, "f32"),       # two batch rows, short documents, padding
+    (11, 1, 2, 2, 512, 64, 3, 2, 200, 200, 0, "f32"),    # one document over the whole sequence
 ]
 
 
@@ -205,13 +210,35 @@ def test_rejects_a_later_owner_chunk():
         ring.chunk_fwd(q, k, k, segs, 64)
 
 
-def test_full_size_ring_sampled_rows_and_sum_rules():
+def _sampled_keys_check(w, ids, q, k, v, do, dks, dvs, out_np, lse_np, order, r, Lc, kvh, n_keys=6, seed=0):
+    """dK/dV element by element at sampled keys of every chunk, from the oracle's per-chunk backward over
+    every query row of the shard (one kv head and its q heads; the global out/lse as the kernels take them)."""
+    rng = np.random.default_rng(seed)
+    grp = w.Hq // w.Hkv
+    heads = slice(kvh * grp, (kvh + 1) * grp)
+    q0 = r * Lc
+    q_ids = ids[:, q0:q0 + Lc]
+    scale = w.D ** -0.5
+    for c, o in enumerate(order):
+        keys = np.unique(np.concatenate([[0, Lc - 1], rng.integers(0, Lc, n_keys)]))
+        kk, vv = k[:, kvh:kvh + 1, o * Lc:(o + 1) * Lc], v[:, kvh:kvh + 1, o * Lc:(o + 1) * Lc]
+        _, bk, bv = ro.chunk_backward(q[:, heads], kk, vv, do[:, heads], out_np[:, heads], lse_np[:, heads], q_ids,
+                                      ids[:, o * Lc:(o + 1) * Lc], q0, o * Lc, o == r, scale)
+        assert_close(f"dK owner {o} keys", dks[c][:, kvh:kvh + 1, keys].float().cpu().numpy(), bk[:, :, keys], "bf16")
+        assert_close(f"dV owner {o} keys", dvs[c][:, kvh:kvh + 1, keys].float().cpu().numpy(), bv[:, :, keys], "bf16")
+
+
+@pytest.mark.parametrize("D", [256, 512])
+def test_full_size_ring_sampled_rows_and_sum_rules(D):
     """The bench workload at its real size (config 2's world as a global layer: rank 3 of 4, chunks of 4096,
-    Hq=16, Hkv=8, D=256, bf16): sampled rows of out, lse and dQ against the oracle, and two rules that hold
-    at any size -- over all chunks and keys, dV sums to the group's dO over its real rows (each real row's
-    probabilities sum to one) and dK sums to zero (each real row's dS sums to zero)."""
+    Hq=16, Hkv=8, bf16), at head dim 256 and at the global layers' 512: sampled rows of out, lse and dQ, and
+    sampled keys of every chunk's dK / dV, against the oracle, and two rules that hold at any size -- over all
+    chunks and keys, dV sums to the group's dO over its real rows (each real row's probabilities sum to one)
+    and dK sums to zero (each real row's dS sums to zero)."""
+    import dataclasses
+
     from sliding_window_attention_fold_amd import workloads as wl
-    w = wl.get(2)
+    w = dataclasses.replace(wl.get(2), D=D)
     r, Lc, D = w.cp_rank, w.L, w.D
     S = (r + 1) * Lc
     glob, pad = wl.global_doc_map(w)
@@ -256,6 +283,7 @@ def test_full_size_ring_sampled_rows_and_sum_rules():
             assert_close(f"out rows {i0}+ head {h}", out_np[:, h:h + 1, rows], acc, "bf16")
             assert_close(f"lse rows {i0}+ head {h}", lse_np[:, h:h + 1, rows], lacc, "bf16")
             assert_close(f"dQ rows {i0}+ head {h}", dq[:, h:h + 1, rows].cpu().numpy(), dq_ref, "bf16")
+    _sampled_keys_check(w, ids, q, k, v, do, dks, dvs, out_np, lse_np, order, r, Lc, kvh=w.Hkv - 1, seed=D)
     real = torch.from_numpy(ids[:, q0:q0 + Lc] > 0)
     dv_sum = sum(t.double().sum(dim=2) for t in dvs).cpu()                    # [B, Hkv, D]
     dk_sum = sum(t.double().sum(dim=2) for t in dks).cpu()
