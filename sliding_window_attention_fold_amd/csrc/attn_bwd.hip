@@ -1008,35 +1008,50 @@ __global__ __launch_bounds__(256, (DqsCfg<T, D>::OCC)) void dq_ds_kernel(BwdPara
 // ---------------------------------------------------------------- Delta
 
 // Delta_i = dO_i . O_i for every row (b, h, i), with O the stored value plus
-// its saved rounding residual (fp32-accurate); 0 for padding rows.  Two rows
-// per wave, 32 lanes per row, D / 32 consecutive elements per lane.
-constexpr int kDeltaRowsPerWg = 8;   // 4 waves x 2 rows (half a wave per row); small workgroups stream best
+// its saved rounding residual (fp32-accurate); 0 for padding rows.  Every lane
+// reads 16 bytes of a row per tensor (D / 8 lanes per bf16 row, D / 4 per
+// float32 row) and handles IT rows, all of whose loads are issued before any
+// arithmetic, so each lane keeps 3 x IT 16-byte loads in flight; the lanes of a
+// row reduce with shuffles.  (Eight rows per workgroup with 4- to 16-byte
+// loads launched one workgroup per 12 KB moved and measured about half the
+// HBM rate.)
+template <typename T, int D>
+struct DeltaCfg {
+  // elements per load: 16 bytes, or more where a row would need more than a wave
+  static constexpr int V = (16 / (int)sizeof(T)) * 64 >= D ? 16 / (int)sizeof(T) : D / 64;
+  static constexpr int LPR = D / V;               // lanes per row
+  static constexpr int RPI = 64 / LPR;            // rows of a wave per load round
+  static constexpr int IT = D >= 512 ? 2 : D >= 256 ? 1 : 4;   // load rounds in flight (measured per head dim)
+  static constexpr int ROWS = 4 * RPI * IT;       // rows per workgroup (four waves)
+  static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "a row's lanes tile the wave");
+};
 
 template <typename T, int D>
 __device__ __forceinline__ void delta_rows(const BwdParams& p, int wg) {
-  constexpr int E = D / 32;
-  constexpr int R = kDeltaRowsPerWg / 8;   // row pairs per wave, loaded together
-  typedef T VE __attribute__((ext_vector_type(E)));   // the lane's E elements, one vector load
-  const int lane = threadIdx.x & 63, l32 = lane & 31;
+  typedef DeltaCfg<T, D> C;
+  typedef T VE __attribute__((ext_vector_type(C::V)));   // one 16-byte (or wider) load
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int sub = lane % C::LPR, rsub = lane / C::LPR;
   const long long n_rows = (long long)p.B * p.Hq * p.L;
-  VE dv[R], ov[R], lv[R];
-  long long row[R];
+  VE dv[C::IT], ov[C::IT], lv[C::IT];
+  long long row[C::IT];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    row[r] = (long long)wg * kDeltaRowsPerWg + ((threadIdx.x >> 6) * R + r) * 2 + (lane >> 5);
+  for (int r = 0; r < C::IT; ++r) {
+    row[r] = (long long)wg * C::ROWS + (w * C::IT + r) * C::RPI + rsub;
     const long long rr = row[r] < n_rows ? row[r] : n_rows - 1;
-    dv[r] = *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.dout) + rr * D + l32 * E);
-    ov[r] = *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.o) + rr * D + l32 * E);
-    lv[r] = p.o_lo ? *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.o_lo) + rr * D + l32 * E) : ov[r];
+    const size_t e0 = (size_t)rr * D + (size_t)sub * C::V;
+    dv[r] = *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.dout) + e0);
+    ov[r] = *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.o) + e0);
+    lv[r] = p.o_lo ? *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.o_lo) + e0) : ov[r];
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int r = 0; r < C::IT; ++r) {
     float part = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) part += to_f32(dv[r][e]) * (to_f32(ov[r][e]) + (p.o_lo ? to_f32(lv[r][e]) : 0.f));
+    for (int e = 0; e < C::V; ++e) part += to_f32(dv[r][e]) * (to_f32(ov[r][e]) + (p.o_lo ? to_f32(lv[r][e]) : 0.f));
 #pragma unroll
-    for (int o = 16; o > 0; o >>= 1) part += __shfl_xor(part, o);
-    if (row[r] < n_rows && l32 == 0) {
+    for (int o = C::LPR / 2; o > 0; o >>= 1) part += __shfl_xor(part, o);
+    if (row[r] < n_rows && sub == 0) {
       const int i = (int)(row[r] % p.L), b = (int)(row[r] / ((long long)p.Hq * p.L));
       const bool real = p.row_klo[(size_t)b * p.L + i] - p.k_origin <= p.q_off + i;
       p.delta[row[r]] = real ? part : 0.f;
@@ -1158,7 +1173,7 @@ __device__ void work_order(const BwdParams& p, int modes, unsigned long long* ke
 
 // The prep launch: workgroup 0 computes the work orders (dispatched first, so
 // the serial sort overlaps the streaming), workgroups 1 .. gridDim.x - 1 form
-// Delta (kDeltaRowsPerWg rows each); a grid of one workgroup computes the
+// Delta (DeltaCfg::ROWS rows each); a grid of one workgroup computes the
 // orders only.
 // Owner o is attended iff some real key of its range [off[o], off[o + 1]) lies
 // at or after its batch row's kcov_lo (the first key any segment covers): one
@@ -1302,7 +1317,8 @@ static hipError_t launch_prep_t(const BwdParams& p, bool with_delta, int modes, 
   typedef DqCfg<T, D> CQ;
   static_assert(CK::BK >= 32 && CQ::BM >= 32, "the work-order arrays are sized for tiles of >= 32");
   const long long rows = (long long)p.B * p.Hq * p.L;
-  const unsigned n_delta = with_delta ? (unsigned)((rows + kDeltaRowsPerWg - 1) / kDeltaRowsPerWg) : 0u;
+  constexpr int RW = DeltaCfg<T, D>::ROWS;
+  const unsigned n_delta = with_delta ? (unsigned)((rows + RW - 1) / RW) : 0u;
   if (p.own.n_owner > 0)
     hipLaunchKernelGGL((bwd_prep_kernel<T, D, CK::BK, CK::BQ, CQ::BM, true>), dim3(n_delta + 1 + p.own.n_owner),
                        dim3(kPrepNT), 0, s, p, modes);
