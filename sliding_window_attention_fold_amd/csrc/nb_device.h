@@ -221,6 +221,48 @@ __device__ __forceinline__ void dma_tile(T* lds, const T* __restrict__ src, int 
 // slow path for the last, partial tile).
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
+// ---------------------------------------------------------------------------
+// Copies into LDS issued through inline asm ("unseen" copies).  The compiler
+// does not know these instructions write LDS, so it adds no waits of its own:
+// where a ring's slot index is a run-time value it cannot tell a copy's LDS
+// destination from the slot a later LDS read uses, and would wait for every
+// copy in flight before each such read -- including the copies just issued
+// for later steps, which serialises the ring.  The caller orders every LDS
+// read of a destination after its copies with wait_global / wait_global_le
+// (and a barrier where other waves read it).  The instructions write no
+// register; M0 is set inside the asm and declared clobbered.
+// ---------------------------------------------------------------------------
+// Raw buffer descriptor words (base, stride 0, num_records bytes, kBufferWord3).
+__device__ __forceinline__ u32x4 buffer_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, (uint32_t)kBufferWord3};
+}
+// LDS byte address of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// 16 bytes per lane from rsrc + voff into LDS at lds_byte + 16 * lane (wave-uniform lds_byte).
+__device__ __forceinline__ void unseen_copy16(const u32x4& rsrc, uint32_t lds_byte, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_byte)), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+// 4 bytes per lane from gaddr into LDS at lds_byte + 4 * lane.
+__device__ __forceinline__ void unseen_copy4(const void* gaddr, uint32_t lds_byte) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_byte)), "v"(gaddr)
+      : "memory", "m0");
+}
+
+
 template <typename T, int ROWS, int D, int NW>
 struct TileDma {
   typedef Tile<T, ROWS, D> TL;
@@ -289,6 +331,24 @@ struct TileDma {
     }
 #endif
   }
+  // issue() through unseen copies (see unseen_copy16).
+  __device__ __forceinline__ void issue_unseen(T* lds, const T* __restrict__ src, int nrows) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int w = wave_id(), l = threadIdx.x & 63;
+    const uint32_t lb = lds_addr(lds);
+    const u32x4 rs = buffer_words(src, (uint32_t)(min(nrows, ROWS) * RB));
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      const int blk = w + x * NW;
+      uint32_t o = voff[x];
+      if (nrows < ROWS) {
+        const int r = (blk * 64 + l) / TL::CPR;
+        o -= (uint32_t)((r - min(r, nrows - 1)) * RB);
+      }
+      if (TL::BLOCKS % NW == 0 || blk < TL::BLOCKS) unseen_copy16(rs, lb + (uint32_t)(blk * 64 * TL::EPC * sizeof(T)), o);
+    }
+#endif
+  }
   __device__ __forceinline__ void issue(T* lds, const T* __restrict__ src, int nrows) const {
     // The buffer-resource type exists only for the device target; the host
     // pass (which only needs the kernels' launch stubs) sees an empty body.
@@ -322,10 +382,12 @@ struct TileDma {
 
 // Asynchronous copy of n <= 64 consecutive 4-byte words (one wave; lanes >= n
 // repeat word n-1).  The destination must hold 64 words.
+template <bool UNSEEN = false>
 __device__ __forceinline__ void dma_words(void* lds, const void* __restrict__ src, int n) {
   const int l = threadIdx.x & 63;
   const char* g = reinterpret_cast<const char*>(src) + 4 * min(l, n - 1);
-  __builtin_amdgcn_global_load_lds(NB_GLOBAL(g), NB_LOCAL(lds), 4, 0, 0);
+  if constexpr (UNSEEN) unseen_copy4(g, lds_addr(lds));
+  else __builtin_amdgcn_global_load_lds(NB_GLOBAL(g), NB_LOCAL(lds), 4, 0, 0);
 }
 
 // Scheduling hints: interleave N MFMAs each preceded by R LDS reads, so that
