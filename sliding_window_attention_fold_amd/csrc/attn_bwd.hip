@@ -219,28 +219,20 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   const float* const dl_it = p.delta + hb;
   const int* const klo_it = p.row_klo + (size_t)b * p.L;
   const int Lr = p.L;
-  // The skewed schedule indexes its slots at run time, so its copies are
-  // unseen (nb_device.h): the compiler would otherwise wait for the copies of
-  // later steps before every LDS read; its own counted waits order each slot's
-  // reads after that slot's copies.
+  // Unseen copies (nb_device.h): the compiler cannot tell a copy's LDS
+  // destination from the slot a later LDS read uses and would wait for the
+  // copies of later steps before the step's reads; every schedule below orders
+  // each slot's reads after that slot's copies with its own waits.
   auto load = [&](T* Qs, T* Gs, float* ls, float* ds, int* ks, int it) {
     const int hh = it / n_t, t = t_first + it % n_t;
     const int i0 = t * C::BQ;
     const int nr = min(C::BQ, Lr - i0);
     const size_t rb = (size_t)hh * Lr + i0;
-    if constexpr (C::SKEW) {
-      dma.issue_unseen(Qs, q_it + rb * D, nr);
-      dma.issue_unseen(Gs, do_it + rb * D, nr);
-      if (w == 0) dma_words<true>(ls, lse_it + rb, nr);
-      if (w == 1) dma_words<true>(ds, dl_it + rb, nr);
-      if (w == 2) dma_words<true>(ks, klo_it + i0, nr);
-    } else {
-      dma.issue(Qs, q_it + rb * D, nr);
-      dma.issue(Gs, do_it + rb * D, nr);
-      if (w == 0) dma_words(ls, lse_it + rb, nr);
-      if (w == 1) dma_words(ds, dl_it + rb, nr);
-      if (w == 2) dma_words(ks, klo_it + i0, nr);
-    }
+    dma.issue_unseen(Qs, q_it + rb * D, nr);
+    dma.issue_unseen(Gs, do_it + rb * D, nr);
+    if (w == 0) dma_words<true>(ls, lse_it + rb, nr);
+    if (w == 1) dma_words<true>(ds, dl_it + rb, nr);
+    if (w == 2) dma_words<true>(ks, klo_it + i0, nr);
   };
   constexpr int NS = C::STAGES;
   auto load_slot = [&](int slot, int it) {
@@ -692,10 +684,10 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
       kv_tile_load<T, C::BN, D, C::NW>(dma, p.kv, bh, j0, min(C::BN, p.S - j0), sm.K[slot], sm.V[slot]);
     } else if constexpr (KV == kKvPair) {
       pair.load(dma, j0, sm.K[slot], sm.V[slot]);
-    } else {
+    } else {   // unseen copies: the schedules below wait for each slot themselves
       const int nv = min(C::BN, p.S - j0);
-      dma.issue(sm.K[slot], kbase + (size_t)j0 * D, nv);
-      dma.issue(sm.V[slot], vbase + (size_t)j0 * D, nv);
+      dma.issue_unseen(sm.K[slot], kbase + (size_t)j0 * D, nv);
+      dma.issue_unseen(sm.V[slot], vbase + (size_t)j0 * D, nv);
     }
   };
 #pragma unroll

@@ -237,10 +237,10 @@ __device__ __forceinline__ u32x4 buffer_words(const void* base, uint32_t bytes) 
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, (uint32_t)kBufferWord3};
 }
-// LDS byte address of a __shared__ pointer.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
+// LDS byte address of a (generic) pointer to __shared__ memory: the low 32
+// bits of a flat address in the LDS aperture are the LDS offset.  (An
+// address-space cast of a run-time pointer here tripped the backend.)
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)reinterpret_cast<uintptr_t>(p); }
 // 16 bytes per lane from rsrc + voff into LDS at lds_byte + 16 * lane (wave-uniform lds_byte).
 __device__ __forceinline__ void unseen_copy16(const u32x4& rsrc, uint32_t lds_byte, uint32_t voff) {
   asm volatile(
