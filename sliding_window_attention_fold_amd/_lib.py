@@ -9,7 +9,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnbattn.so")
+# NBATTN_LIB selects another build of the same library (the host-AddressSanitizer
+# debug build, libnbattn_asan.so, in its CPU test); by default the in-tree one.
+LIB_PATH = os.environ.get("NBATTN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnbattn.so")
 
 NB_OK, NB_ERR_INVALID_ARG, NB_ERR_UNSUPPORTED, NB_ERR_WORKSPACE, NB_ERR_LAUNCH, NB_ERR_DEVICE = range(6)
 NB_BF16, NB_F32 = 0, 1

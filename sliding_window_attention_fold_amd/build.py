@@ -66,9 +66,47 @@ def build(jobs: int = 4) -> str:
     return LIB
 
 
+ASAN_LIB = os.path.join(PKG, "libnbattn_asan.so")
+# Host-only AddressSanitizer: the sanitizer flags follow -Xarch_host, so the
+# device code is the same as in libnbattn.so and only the host side (the C-ABI
+# preflight and launch code) is instrumented.
+ASAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-shared-libasan"]
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime a process must preload to load libnbattn_asan.so."""
+    import glob
+
+    hits = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("no clang AddressSanitizer runtime under /opt/rocm/lib/llvm")
+    return hits[-1]
+
+
+def build_asan() -> str:
+    """libnbattn_asan.so: nbattn_host.cpp rebuilt with host-side AddressSanitizer, linked with the other
+    objects of the regular build (run build() first).  A debug build for the CPU tests of the C-ABI."""
+    src = os.path.join(PKG, "csrc/nbattn_host.cpp")
+    obj = os.path.join(BUILD, "nbattn_host_asan.o")
+    r = subprocess.run([HIPCC, *FLAGS, *ASAN_HOST, "-x", "hip", "-c", src, "-o", obj], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc (asan) failed:\n{r.stderr}")
+    objs = [os.path.join(BUILD, os.path.basename(x) + ".o") for x in SOURCES if not x.endswith("nbattn_host.cpp")]
+    tmp = ASAN_LIB + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *ASAN_HOST, *objs, obj, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (asan) failed:\n{r.stderr}")
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
+
+
 def clean() -> None:
     shutil.rmtree(BUILD, ignore_errors=True)
 
 
 if __name__ == "__main__":
     print(build())
+    if "--asan" in sys.argv:
+        print(build_asan())
