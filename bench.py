@@ -360,9 +360,15 @@ def main() -> int:
                                                  D, scale, W, bf, P(dq), P(dk), P(dv), P(ws), ws_bytes, sp),
         "owner_flags": lambda: lib.nb_owner_attended(P(segbuf), P(folded), B, L, S, ctypes.cast(off_c,
                                                      ctypes.c_void_p), n_owner, P(attended), sp),
+        # the product entry point: prep (Delta, work orders and, in extra workgroups, the owner flags) + main
+        "attn_bwd": lambda: lib.nb_attn_bwd(P(dod), P(qd), P(kd), P(vd), P(out), P(resid), P(lse), P(segbuf),
+                                            P(folded), B, Hq, Hkv, L, S, D, scale, W, bf, P(dq), P(dk), P(dv),
+                                            ctypes.cast(off_c, ctypes.c_void_p), n_owner, P(attended), P(ws),
+                                            ws_bytes, sp),
     }
-    names = list(calls)
-    fb = names[1:]   # fwd+bwd: everything but the segment build (built once per step, reused by every layer)
+    names = ["segment_build", "attn_fwd", "bwd_prep", "bwd_main", "owner_flags"]
+    fb = names[1:]           # the backward as its separate launches (per-kernel times, the roofline)
+    step_calls = ["attn_fwd", "attn_bwd"]   # one fwd+bwd step through the product entry points
 
     def run(seq, events=None):
         for i, n in enumerate(seq):
@@ -383,6 +389,7 @@ def main() -> int:
 
     for _ in range(args.warmup):
         run(names)
+        run(step_calls)
     torch.cuda.synchronize()
 
     # Segment build alone (once per step in training, outside fwd+bwd).
@@ -391,9 +398,12 @@ def main() -> int:
     # its inputs.  Each iteration is bracketed by its own events.
     scratch = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
-    flushed = time_iters(stream, lambda ev: run(fb, ev), len(fb), args.steps, scratch)
+    flushed = time_iters(stream, lambda ev: run(step_calls, ev), len(step_calls), args.steps, scratch)
     # Warm: the same iterations back to back (inputs partly cached from the previous iteration).
-    warm = time_iters(stream, lambda ev: run(fb, ev), len(fb), args.steps, None)
+    warm = time_iters(stream, lambda ev: run(step_calls, ev), len(step_calls), args.steps, None)
+    # The backward's launches one by one, after the same flush: per-kernel times and the roofline.
+    split = time_iters(stream, lambda ev: run(fb, ev), len(fb), args.steps, scratch)
+    split_warm = time_iters(stream, lambda ev: run(fb, ev), len(fb), args.steps, None)
     # The K timed steps as one bracket (barrier + synchronise on both sides), back to back, segment build
     # included: the whole hot path.
     torch.cuda.synchronize()
@@ -401,12 +411,12 @@ def main() -> int:
     wall0 = time.perf_counter()
     t_start.record(stream)
     for _ in range(args.steps):
-        run(names)
+        run(["segment_build"] + step_calls)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     hot_path_ms = t_start.elapsed_time(t_end) / args.steps
-    sclk = sample_sclk(lambda: run(fb), stream)
+    sclk = sample_sclk(lambda: run(step_calls), stream)
     del scratch
 
     if args.copy_mib > 0:
@@ -416,7 +426,7 @@ def main() -> int:
     fb_w = warm.sum(axis=1)
     ms_step = float(np.median(fb_f))
     tflops = useful / (ms_step * 1e-3) / 1e12
-    per_mean = {n: float(flushed[:, i].mean()) for i, n in enumerate(fb)}
+    per_mean = {n: float(split[:, i].mean()) for i, n in enumerate(fb)}
     dom = max(KERNELS, key=lambda n: per_mean[n])
     dom_ms = per_mean[dom]
     bound = "mfma" if acct["ai"] >= RIDGE_FLOP_PER_BYTE else "hbm"
@@ -448,16 +458,18 @@ def main() -> int:
             "pairs_per_head": pairs, "useful_flop_per_step": useful,
         },
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "step": "fwd+bwd (nb_attn_fwd, nb_attn_bwd_prep, nb_attn_bwd_main, nb_owner_attended), each iteration "
-                "after a 512 MiB scratch write; value and ms_per_step from the median",
+        "step": "fwd+bwd through the product entry points (nb_attn_fwd, nb_attn_bwd: prep with the owner flags, "
+                "main), each iteration after a 512 MiB scratch write; value and ms_per_step from the median",
+        "fwd_ms": stats(flushed[:, 0]),
+        "bwd_ms": stats(flushed[:, 1]),
         "fwd_bwd_ms": stats(fb_f),
         "fwd_bwd_warm_ms": stats(fb_w),
         "warm_tflops": round(useful / (float(np.median(fb_w)) * 1e-3) / 1e12, 3),
         "segment_build_ms": stats(seg_ms),
         "hot_path_back_to_back_ms": round(hot_path_ms, 5),
         "hot_path_tflops": round(useful / (hot_path_ms * 1e-3) / 1e12, 3),
-        "ms_per_kernel": {n: stats(flushed[:, i]) for i, n in enumerate(fb)},
-        "ms_per_kernel_warm": {n: round(float(np.median(warm[:, i])), 5) for i, n in enumerate(fb)},
+        "ms_per_kernel": {n: stats(split[:, i]) for i, n in enumerate(fb)},
+        "ms_per_kernel_warm": {n: round(float(np.median(split_warm[:, i])), 5) for i, n in enumerate(fb)},
         "compulsory_bytes_per_step": acct["bytes"]["step"],
         "hbm_gbs_compulsory": round(acct["bytes"]["step"] / (ms_step * 1e-3) / 1e9, 1),
         "arithmetic_intensity": round(acct["ai"], 1),
