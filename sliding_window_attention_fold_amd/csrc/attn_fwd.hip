@@ -236,21 +236,29 @@ __global__ __launch_bounds__((FwdCfg<T, D>::NT), (FwdCfg<T, D>::OCC)) void attn_
         }
       }
     }
+    // The element mask, only on tiles that a band edge crosses (one uniform
+    // branch around the whole block: per element the compiler would turn it
+    // into selects executed on every tile).
+    if (!full) {
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + 32 * sb + acc_row(r, g);
+          if ((j < bs) | (j > pos)) sacc[sb][r] = -INFINITY;
+        }
+      }
+    }
+    // Row maximum of the raw scores; scaling by the positive scale_log2
+    // commutes with the maximum (rounding is monotonic), so the scale folds
+    // into the exponent's fma below.
     float tmax = -INFINITY;
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sacc[sb][r] * p.scale_log2;
-        if (!full) {
-          const int j = j0 + 32 * sb + acc_row(r, g);
-          if ((j < bs) | (j > pos)) x = -INFINITY;
-        }
-        sacc[sb][r] = x;
-        tmax = fmaxf(tmax, x);
-      }
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[sb][r]);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = fmaxf(tmax, other_half(tmax)) * p.scale_log2;
     // Move the reference (and rescale O) when some row's maximum passed it by
     // more than kRefLag (0: any growth); the wave decides together so the
     // branch is uniform, and rows whose maximum did not grow scale by 1.
@@ -267,7 +275,7 @@ __global__ __launch_bounds__((FwdCfg<T, D>::NT), (FwdCfg<T, D>::OCC)) void attn_
     for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(sacc[sb][r] - m_use);
+        const float e = fast_exp2(fmaf(sacc[sb][r], p.scale_log2, -m_use));
         sacc[sb][r] = e;
         l_run += e;
       }
@@ -309,7 +317,7 @@ __global__ __launch_bounds__((FwdCfg<T, D>::NT), (FwdCfg<T, D>::OCC)) void attn_
     }
   }
 
-  const float l = l_run + __shfl_xor(l_run, 32);
+  const float l = l_run + other_half(l_run);
   if (!in_range) return;
   const float inv = real ? 1.f / l : 0.f;
   T* op = reinterpret_cast<T*>(p.o) + qrow * D + hf * C::DW;

@@ -134,6 +134,16 @@ __device__ __forceinline__ void store_quad_split(T* hi, T* lo, float a, float b,
   }
 }
 
+// The value lane l ^ 32 holds (the other half of the wave), through
+// v_permlane32_swap: no LDS round trip and no wait on outstanding LDS reads.
+// The swap trades the upper half of its first operand with the lower half of
+// its second, so with x in both, lanes 0..31 find their partner in the second
+// result and lanes 32..63 in the first.
+__device__ __forceinline__ float other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
