@@ -124,6 +124,12 @@ struct DkvSmemTilesFirst : DkvTiles<T, D>, DkvMeta<T, D> {};
 template <typename T, int D>
 using DkvSmem = typename std::conditional<DkvCfg<T, D>::SKEW, DkvSmemMetaFirst<T, D>, DkvSmemTilesFirst<T, D>>::type;
 
+// Slot of key k (0..31) in a row of a stored 32 x 32 dS block: k with bits 2
+// and 3 swapped.  A lane's B fragment of a 32x32x16 product covers keys
+// 4g + {0..3} and 8 + 4g + {0..3} of a 16-key half (g = lane / 32), the
+// accumulator order of S; in this order they are one contiguous run of eight.
+__device__ __forceinline__ constexpr int ds_slot(int k) { return (k & 0x13) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
 // One dK/dV item f: (kv head, batch row, key tile) with the kv head fastest
 // and the (batch row, key tile) pairs in the order of decreasing work
 // (work_order_kernel), so the long tiles start first.
@@ -343,7 +349,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   const int ds_ntq = (p.L + 31) >> 5;                 // 32-row tiles per head
   auto store_ds = [&](const f32x16& ds, int it, const int* ks) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const int ds_lane = (ln + 4 * g * 32) * (int)sizeof(T);   // (formed here: nothing extra held in the loop)
+    const int ds_lane = (ds_slot(ln) + 4 * g * 32) * (int)sizeof(T);   // (formed here: nothing extra held in the loop)
     const int hh = it / n_t, tq = t_first + it % n_t, i0 = tq * C::BQ;
     int bs0 = max(0, ks[0] - kor);
     if (p.window >= 0) bs0 = max(bs0, off + i0 - p.window);
@@ -867,7 +873,6 @@ __global__ __launch_bounds__(256, (DqsCfg<T, D>::OCC)) void dq_ds_kernel(BwdPara
   typedef DqsCfg<T, D> C;
   typedef Tile<T, C::BN, D> TL;
   typedef typename Frag<T>::type F;
-  typedef typename Quad<T>::type Q4;
   __shared__ __attribute__((aligned(1024))) T K0[TL::ELEMS];
   __shared__ __attribute__((aligned(1024))) T K1[TL::ELEMS];
   __shared__ int red[C::NW][2];
@@ -915,37 +920,44 @@ __global__ __launch_bounds__(256, (DqsCfg<T, D>::OCC)) void dq_ds_kernel(BwdPara
   const KvPair<T, C::BN> pair = KV == kKvConcat ? KvPair<T, C::BN>() : KvPair<T, C::BN>(p.kv, bh, kstart, kend, D);
   auto load = [&](T* Ks, int j0) {
     if constexpr (KV == kKvConcat) {
-      dma.issue(Ks, kbase + (size_t)j0 * D, min(C::BN, p.S - j0));
+      // unseen copies (nb_device.h): the loop's wait and barrier at the top of
+      // each tile order the reads; a copy the compiler saw would make it wait
+      // for the next tile's copies and dS loads before this tile's reads
+      dma.issue_unseen(Ks, kbase + (size_t)j0 * D, min(C::BN, p.S - j0));
     } else {
       if (pair.ok) pair.load_k(dma, j0, Ks);   // uniform
       else kv_tile_load<T, C::BN, D, C::NW, false>(dma, p.kv, bh, j0, min(C::BN, p.S - j0), Ks, nullptr);
     }
   };
-  // the B-operand fragments of one tile (zeros outside the wave's blocks, for
-  // keys past S and for rows past L)
+  // The B-operand fragments of one tile as stored: one load per 16 keys (the
+  // lane's eight keys are contiguous, ds_slot), issued a tile ahead and used
+  // only after the next top-of-tile wait, so nothing consumes them early.  The
+  // block index is clamped to the row tile's own blocks (always in bounds); a
+  // block outside the wave's range is replaced by zeros where it is used.
   constexpr int NM = C::BN / 16;
-  auto ds_frags = [&](F* fr, int j0) {
+  auto ds_load = [&](F* raw, int j0) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int blk = min(max((j0 + 32 * (m >> 1) - kb) >> 5, 0), ds_nb - 1);
+      raw[m] = *reinterpret_cast<const F*>(drow + blk * 1024 + 16 * (m & 1) + 8 * g);
+    }
+  };
+  // zeros for blocks outside the wave's range (uniform), for rows past L and
+  // for keys past S (the dK/dV items never wrote them)
+  const bool rows_all = __builtin_amdgcn_readfirstlane(wave_min_i(in_range ? 1 : 0)) != 0;
+  auto ds_mask = [&](F* fr, const F* raw, int j0) {
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const int jw = j0 + 32 * (m >> 1);
-      fr[m] = F{};
-      if (jw >= kb && jw <= ke && in_range) {
-        const int c = ((jw - kb) >> 5) * 1024 + 16 * (m & 1) + 4 * g;
-        const Q4 x = *reinterpret_cast<const Q4*>(drow + c);
-        const Q4 y = *reinterpret_cast<const Q4*>(drow + c + 8);
+      fr[m] = (jw >= kb && jw <= ke) ? raw[m] : F{};
+    }
+    if (!rows_all || j0 + C::BN > p.S) {   // uniform: the last row tile or the last key tile
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          fr[m][t] = x[t];
-          fr[m][4 + t] = y[t];
-        }
-        if (jw + 32 > p.S) {   // keys past the neighbourhood were never written
-          const int k0 = jw + 16 * (m & 1) + 4 * g;
+      for (int m = 0; m < NM; ++m) {
+        const int k0 = j0 + 32 * (m >> 1) + 16 * (m & 1) + 4 * g;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            if (k0 + t >= p.S) fr[m][t] = to_elem<T>(0.f);
-            if (k0 + 8 + t >= p.S) fr[m][4 + t] = to_elem<T>(0.f);
-          }
-        }
+        for (int t = 0; t < 8; ++t)
+          if (!in_range || k0 + (t & 3) + 8 * (t >> 2) >= p.S) fr[m][t] = to_elem<T>(0.f);
       }
     }
   };
@@ -954,8 +966,10 @@ __global__ __launch_bounds__(256, (DqsCfg<T, D>::OCC)) void dq_ds_kernel(BwdPara
 #pragma unroll
   for (int d = 0; d < D / 32; ++d) oacc[d] = f32x16{};
   constexpr int ND = D / 32;
-  auto compute = [&](const T* Ks, const F* fr, int j0) __attribute__((always_inline)) {
+  auto compute = [&](const T* Ks, const F* raw, int j0) __attribute__((always_inline)) {
     if (!w_any || j0 > ke || j0 + C::BN <= kb) return;
+    F fr[NM];
+    ds_mask(fr, raw, j0);
     lds_mfma_pipeline<NM * ND, C::AHEAD, F>(
         [&](int x) { return acc.col(Ks, x % ND, x / ND); },
         [&](int x, const F& a) { oacc[x % ND] = mma(a, fr[x / ND], oacc[x % ND]); });
@@ -963,14 +977,14 @@ __global__ __launch_bounds__(256, (DqsCfg<T, D>::OCC)) void dq_ds_kernel(BwdPara
   F f0[NM], f1[NM];
   if (kstart < kend) {
     load(K0, kstart);
-    ds_frags(f0, kstart);
+    ds_load(f0, kstart);
   }
   for (int j0 = kstart; j0 < kend; j0 += 2 * C::BN) {
     wait_global();
     __syncthreads();
     if (j0 + C::BN < kend) {
       load(K1, j0 + C::BN);
-      ds_frags(f1, j0 + C::BN);
+      ds_load(f1, j0 + C::BN);
     }
     __builtin_amdgcn_sched_barrier(0);
     compute(K0, f0, j0);
@@ -979,7 +993,7 @@ __global__ __launch_bounds__(256, (DqsCfg<T, D>::OCC)) void dq_ds_kernel(BwdPara
     __syncthreads();
     if (j0 + 2 * C::BN < kend) {
       load(K0, j0 + 2 * C::BN);
-      ds_frags(f0, j0 + 2 * C::BN);
+      ds_load(f0, j0 + 2 * C::BN);
     }
     __builtin_amdgcn_sched_barrier(0);
     compute(K1, f1, j0 + C::BN);

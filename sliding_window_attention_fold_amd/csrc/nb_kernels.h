@@ -108,7 +108,9 @@ struct BwdParams {
   int dq_mode;       // kDqStore: dq is T, written; kDqSetF32 / kDqAddF32: dq is fp32, set / added to
   // Optional banded dS (windowed neighbourhoods): per (batch row, q head,
   // 32-row query tile) ds_w / 32 blocks of 32 rows x 32 keys (row-major T), the
-  // tile's keys from its first row's band start rounded down to 32.  Non-null:
+  // tile's keys from its first row's band start rounded down to 32.  Within a
+  // row, key k of the block sits at k with bits 2 and 3 swapped (ds_slot), so
+  // the eight keys one lane feeds to a 32x32x16 product are contiguous.  Non-null:
   // the dK/dV items store dS there and dQ = dS K runs as a separate pass
   // instead of the dQ items.
   void* dsbuf;
