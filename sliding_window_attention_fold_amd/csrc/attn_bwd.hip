@@ -308,11 +308,17 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   auto to_p = [&](f32x16& sacc, const float* ls, const int* ks, const StepInfo& si, auto& px) {
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      // rows 8*rq + 4*g + e: their LSE (and band starts) as one 16-byte read
+      // rows 8*rq + 4*g + e: their LSE as one 16-byte read
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + 8 * rq + 4 * g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) sacc[4 * rq + e] = fast_exp2(fmaf(sacc[4 * rq + e], p.scale_log2, -l4[e] * kLog2e));
-      if (!si.full) {
+    }
+    // the element mask, only on steps a band edge crosses: one uniform branch
+    // around the whole block (per element the compiler turns it into selects
+    // executed on every step)
+    if (!si.full) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
         const int4 k4 = *reinterpret_cast<const int4*>(ks + 8 * rq + 4 * g);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -731,13 +737,16 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float pr = fast_exp2(fmaf(sacc[sb][r], p.scale_log2, -lse2));
-            if (!full) {
+          for (int r = 0; r < 16; ++r) sacc[sb][r] = fast_exp2(fmaf(sacc[sb][r], p.scale_log2, -lse2));
+        }
+        if (!full) {   // one uniform branch around the element mask (see the dK/dV item)
+#pragma unroll
+          for (int sb = 0; sb < NSB; ++sb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
               const int jj = j0 + 32 * sb + acc_row(r, g);
-              if ((!real) | (jj < bs) | (jj > pos)) pr = 0.f;
+              if ((!real) | (jj < bs) | (jj > pos)) sacc[sb][r] = 0.f;
             }
-            sacc[sb][r] = pr;
           }
         }
       }
@@ -769,13 +778,38 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
     F sf[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) sf[m] = acc_to_frag<T>(sacc[m >> 1], m & 1);
-    if constexpr (C::AHEAD > 0) {
-      lds_mfma_pipeline<NM * DH, C::AHEAD, F>(
-          [&](int x) { return acc.col(Ks, dh0 + x % DH, x / DH); },
-          [&](int x, const F& a) { dqacc[x % DH] = mma(a, sf[x / DH], dqacc[x % DH]); });
-    } else {
+    // This role's d blocks as compile-time indices (one branch per role): a
+    // block index known only at run time would index the column reader's
+    // per-lane address arrays at run time, and the compiler then keeps those
+    // arrays in LDS and loads every read's address from there (bank-conflicted).
+    auto dq_product_rt = [&](int d0) __attribute__((always_inline)) {
+      if constexpr (C::AHEAD > 0) {
+        lds_mfma_pipeline<NM * DH, C::AHEAD, F>(
+            [&](int x) { return acc.col(Ks, d0 + x % DH, x / DH); },
+            [&](int x, const F& a) { dqacc[x % DH] = mma(a, sf[x / DH], dqacc[x % DH]); });
+      } else {
 #pragma unroll
-      for (int x = 0; x < NM * DH; ++x) dqacc[x % DH] = mma(acc.col(Ks, dh0 + x % DH, x / DH), sf[x / DH], dqacc[x % DH]);
+        for (int x = 0; x < NM * DH; ++x) dqacc[x % DH] = mma(acc.col(Ks, d0 + x % DH, x / DH), sf[x / DH], dqacc[x % DH]);
+      }
+    };
+    auto dq_product = [&](auto half) __attribute__((always_inline)) {
+      constexpr int d0 = decltype(half)::value * DH;
+      if constexpr (C::AHEAD > 0) {
+        lds_mfma_pipeline<NM * DH, C::AHEAD, F>(
+            [&](int x) { return acc.col(Ks, d0 + x % DH, x / DH); },
+            [&](int x, const F& a) { dqacc[x % DH] = mma(a, sf[x / DH], dqacc[x % DH]); });
+      } else {
+#pragma unroll
+        for (int x = 0; x < NM * DH; ++x) dqacc[x % DH] = mma(acc.col(Ks, d0 + x % DH, x / DH), sf[x / DH], dqacc[x % DH]);
+      }
+    };
+    if constexpr (sizeof(T) == 2 && D <= 128) {
+      if (role_a) dq_product(std::integral_constant<int, 0>{});
+      else dq_product(std::integral_constant<int, 1>{});
+    } else {
+      // (at D >= 256 a role's first block is a multiple of the reader's block
+      // count, so the array index is a compile-time constant already)
+      dq_product_rt(dh0);
     }
   };
 
