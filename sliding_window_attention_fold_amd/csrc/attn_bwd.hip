@@ -364,19 +364,24 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(p.dsbuf, (short)0, p.ds_bytes, kBufferWord3);
     const int nrows = p.L - i0;
     if (j < p.S && hf == 0) {   // (at D = 512 the other role-B wave holds the same dS)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (acc_row(r, g) < nrows) {
-          const int voff = ds_lane + (8 * (r >> 2) + (r & 3)) * 32 * (int)sizeof(T);
-          if constexpr (sizeof(T) == 2) {
-            const bf16 v = to_elem<bf16>(ds[r]);
-            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), rs, voff,
-                                                      blk * 32 * 32 * 2, 0);
-          } else {
-            const float v = ds[r];
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, voff, blk * 32 * 32 * 4, 0);
-          }
+      auto put = [&](int r) __attribute__((always_inline)) {
+        const int voff = ds_lane + (8 * (r >> 2) + (r & 3)) * 32 * (int)sizeof(T);
+        if constexpr (sizeof(T) == 2) {
+          const bf16 v = to_elem<bf16>(ds[r]);
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), rs, voff,
+                                                    blk * 32 * 32 * 2, 0);
+        } else {
+          const float v = ds[r];
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, voff, blk * 32 * 32 * 4, 0);
         }
+      };
+      if (nrows >= C::BQ) {   // uniform: a whole tile of rows, no per-row test (no exec mask per store)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) put(r);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (acc_row(r, g) < nrows) put(r);
       }
     }
 #endif
