@@ -70,9 +70,14 @@ struct DkvCfg {
   static constexpr int NKG = NW / (2 * HS);   // key groups of 32 keys
   static constexpr int BK = 32 * NKG;  // keys per workgroup
   static constexpr int BQ = 32;        // query rows per step
-  // operand fragments read ahead of their MFMA; 0 = plain loop (D = 256 and the
-  // float path have no registers to spare)
+  // operand fragments read ahead of their MFMA; 0 = plain loop (the float path
+  // and D = 512 have no registers to spare).  At D = 256 the room comes from
+  // the XOR-addressed readers (XREAD: one and two address registers per lane
+  // instead of sixteen), in the dK/dV-only kernel (AHEAD_DS); the kernel that
+  // also runs dQ items carries their registers and reads none ahead.
+  static constexpr bool XREAD = sizeof(T) == 2 && D == 256;
   static constexpr int AHEAD = (D <= 128 && sizeof(T) == 2) ? 4 : 0;
+  static constexpr int AHEAD_DS = XREAD ? 3 : AHEAD;
   static constexpr int TILE_BYTES = BQ * D * (int)sizeof(T);
   static constexpr int PEX_BYTES = NKG * 4 * 64 * 16;   // one P hand-over buffer
   static constexpr int META_BYTES = 3 * 64 * 4;         // LSE, Delta, band starts of one step
@@ -152,7 +157,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   constexpr int NDA = C::DA / 32;                 // 32-wide column blocks of the accumulator
   const int off = p.q_off;                        // row i sits at key position off + i
   const int kor = p.k_origin;                     // row_klo values count keys from here
-  const TileAccess<T, TL> acc(ln, lane);
+  // (at D = 256 the one- and two-register readers leave room to read ahead)
+  typedef typename std::conditional<C::XREAD, TileAccessX<TL>, TileAccess<T, TL>>::type Access;
+  const Access acc(ln, lane);
   const TileDma<T, C::BQ, D, C::NW> dma;   // Q and dO tiles share one layout
   const int kvh = f % p.Hkv;
   const int code = p.order[f / p.Hkv];
@@ -294,9 +301,10 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
     return si;
   };
   // acc += rows of src (Q or dO) x this lane's K or V row: S^T or dP^T blocks
+  constexpr int AH = DS ? C::AHEAD_DS : C::AHEAD;   // (see DkvCfg)
   auto rows_x_kv = [&](const T* src, f32x16& sacc) {
-    if constexpr (C::AHEAD > 0) {
-      lds_mfma_pipeline<D / 16, C::AHEAD, F>([&](int kk) { return acc.row(src, 0, kk); },
+    if constexpr (AH > 0) {
+      lds_mfma_pipeline<D / 16, AH, F>([&](int kk) { return acc.row(src, 0, kk); },
                                              [&](int kk, const F& a) { sacc = mma(a, kv[kk], sacc); });
     } else {
 #pragma unroll
@@ -389,10 +397,10 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   // gacc += src^T (P or dS): dV^T = dO^T P (role A) or dK^T = Q^T dS (role B)
   auto accumulate = [&](const T* src, const f32x16& sacc) {
     const int d0 = hf * NDA;   // first column block of this wave's half
-    if constexpr (C::AHEAD > 0) {
+    if constexpr (AH > 0) {
       const F sf[2] = {acc_to_frag<T>(sacc, 0), acc_to_frag<T>(sacc, 1)};
       constexpr int ND = NDA;
-      lds_mfma_pipeline<2 * ND, C::AHEAD, F>(
+      lds_mfma_pipeline<2 * ND, AH, F>(
           [&](int x) { return acc.col(src, d0 + x % ND, x / ND); },
           [&](int x, const F& a) { gacc[x % ND] = mma(a, sf[x / ND], gacc[x % ND]); });
     } else {

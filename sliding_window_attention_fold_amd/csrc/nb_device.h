@@ -561,6 +561,56 @@ __device__ __forceinline__ typename Frag<T>::type frag_col(const T* lds, int dbl
   }
 }
 
+// The same two readers with one and two address registers instead of NB and
+// 2*NB.  The swizzle only permutes 16-byte chunks inside a row, and a tile
+// starts on a 1 KB boundary with rows of at least 256 bytes, so a lane's
+// address for fragment j is its base with a constant XORed into bits 5..7
+// (row reads) or 6..7 (transposed reads): one v_xor per read in place of a
+// register per fragment, for kernels short of registers to read ahead with.
+template <typename TL>
+struct RowReaderX {
+  static constexpr int RB = TL::CPR * 16;
+  static_assert(RB >= 256 && TL::CPR >= 16, "one row must span whole 256-byte bank lines");
+  int b;   // row r0, chunk bits g ^ swz(r0)
+  __device__ __forceinline__ RowReaderX(int r0, int g) : b(r0 * RB + 16 * (g ^ TL::swz(r0))) {}
+  __device__ __forceinline__ bf16x8 read(const bf16* lds, int sb, int kk) const {
+    typedef __attribute__((address_space(3))) const bf16x8 lds_b8;
+    const uint32_t a = ((lds_addr(lds) + (uint32_t)b) ^ (uint32_t)(32 * (kk % 8))) + 256u * (kk / 8) + sb * 32 * RB;
+    return *reinterpret_cast<lds_b8*>((uintptr_t)a);
+  }
+};
+template <typename TL>
+struct ColReaderX {
+  static constexpr int NB = 4;
+  static constexpr int RB = TL::CPR * 16;
+  static_assert(RB >= 256 && TL::CPR >= 16, "one row must span whole 256-byte bank lines");
+  int lo, hi;   // rows r and r + 8 at d block 0 (see ColReader)
+  __device__ __forceinline__ ColReaderX(int lane) {
+    const int g = lane >> 5, s = lane & 15, half = (lane >> 4) & 1;
+    const int r = 4 * g + (s >> 2);
+    const int u = 2 * half + ((s >> 1) & 1);   // the chunk within a 64-byte group
+    lo = r * RB + 16 * (u ^ TL::swz(r)) + 8 * (s & 1);
+    hi = (r + 8) * RB + 16 * (u ^ TL::swz(r + 8)) + 8 * (s & 1);
+  }
+  __device__ __forceinline__ bf16x8 read(const bf16* lds, int dblk, int m) const {
+    typedef __attribute__((address_space(3))) bf16x4 lds_b4;
+    const uint32_t base = lds_addr(lds);
+    const uint32_t sw = 64u * (dblk % NB), extra = (dblk / NB) * (NB * 4 * 16) + m * 16 * RB;
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4*)(uintptr_t)(((base + lo) ^ sw) + extra));
+    const bf16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4*)(uintptr_t)(((base + hi) ^ sw) + extra));
+    return bf16x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+  }
+};
+// A TileAccess through the X readers (bf16, rows of at least 256 bytes).
+template <typename TL>
+struct TileAccessX {
+  RowReaderX<TL> rr;
+  ColReaderX<TL> cr;
+  __device__ __forceinline__ TileAccessX(int r0, int lane) : rr(r0, lane >> 5), cr(lane) {}
+  __device__ __forceinline__ bf16x8 row(const bf16* lds, int sb, int kk) const { return rr.read(lds, sb, kk); }
+  __device__ __forceinline__ bf16x8 col(const bf16* lds, int dblk, int m) const { return cr.read(lds, dblk, m); }
+};
+
 // Operand access to a tile for one lane: rows r0 + 32*sb along D, and the
 // transposed fragments; bf16 through the precomputed readers, float (debug
 // path) through the generic element reads.
