@@ -9,10 +9,11 @@
 //   dQ = scale * dS K.
 // Two passes keep every output owned by exactly one workgroup (no atomics, the
 // result is bitwise reproducible):
-//   1. dQ:     one workgroup per (128 query rows, q head, batch row): four query
-//      groups of 32 rows, each served by a pair of waves (Q side: S, P; dO
-//      side: dP; they swap P and dP through LDS and each accumulates half of
-//      dQ).  K/V tiles are copied into LDS asynchronously (double-buffered); K^T
+//   1. dQ:     one workgroup per (query rows, q head, batch row).  bf16 at
+//      D <= 128: eight query groups of 32 rows (256 rows), one wave each,
+//      forming S, P, dP, dS and all of dQ; otherwise four query groups, each
+//      served by a pair of waves (Q side: S, P; dO side: dP; they swap P and dP
+//      through LDS and each accumulates half of dQ).  K/V tiles are copied into LDS asynchronously (double-buffered); K^T
 //      is read transposed from the same row-major tile.  Its prologue forms
 //      Delta = dO . O (O = stored value + saved rounding residual) and
 //      publishes it for pass 2;
@@ -594,8 +595,13 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
 // each SIMD at D = 256; the matrix-core work is the same as one wave doing all.
 template <typename T, int D>
 struct DqCfg {
-  static constexpr int NQG = BwdShape<T, D>::NT / 128;   // query groups of 32 rows
-  static constexpr int NW = 2 * NQG;
+  // FUSED (bf16, D <= 128): every wave is a query group of its own and forms S,
+  // P, dP and dS for its 32 rows and all of dQ -- Q and dO rows plus the whole
+  // accumulator fit 256 registers at these head dims -- so no P / dP crosses
+  // between waves and the step keeps one barrier, for the K/V ring.
+  static constexpr bool FUSED = sizeof(T) == 2 && D <= 128;
+  static constexpr int NQG = FUSED ? BwdShape<T, D>::NT / 64 : BwdShape<T, D>::NT / 128;   // query groups of 32 rows
+  static constexpr int NW = FUSED ? NQG : 2 * NQG;
   static constexpr int NT = 64 * NW;
   static constexpr int BM = 32 * NQG;               // query rows per workgroup
   static constexpr int BN = (D * sizeof(T) <= 256) ? 64 : 32;   // keys per tile
@@ -610,7 +616,7 @@ struct DqSmem {
   typedef Tile<T, DqCfg<T, D>::BN, D> TL;
   static constexpr int NSB = DqCfg<T, D>::BN / 32;
   static constexpr int TILE_BYTES = TL::ELEMS * (int)sizeof(T);
-  static constexpr int NQG = DqCfg<T, D>::NQG;
+  static constexpr int NQG = DqCfg<T, D>::FUSED ? 1 : DqCfg<T, D>::NQG;   // (fused: the exchange only hosts the wave bounds)
   static constexpr int XCH_BYTES = 2 * NQG * NSB * 4 * 64 * 16;
   // three K/V slots and a double-buffered exchange (one barrier per step) when
   // they fit, else two slots and one exchange buffer (two barriers per step)
@@ -634,7 +640,7 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
   typedef typename Frag<T>::type F;
   constexpr int NSB = C::BN / 32;
   constexpr int NM = C::BN / 16;
-  constexpr int DH = D / 64;   // 32-wide d blocks of dQ per role
+  constexpr int DH = C::FUSED ? D / 32 : D / 64;   // 32-wide d blocks of dQ per wave
   constexpr int NS = DqSmem<T, D>::NS;
   // wave bounds: scratch at the start of the exchange, dead before the first
   // exchange write (barriers separate them)
@@ -643,8 +649,9 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
   const int n_qt = (p.L + C::BM - 1) / C::BM;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
   const int qg = w % C::NQG;            // query group
-  const bool role_a = w < C::NQG;       // A: Q, S, P   B: dO, dP
-  const TileAccess<T, TL> acc(ln, lane);
+  const bool role_a = C::FUSED || w < C::NQG;   // A: Q, S, P   B: dO, dP   (fused: both)
+  typedef TileAccess<T, TL> Access;
+  const Access acc(ln, lane);
   const TileDma<T, C::BN, D, C::NW> dma;   // K and V tiles share one layout
   const int kvh = f % p.Hkv;
   const int h = kvh * grp + (f / p.Hkv) % grp;
@@ -671,13 +678,23 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
   const size_t qrow = ((size_t)b * p.Hq + h) * p.L + i;
   const size_t qrow_c = ((size_t)b * p.Hq + h) * p.L + min(i, p.L - 1);  // rows past L read row L-1
   // this lane's row of Q (role A) or dO (role B): the B operand of S^T or dP^T
+  // (fused: Q in rf, dO in rg)
   F rf[D / 16];
+  F rg[C::FUSED ? D / 16 : 1];
   {
     const T* src = reinterpret_cast<const T*>(role_a ? p.q : p.dout) + qrow_c * D;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       rf[kk] = load_frag<T>(src + 16 * kk + 8 * g);
       if (!in_range) rf[kk] = zero_frag<T>();
+    }
+    if constexpr (C::FUSED) {
+      const T* so = reinterpret_cast<const T*>(p.dout) + qrow_c * D;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        rg[kk] = load_frag<T>(so + 16 * kk + 8 * g);
+        if (!in_range) rg[kk] = zero_frag<T>();
+      }
     }
   }
   // Delta of the row (bwd_delta_kernel), 0 for padding rows
@@ -719,12 +736,64 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
   for (int x = 0; x < NS - 1; ++x)
     if (x < nt) load(x, x);
 
-  const int dh0 = role_a ? 0 : DH;      // first 32-wide d block of this wave's dQ half
+  const int dh0 = (C::FUSED || role_a) ? 0 : DH;      // first 32-wide d block of this wave's dQ part
   f32x16 dqacc[DH];
 #pragma unroll
   for (int d = 0; d < DH; ++d) dqacc[d] = f32x16{};
 
+  // fused: S and dP of the wave's rows, P and dS in place, then (after the
+  // ring's barrier) dQ^T += K^T dS^T over all of D
+  auto step_fused = [&](const T* Ks, const T* Vs, int n, auto&& mid) {
+    const int j0 = kstart + n * C::BN;
+    const bool active = !(j0 >= w_hi || j0 + C::BN <= w_lo);
+    const bool full = w_all_real && j0 >= w_bs_max && j0 + C::BN - 1 <= w_p_min;
+    constexpr int NK = D / 16;
+    f32x16 sacc[NSB], dpa[NSB];
+    if (active) {
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) sacc[sb] = dpa[sb] = f32x16{};
+      lds_mfma_pipeline<NSB * NK, C::AHEAD, F>(
+          [&](int x) { return acc.row(Ks, x / NK, x % NK); },
+          [&](int x, const F& a) { sacc[x / NK] = mma(a, rf[x % NK], sacc[x / NK]); });
+      lds_mfma_pipeline<NSB * NK, C::AHEAD, F>(
+          [&](int x) { return acc.row(Vs, x / NK, x % NK); },
+          [&](int x, const F& a) { dpa[x / NK] = mma(a, rg[x % NK], dpa[x / NK]); });
+      // accumulator r of block sb: key j0 + 32*sb + acc_row(r, g), query row i (this lane)
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[sb][r] = fast_exp2(fmaf(sacc[sb][r], p.scale_log2, -lse2));
+      }
+      if (!full) {   // one uniform branch around the element mask (see the dK/dV item)
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int jj = j0 + 32 * sb + acc_row(r, g);
+            if ((!real) | (jj < bs) | (jj > pos)) sacc[sb][r] = 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[sb][r] = sacc[sb][r] * (dpa[sb][r] - dl);
+      }
+    }
+    mid();   // the ring's barrier (and maintenance)
+    if (!active) return;
+    F sf[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) sf[m] = acc_to_frag<T>(sacc[m >> 1], m & 1);
+    lds_mfma_pipeline<NM * DH, C::AHEAD, F>(
+        [&](int x) { return acc.col(Ks, x % DH, x / DH); },
+        [&](int x, const F& a) { dqacc[x % DH] = mma(a, sf[x / DH], dqacc[x % DH]); });
+  };
   auto step = [&](const T* Ks, const T* Vs, int n, auto&& mid) {
+    if constexpr (C::FUSED) {
+      step_fused(Ks, Vs, n, mid);
+      return;
+    }
     const int j0 = kstart + n * C::BN;
     auto& xb = sm.xch[DqSmem<T, D>::NX > 1 ? (n & 1) : 0];
     f32x4 (*xp)[NSB][4][64] = xb[0];
