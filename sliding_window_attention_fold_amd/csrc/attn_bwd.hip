@@ -377,8 +377,11 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
         const int voff = ds_lane + (8 * (r >> 2) + (r & 3)) * 32 * (int)sizeof(T);
         if constexpr (sizeof(T) == 2) {
           const bf16 v = to_elem<bf16>(ds[r]);
+          // non-temporal (aux 2): the band streams through once, and cached it
+          // evicted the Q / dO tiles other items re-read (the pass fetched 417
+          // instead of 307 MB past the L2 on the sliding layer)
           __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), rs, voff,
-                                                    blk * 32 * 32 * 2, 0);
+                                                    blk * 32 * 32 * 2, 2);
         } else {
           const float v = ds[r];
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, voff, blk * 32 * 32 * 4, 0);
@@ -1055,7 +1058,7 @@ __global__ __launch_bounds__(256, (DqsCfg<T, D>::OCC)) void dq_ds_kernel(BwdPara
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const int blk = min(max((j0 + 32 * (m >> 1) - kb) >> 5, 0), ds_nb - 1);
-      raw[m] = *reinterpret_cast<const F*>(drow + blk * 1024 + 16 * (m & 1) + 8 * g);
+      raw[m] = __builtin_nontemporal_load(reinterpret_cast<const F*>(drow + blk * 1024 + 16 * (m & 1) + 8 * g));   // (read once)
     }
   };
   // zeros for blocks outside the wave's range (uniform), for rows past L and
