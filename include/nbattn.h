@@ -81,6 +81,12 @@ int nb_version(void);
  *   row_klo[N]         first key of that row's segment (neighbourhood position);
  *                      p + 1 for padding rows (an empty key range)
  *   kcov_lo[B]         first covered key of batch row b (S if none)
+ *   fwd_order[B * ceil(L / 128)]
+ *                      per batch row, the indices of its 128-row query tiles
+ *                      by decreasing band work (ties: higher index first); the
+ *                      identity when a row has more than 2048 tiles.  The
+ *                      forward launches its tiles in this order; it changes
+ *                      no result
  *   scratch            builder-private (per-tile records, duplicate-id set)
  * Entries past n_seg (past n_seg + 1 for cu_q / cu_k) are unspecified.
  * ------------------------------------------------------------------------ */
@@ -101,6 +107,7 @@ size_t nb_segment_offset_k_row0(int B, int L);
 size_t nb_segment_offset_row_seg(int B, int L);
 size_t nb_segment_offset_row_klo(int B, int L);
 size_t nb_segment_offset_kcov_lo(int B, int L);
+size_t nb_segment_offset_fwd_order(int B, int L);
 
 /* int32 elements the caller must provide for seg_buf (0 on invalid sizes). */
 size_t nb_segment_buffer_elems(int B, int L, int S);

@@ -31,6 +31,7 @@ SIGNATURES = {
     "nb_segment_offset_row_seg": (_Z, [_I, _I]),
     "nb_segment_offset_row_klo": (_Z, [_I, _I]),
     "nb_segment_offset_kcov_lo": (_Z, [_I, _I]),
+    "nb_segment_offset_fwd_order": (_Z, [_I, _I]),
     "nb_segment_buffer_elems": (_Z, [_I, _I, _I]),
     "nb_segment_build": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "nb_segment_header": (_I, [_P, _P, _P]),

@@ -95,6 +95,11 @@ class Segments:
     def kcov_lo(self):
         return self._view("nb_segment_offset_kcov_lo", self.B)
 
+    @property
+    def fwd_order(self):
+        """Per batch row, the forward's 128-row query tiles in launch order (longest band first)."""
+        return self._view("nb_segment_offset_fwd_order", self.B * ((self.L + 127) // 128))
+
 
 def segment_build(nb_ids: torch.Tensor, L: int, window: int = -1,
                   pad_mask: Optional[torch.Tensor] = None) -> Segments:

@@ -1225,34 +1225,6 @@ constexpr int kPrepNT = 256;          // threads of the prep kernel's workgroups
 constexpr int kOrderMax = 2048;       // items sorted in LDS
 constexpr int kOrderBandMax = 2048;   // query-tile band starts staged in LDS
 
-// Sort keys[0, N) ascending (N a power of two) and emit the item indices they
-// carry (key = (2^32 - 1 - work) << 32 | (n - 1 - item)).
-__device__ void order_by_work(unsigned long long* keys, int n, int N, int* out) {
-  const int tid = threadIdx.x;
-  __syncthreads();
-  for (int k = 2; k <= N; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < N; i += kPrepNT) {
-        const int l = i ^ j;
-        if (l > i) {
-          const unsigned long long a = keys[i], c = keys[l];
-          if ((a > c) == ((i & k) == 0)) {
-            keys[i] = c;
-            keys[l] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int i = tid; i < n; i += kPrepNT) out[i] = n - 1 - (int)(unsigned)(keys[i] & 0xFFFFFFFFu);
-  __syncthreads();
-}
-
-__device__ __forceinline__ unsigned long long work_key(unsigned work, int i, int n) {
-  return ((unsigned long long)(0xFFFFFFFFu - work) << 32) | (unsigned)(n - 1 - i);
-}
-
 template <int BK, int BQ, int BM>
 __device__ void work_order(const BwdParams& p, int modes, unsigned long long* keys, int* bst) {
   const int tid = threadIdx.x;
@@ -1294,7 +1266,7 @@ __device__ void work_order(const BwdParams& p, int modes, unsigned long long* ke
         }
         keys[i] = key;
       }
-      order_by_work(keys, n, N, p.order);
+      order_by_work<kPrepNT>(keys, n, N, p.order);
     }
   }
   if (modes & 2) {
@@ -1316,7 +1288,7 @@ __device__ void work_order(const BwdParams& p, int modes, unsigned long long* ke
         }
         keys[i] = key;
       }
-      order_by_work(keys, n, N, p.qorder);
+      order_by_work<kPrepNT>(keys, n, N, p.qorder);
     }
   }
 }
@@ -1449,15 +1421,6 @@ __global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void b
     dq_item<T, D, kKvAny>(p, sm, f);
     __syncthreads();
   }
-}
-
-// Compute units of the current device (the persistent grid's size).
-static int device_cu_count() {
-  int dev = 0, n_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
-    n_cu = 256;
-  return n_cu;
 }
 
 // Delta (when with_delta) and the work orders of the passes in `modes`.

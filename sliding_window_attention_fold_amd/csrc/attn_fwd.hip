@@ -106,12 +106,14 @@ __global__ __launch_bounds__((FwdCfg<T, D>::NT), (FwdCfg<T, D>::OCC)) void attn_
   // Work order: the kv group (batch row, kv head) varies fastest, so with the
   // round-robin dispatch over 8 XCDs every group stays on one XCD and the K/V
   // window its query tiles share stays in that XCD's L2; the group's q heads
-  // come next, then the query tiles in order.
+  // come next, then the query tiles, in grid order or, when the grid takes
+  // more than one round of workgroups, longest band first (qt_order).
   const int grp = p.Hq / p.Hkv;
   const int ngroups = p.B * p.Hkv;
   const int gid = blockIdx.x % ngroups, rest = blockIdx.x / ngroups;
   const int b = gid / p.Hkv, kvh = gid % p.Hkv;
-  const int h = kvh * grp + rest % grp, qt = rest / grp;
+  const int h = kvh * grp + rest % grp, rank = rest / grp;
+  const int qt = p.qt_order ? p.qt_order[(size_t)b * ((p.L + C::BM - 1) / C::BM) + rank] : rank;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, ln = lane & 31;
   const int rg = C::DS > 1 ? w % C::NRG : w;   // 32-row group
   const int hf = C::DS > 1 ? w / C::NRG : 0;   // half of D (head-dim split)
@@ -338,9 +340,13 @@ __global__ __launch_bounds__((FwdCfg<T, D>::NT), (FwdCfg<T, D>::OCC)) void attn_
 static bool kv_concatenated(const KvChunks& c, int S) { return c.n == 1 && c.start[0] == 0 && c.rows[0] == S; }
 
 template <typename T, int D>
-static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
+static hipError_t launch_fwd_t(const FwdParams& p_in, hipStream_t s) {
   typedef FwdCfg<T, D> C;
-  dim3 grid((unsigned)((p.L + C::BM - 1) / C::BM) * p.Hq * p.B);
+  dim3 grid((unsigned)((p_in.L + C::BM - 1) / C::BM) * p_in.Hq * p_in.B);
+  // The launch order only pays when workgroups wait for slots (and it is
+  // built for kFwdOrderRows-row tiles).
+  FwdParams p = p_in;
+  if (C::BM != kFwdOrderRows || (long long)grid.x <= (long long)device_cu_count() * C::OCC) p.qt_order = nullptr;
   if constexpr (D >= 512) {   // the global layers' head dim: one concatenated K/V buffer only
     if (!kv_concatenated(p.kv, p.S)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attn_fwd_kernel<T, D, kKvConcat>), grid, dim3(C::NT), 0, s, p);

@@ -641,4 +641,37 @@ struct TileAccess<float, TL> {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Work orders: items sorted by decreasing work, ties by decreasing index.  A
+// key carries both, (2^32 - 1 - work) << 32 | (n - 1 - item), so an ascending
+// sort of the keys gives the order.
+__device__ __forceinline__ unsigned long long work_key(unsigned work, int i, int n) {
+  return ((unsigned long long)(0xFFFFFFFFu - work) << 32) | (unsigned)(n - 1 - i);
+}
+// Bitonic sort of keys[0, N) in LDS (N a power of two, entries past n padded
+// with ~0) by the NT threads of the workgroup, then out[0, n) = the items in
+// key order.  Every thread of the workgroup calls it.
+template <int NT>
+__device__ void order_by_work(unsigned long long* keys, int n, int N, int* out) {
+  const int tid = threadIdx.x;
+  __syncthreads();
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < N; i += NT) {
+        const int l = i ^ j;
+        if (l > i) {
+          const unsigned long long a = keys[i], c = keys[l];
+          if ((a > c) == ((i & k) == 0)) {
+            keys[i] = c;
+            keys[l] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < n; i += NT) out[i] = n - 1 - (int)(unsigned)(keys[i] & 0xFFFFFFFFu);
+  __syncthreads();
+}
+
 }  // namespace nb

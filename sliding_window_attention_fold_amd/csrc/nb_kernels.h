@@ -7,8 +7,16 @@
 
 namespace nb {
 
+// The forward's query tiles: kFwdOrderRows rows of one (batch row, q head).
+// The segment builder orders each batch row's tiles by decreasing band work
+// (fwd_order, B * ceil(L / kFwdOrderRows) entries) when there are at most
+// kFwdOrderMax of them, else writes the identity.
+constexpr int kFwdOrderRows = 128;
+constexpr int kFwdOrderMax = 2048;
+
 struct SegLayout {
   size_t cu_q, cu_k, q_row0, k_row0, row_seg, row_klo, kcov_lo;
+  size_t fwd_order;
   size_t tiles;   // builder scratch: per-tile records
   size_t hash;    // builder scratch: (row, id) set, hash_size 8-byte entries
   size_t hash_size;  // power of two >= 2 * B * S
@@ -70,6 +78,9 @@ struct FwdParams {
   void* o_lo;        // optional: rounding residual of o (fp32 value minus stored value)
   float* lse;
   const int32_t* row_klo;
+  // Optional (null: grid order): per batch row, its query tiles in the order
+  // to launch them (longest first; the segment builder's fwd_order).
+  const int32_t* qt_order;
   int B, Hq, Hkv, L, S, window;
   // Query row i sits at key position q_off + i; row_klo values count keys from
   // k_origin.  Neighbourhood attention: q_off = S - L, k_origin = 0.  A ring
@@ -125,6 +136,16 @@ struct BwdParams {
 
 
 hipError_t launch_segment_build(const SegParams& p, hipStream_t s);
+
+// Compute units of the current device (sizes persistent grids; decides
+// whether a grid runs in one round).
+inline int device_cu_count() {
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+    n_cu = 256;
+  return n_cu;
+}
 hipError_t launch_attn_fwd(const FwdParams& p, int D, bool f32, hipStream_t s);
 // Backward launches: kBwdPrep = Delta + work orders; kBwdMain = both passes in
 // one persistent grid (after kBwdPrep); kBwdDq = Delta + dQ pass; kBwdDkdv =

@@ -126,6 +126,7 @@ size_t nb_segment_offset_k_row0(int B, int L) { return nb::seg_layout(B, L, 1).k
 size_t nb_segment_offset_row_seg(int B, int L) { return nb::seg_layout(B, L, 1).row_seg; }
 size_t nb_segment_offset_row_klo(int B, int L) { return nb::seg_layout(B, L, 1).row_klo; }
 size_t nb_segment_offset_kcov_lo(int B, int L) { return nb::seg_layout(B, L, 1).kcov_lo; }
+size_t nb_segment_offset_fwd_order(int B, int L) { return nb::seg_layout(B, L, 1).fwd_order; }
 
 size_t nb_segment_buffer_elems(int B, int L, int S) {
   if (!dims_ok(B, L, S)) return 0;
@@ -177,7 +178,10 @@ int attn_fwd_kv(const void* q, const nb::KvChunks& kv, void* o, void* o_resid, f
   p.o = o;
   p.o_lo = o_resid;
   p.lse = lse;
-  p.row_klo = seg_buf + nb::seg_layout(B, L, S).row_klo;
+  const nb::SegLayout lay = nb::seg_layout(B, L, S);
+  p.row_klo = seg_buf + lay.row_klo;
+  // the builder's launch order is for the neighbourhood geometry (q_off < 0)
+  p.qt_order = q_off < 0 ? seg_buf + lay.fwd_order : nullptr;
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;

@@ -9,7 +9,7 @@
 // start .. last local row (bottom-right alignment), cu_seqlens_q[i] paired
 // with cu_seqlens_k[i].
 //
-// Two launches over tiles of 2048 positions of one batch row each:
+// Three launches; the first two over tiles of 2048 positions of one batch row each:
 //   1. stats (one workgroup per tile): fold the padding, write the folded ids,
 //      clear the duplicate-id set, and reduce the tile to a few numbers -- its
 //      last run start, its segment ends (ends at or after the shard start),
@@ -24,7 +24,10 @@
 //      per-segment cu_seqlens / row offsets from those prefixes plus in-tile
 //      scans.
 //      Run starts are inserted into an open-addressing set keyed by (row, id)
-//      to detect an id that occurs in two separate runs (status bit 0).
+//      to detect an id that occurs in two separate runs (status bit 0);
+//   3. order (one workgroup per batch row): the forward's launch order of the
+//      row's query tiles, longest band first (scheduling only: any order gives
+//      the same results).
 // Segment indices are global and ordered by (row, position).
 #include "../../include/nbattn.h"
 #include "nb_device.h"
@@ -365,6 +368,57 @@ __global__ __launch_bounds__(SB_NT) void seg_emit_kernel(SegParams p) {
   if (__syncthreads_or(dup) && threadIdx.x == 0) atomicOr(seg + NB_HDR_STATUS, NB_SEG_STATUS_SPLIT_DOC);
 }
 
+// The forward's query tiles of batch row blockIdx.x by decreasing work.  A
+// tile's work: the keys of each 32-row group's band union (the key tiles that
+// group computes) plus those of the tile's union (the tiles its workgroup
+// steps through).  Bands as the forward forms them for the neighbourhood
+// call: row i at key position S - L + i, [max(row_klo, p - W), p].  The
+// hardware starts workgroups in grid order as slots free up, so launching the
+// long tiles first keeps short ones for the end (list scheduling, longest
+// first).
+__global__ __launch_bounds__(SB_NT) void seg_order_kernel(SegParams p) {
+  __shared__ unsigned long long keys[kFwdOrderMax];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int nq = (p.L + kFwdOrderRows - 1) / kFwdOrderRows;
+  int32_t* out = p.seg + p.lay.fwd_order + (size_t)b * nq;
+  const int32_t* klo = p.seg + p.lay.row_klo + (size_t)b * p.L;
+  if (nq > kFwdOrderMax) {
+    for (int t = tid; t < nq; t += SB_NT) out[t] = t;
+    return;
+  }
+  int N = 1;
+  while (N < nq) N <<= 1;
+  for (int t = tid; t < N; t += SB_NT) {
+    unsigned long long key = ~0ull;   // padding sorts last
+    if (t < nq) {
+      unsigned work = 0;
+      int ulo = INT_MAX, uhi = INT_MIN;
+      for (int g = 0; g < kFwdOrderRows / 32; ++g) {
+        int lo = INT_MAX, hi = INT_MIN;
+        const int i0 = t * kFwdOrderRows + 32 * g, i1 = min(i0 + 32, p.L);
+        for (int i = i0; i < i1; ++i) {
+          const int pq = p.S - p.L + i;
+          int bs = max(0, klo[i]);
+          if (p.window >= 0) bs = max(bs, pq - p.window);
+          if (bs <= pq) {
+            lo = min(lo, bs);
+            hi = max(hi, pq + 1);
+          }
+        }
+        if (lo < hi) {
+          work += (unsigned)(hi - lo);
+          ulo = min(ulo, lo);
+          uhi = max(uhi, hi);
+        }
+      }
+      if (ulo < uhi) work += (unsigned)(uhi - ulo);
+      key = work_key(work, t, nq);
+    }
+    keys[t] = key;
+  }
+  order_by_work<SB_NT>(keys, nq, N, out);
+}
+
 SegLayout seg_layout(int B, int L, int S) {
   SegLayout l;
   const size_t N = (size_t)B * L;
@@ -375,7 +429,8 @@ SegLayout seg_layout(int B, int L, int S) {
   l.row_seg = l.k_row0 + N;
   l.row_klo = l.row_seg + N;
   l.kcov_lo = l.row_klo + N;
-  size_t t = l.kcov_lo + B;
+  l.fwd_order = (l.kcov_lo + B + 15) & ~(size_t)15;
+  size_t t = l.fwd_order + (size_t)B * ((L + kFwdOrderRows - 1) / kFwdOrderRows);
   t = (t + 63) & ~(size_t)63;
   l.tiles = t;
   const size_t n_tiles = (size_t)B * ((S + SB_TILE - 1) / SB_TILE);
@@ -399,6 +454,9 @@ hipError_t launch_segment_build(const SegParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(seg_emit_kernel, dim3(n_tiles), dim3(SB_NT), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(seg_order_kernel, dim3((unsigned)p.B), dim3(SB_NT), 0, s, p);
   return hipGetLastError();
 }
 

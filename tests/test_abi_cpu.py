@@ -50,6 +50,11 @@ def test_segment_buffer_sizes():
     assert lib.nb_segment_offset_cu_k(2, 8) == 16 + N + 1
     assert lib.nb_segment_offset_row_klo(2, 8) == 16 + 2 * (N + 1) + 3 * N
     assert n >= lib.nb_segment_offset_kcov_lo(2, 8) + 2 + 2 * 16
+    # the forward's launch order follows kcov_lo, 16-element aligned, one entry per 128-row tile
+    for B, L, S in ((2, 8, 16), (3, 1000, 4000), (1, 8192, 65536)):
+        fo = lib.nb_segment_offset_fwd_order(B, L)
+        assert fo >= lib.nb_segment_offset_kcov_lo(B, L) + B and fo % 16 == 0
+        assert lib.nb_segment_buffer_elems(B, L, S) >= fo + B * ((L + 127) // 128)
 
 
 def _r256(n):
