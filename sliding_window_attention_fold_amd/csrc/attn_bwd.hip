@@ -161,7 +161,11 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   // (at D = 256 the one- and two-register readers leave room to read ahead)
   typedef typename std::conditional<C::XREAD, TileAccessX<TL>, TileAccess<T, TL>>::type Access;
   const Access acc(ln, lane);
-  const TileDma<T, C::BQ, D, C::NW> dma;   // Q and dO tiles share one layout
+  // Q and dO tiles share one layout.  In the skewed schedule role A (waves 0 ..
+  // NKG - 1) issues every copy: role B's dS stores count in the same vector
+  // memory counter as copies, so a role-B wait for a step's copies would also
+  // wait for the stores issued after them -- and role A has the slack.
+  const TileDma<T, C::BQ, D, C::SKEW ? C::NKG : C::NW> dma;
   const int kvh = f % p.Hkv;
   const int code = p.order[f / p.Hkv];
   const int b = code / n_kt, kt = code % n_kt;
@@ -255,8 +259,10 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
     const int i0 = t * C::BQ;
     const int nr = min(C::BQ, Lr - i0);
     const size_t rb = (size_t)hh * Lr + i0;
-    dma.issue_unseen(Qs, q_it + rb * D, nr);
-    dma.issue_unseen(Gs, do_it + rb * D, nr);
+    if (!C::SKEW || role_a) {
+      dma.issue_unseen(Qs, q_it + rb * D, nr);
+      dma.issue_unseen(Gs, do_it + rb * D, nr);
+    }
     if (w == 0) dma_words<true>(ls, lse_it + rb, nr);
     if (w == 1) dma_words<true>(ds, dl_it + rb, nr);
     if (w == 2) dma_words<true>(ks, klo_it + i0, nr);
@@ -440,7 +446,8 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
     // copies in flight.  The loop is not unrolled over the slots: a copy of
     // the step per slot and role outgrows the instruction cache.
     constexpr int LA = NS - 2;
-    const int n_vm = 2 * dma.count() + (w < 3 ? 1 : 0);   // this wave's copies per step
+    static_assert(C::NKG >= 3, "the row metadata copies come from role-A waves 0, 1, 2");
+    const int n_vm = 2 * dma.count() + (w < 3 ? 1 : 0);   // a role-A wave's copies per step
     wait_global();   // the prologue's copies (steps 0 .. LA - 1)
     __syncthreads();
     // Each role runs a loop of its own (same copies and barriers, one branch
@@ -450,25 +457,35 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
       constexpr bool A = decltype(is_a)::value;
       f32x16 dp = f32x16{};   // role B: dP of the previous step
       bool act_prev = false;  // role B: the previous step met the group's keys
+      // The vector memory traffic of a step -- role A's copies of step t + LA
+      // (into step t - 2's slot) and role B's dS stores -- is spread out: the
+      // copies go out after role A's S products, the stores after role B's dK
+      // products.  Issued together at the top of the step they queued behind
+      // each other (measured: the backward 3 % slower; either move alone did
+      // not pay).
       auto stage = [&](int t, int x) {
-        if (t + LA < n_iter) load_slot(x + LA < NS ? x + LA : x + LA - NS, t + LA);   // step t - 2's slot
+        const int slot_next = x + LA < NS ? x + LA : x + LA - NS;
         if constexpr (A) {
+          bool copied = false;
           if (t < n_iter) {
             const StepInfo si = info(sm.klo[x], t);
             if (si.active) {
               f32x16 sacc = f32x16{};
               rows_x_kv(sm.Q[x], sacc);
+              if (t + LA < n_iter) load_slot(slot_next, t + LA);
+              copied = true;
               to_p(sacc, sm.lse[x], sm.klo[x], si, pex[t & 1]);
               __builtin_amdgcn_sched_barrier(0);   // keep the phases' operands apart
               accumulate(sm.G[x], sacc);
             }
           }
+          if (!copied && t + LA < n_iter) load_slot(slot_next, t + LA);
         } else {
           const int xp = x == 0 ? NS - 1 : x - 1;
           if (act_prev) {
             to_ds(dp, pex[(t - 1) & 1], sm.dl[xp]);
-            if (DS && p.dsbuf) store_ds(dp, t - 1, sm.klo[xp]);
             accumulate(sm.Q[xp], dp);
+            if (DS && p.dsbuf) store_ds(dp, t - 1, sm.klo[xp]);
           }
           __builtin_amdgcn_sched_barrier(0);
           act_prev = false;
@@ -480,9 +497,12 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
             }
           }
         }
-        // step t + 1's copies complete (those of later steps may stay in flight)
-        const int later = min(t + LA, n_iter - 1) - (t + 1);
-        if (t + 1 < n_iter) wait_global_le(later > 0 ? n_vm * later : 0);
+        // step t + 1's copies complete (those of later steps may stay in flight);
+        // role B issued none and leaves its dS stores in flight
+        if constexpr (A) {
+          const int later = min(t + LA, n_iter - 1) - (t + 1);
+          if (t + 1 < n_iter) wait_global_le(later > 0 ? n_vm * later : 0);
+        }
         __syncthreads();
       };
       for (int t = 0, x = 0; t <= n_iter; ++t, x = (x + 1 == NS) ? 0 : x + 1) stage(t, x);
