@@ -87,7 +87,8 @@ int nb_version(void);
  *                      identity when a row has more than 2048 tiles.  The
  *                      forward launches its tiles in this order; it changes
  *                      no result
- *   scratch            builder-private (per-tile records, duplicate-id set)
+ *   scratch            builder-private (per-tile records, completion counters,
+ *                      duplicate-id set)
  * Entries past n_seg (past n_seg + 1 for cu_q / cu_k) are unspecified.
  * ------------------------------------------------------------------------ */
 #define NB_SEG_HEADER 16

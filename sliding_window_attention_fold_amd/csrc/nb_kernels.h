@@ -18,6 +18,7 @@ struct SegLayout {
   size_t cu_q, cu_k, q_row0, k_row0, row_seg, row_klo, kcov_lo;
   size_t fwd_order;
   size_t tiles;   // builder scratch: per-tile records
+  size_t done;    // builder scratch: per batch row, emit workgroups finished
   size_t hash;    // builder scratch: (row, id) set, hash_size 8-byte entries
   size_t hash_size;  // power of two >= 2 * B * S
 };

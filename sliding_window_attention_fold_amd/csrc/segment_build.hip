@@ -9,7 +9,7 @@
 // start .. last local row (bottom-right alignment), cu_seqlens_q[i] paired
 // with cu_seqlens_k[i].
 //
-// Three launches; the first two over tiles of 2048 positions of one batch row each:
+// Two launches over tiles of 2048 positions of one batch row each:
 //   1. stats (one workgroup per tile): fold the padding, write the folded ids,
 //      clear the duplicate-id set, and reduce the tile to a few numbers -- its
 //      last run start, its segment ends (ends at or after the shard start),
@@ -25,9 +25,9 @@
 //      scans.
 //      Run starts are inserted into an open-addressing set keyed by (row, id)
 //      to detect an id that occurs in two separate runs (status bit 0);
-//   3. order (one workgroup per batch row): the forward's launch order of the
-//      row's query tiles, longest band first (scheduling only: any order gives
-//      the same results).
+//      The last emit workgroup of a batch row to finish then orders the row's
+//      query tiles for the forward's launch, longest band first (scheduling
+//      only: any order gives the same results).
 // Segment indices are global and ordered by (row, position).
 #include "../../include/nbattn.h"
 #include "nb_device.h"
@@ -137,7 +137,10 @@ __global__ __launch_bounds__(SB_NT) void seg_stats_kernel(SegParams p) {
   unsigned long long* table = reinterpret_cast<unsigned long long*>(p.seg + p.lay.hash);
   for (size_t x = (size_t)blockIdx.x * SB_NT + threadIdx.x; x < p.lay.hash_size; x += (size_t)gridDim.x * SB_NT)
     table[x] = 0ull;
-  if (k == 0 && threadIdx.x == 0) p.seg[p.lay.kcov_lo + b] = S;
+  if (k == 0 && threadIdx.x == 0) {
+    p.seg[p.lay.kcov_lo + b] = S;
+    p.seg[p.lay.done + b] = 0;   // emit workgroups of row b that have finished
+  }
   if (blockIdx.x == 0 && threadIdx.x == 0) p.seg[NB_HDR_STATUS] = 0;
 
   // run starts: the tile's last, and per thread the last one before it (in-tile)
@@ -284,6 +287,88 @@ __device__ TilePrefix tile_prefix(const SegParams& p, int mine, bool write_heade
   return out;
 }
 
+// The forward's query tiles of batch row b by decreasing work (run by the
+// last emit workgroup of the row, once all its row_klo are written).  A
+// tile's work: the keys of each 32-row group's band union (the key tiles that
+// group computes) plus those of the tile's union (the tiles its workgroup
+// steps through).  Bands as the forward forms them for the neighbourhood
+// call: row i at key position S - L + i, [max(row_klo, p - W), p].  The
+// hardware starts workgroups in grid order as slots free up, so launching the
+// long tiles first keeps short ones for the end (list scheduling, longest
+// first).
+__device__ void fwd_order_row(const SegParams& p, int b) {
+  static_assert(kFwdOrderRows % 64 == 0 && SB_NT % 64 == 0, "a wave's 64 rows lie in one tile");
+  __shared__ unsigned long long keys[kFwdOrderMax];
+  __shared__ int t_lo[kFwdOrderMax], t_hi[kFwdOrderMax];   // the tile's union
+  __shared__ unsigned t_work[kFwdOrderMax];                 // sum of its groups' spans
+  const int tid = threadIdx.x;
+  const int nq = (p.L + kFwdOrderRows - 1) / kFwdOrderRows;
+  int32_t* out = p.seg + p.lay.fwd_order + (size_t)b * nq;
+  const int32_t* klo = p.seg + p.lay.row_klo + (size_t)b * p.L;
+  if (nq > kFwdOrderMax) {
+    for (int t = tid; t < nq; t += SB_NT) out[t] = t;
+    return;
+  }
+  for (int t = tid; t < nq; t += SB_NT) {
+    t_lo[t] = INT_MAX;
+    t_hi[t] = INT_MIN;
+    t_work[t] = 0u;
+  }
+  __syncthreads();
+  // One 32-row group per thread and pass: its 32 band starts are loaded
+  // together (one load latency), then the group's union [lo, hi) over its
+  // real rows goes into its tile's sums.
+  const int ng = (p.L + 31) / 32;
+  for (int gi = tid; gi < ng; gi += SB_NT) {
+    const int i0 = 32 * gi;
+    int kl[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) kl[r] = i0 + r < p.L ? klo[i0 + r] : 0;
+    int lo = INT_MAX, hi = INT_MIN;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const int pq = p.S - p.L + i0 + r;
+      int bs = max(0, kl[r]);
+      if (p.window >= 0) bs = max(bs, pq - p.window);
+      if (i0 + r < p.L && bs <= pq) {
+        lo = min(lo, bs);
+        hi = max(hi, pq + 1);
+      }
+    }
+    if (lo < hi) {
+      const int t = i0 / kFwdOrderRows;
+      atomicAdd(&t_work[t], (unsigned)(hi - lo));
+      atomicMin(&t_lo[t], lo);
+      atomicMax(&t_hi[t], hi);
+    }
+  }
+  __syncthreads();
+  int N = 1;
+  while (N < nq) N <<= 1;
+  for (int t = tid; t < N; t += SB_NT) {
+    unsigned long long key = ~0ull;   // padding sorts last
+    if (t < nq) {
+      unsigned work = t_work[t];
+      if (t_lo[t] < t_hi[t]) work += (unsigned)(t_hi[t] - t_lo[t]);
+      key = work_key(work, t, nq);
+    }
+    keys[t] = key;
+  }
+  if (nq <= SB_NT) {
+    // one tile per thread: its rank is the number of smaller keys (the keys
+    // are distinct), the same order the sort below gives
+    __syncthreads();
+    if (tid < nq) {
+      const unsigned long long k = keys[tid];
+      int rank = 0;
+      for (int u = 0; u < nq; ++u) rank += keys[u] < k ? 1 : 0;
+      out[rank] = tid;
+    }
+    return;
+  }
+  order_by_work<SB_NT>(keys, nq, N, out);
+}
+
 __global__ __launch_bounds__(SB_NT) void seg_emit_kernel(SegParams p) {
   __shared__ int sh[2 * SB_WAVES];
   const int S = p.S, L = p.L, off = S - L;
@@ -366,57 +451,19 @@ __global__ __launch_bounds__(SB_NT) void seg_emit_kernel(SegParams p) {
     }
   }
   if (__syncthreads_or(dup) && threadIdx.x == 0) atomicOr(seg + NB_HDR_STATUS, NB_SEG_STATUS_SPLIT_DOC);
-}
 
-// The forward's query tiles of batch row blockIdx.x by decreasing work.  A
-// tile's work: the keys of each 32-row group's band union (the key tiles that
-// group computes) plus those of the tile's union (the tiles its workgroup
-// steps through).  Bands as the forward forms them for the neighbourhood
-// call: row i at key position S - L + i, [max(row_klo, p - W), p].  The
-// hardware starts workgroups in grid order as slots free up, so launching the
-// long tiles first keeps short ones for the end (list scheduling, longest
-// first).
-__global__ __launch_bounds__(SB_NT) void seg_order_kernel(SegParams p) {
-  __shared__ unsigned long long keys[kFwdOrderMax];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int nq = (p.L + kFwdOrderRows - 1) / kFwdOrderRows;
-  int32_t* out = p.seg + p.lay.fwd_order + (size_t)b * nq;
-  const int32_t* klo = p.seg + p.lay.row_klo + (size_t)b * p.L;
-  if (nq > kFwdOrderMax) {
-    for (int t = tid; t < nq; t += SB_NT) out[t] = t;
-    return;
+  // The last of the row's T workgroups to finish orders its forward tiles:
+  // each publishes its writes (fence) before its count; the last one fences
+  // again before it reads the others' row_klo.
+  __shared__ int last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(seg + p.lay.done + b, 1) == T - 1;
+  __syncthreads();
+  if (last) {
+    __threadfence();
+    fwd_order_row(p, b);
   }
-  int N = 1;
-  while (N < nq) N <<= 1;
-  for (int t = tid; t < N; t += SB_NT) {
-    unsigned long long key = ~0ull;   // padding sorts last
-    if (t < nq) {
-      unsigned work = 0;
-      int ulo = INT_MAX, uhi = INT_MIN;
-      for (int g = 0; g < kFwdOrderRows / 32; ++g) {
-        int lo = INT_MAX, hi = INT_MIN;
-        const int i0 = t * kFwdOrderRows + 32 * g, i1 = min(i0 + 32, p.L);
-        for (int i = i0; i < i1; ++i) {
-          const int pq = p.S - p.L + i;
-          int bs = max(0, klo[i]);
-          if (p.window >= 0) bs = max(bs, pq - p.window);
-          if (bs <= pq) {
-            lo = min(lo, bs);
-            hi = max(hi, pq + 1);
-          }
-        }
-        if (lo < hi) {
-          work += (unsigned)(hi - lo);
-          ulo = min(ulo, lo);
-          uhi = max(uhi, hi);
-        }
-      }
-      if (ulo < uhi) work += (unsigned)(uhi - ulo);
-      key = work_key(work, t, nq);
-    }
-    keys[t] = key;
-  }
-  order_by_work<SB_NT>(keys, nq, N, out);
 }
 
 SegLayout seg_layout(int B, int L, int S) {
@@ -434,7 +481,8 @@ SegLayout seg_layout(int B, int L, int S) {
   t = (t + 63) & ~(size_t)63;
   l.tiles = t;
   const size_t n_tiles = (size_t)B * ((S + SB_TILE - 1) / SB_TILE);
-  size_t h = l.tiles + n_tiles * kTileRec;
+  l.done = l.tiles + n_tiles * kTileRec;
+  size_t h = l.done + (size_t)B;
   h = (h + 63) & ~(size_t)63;   // 8-byte set entries, 256-byte aligned
   l.hash = h;
   size_t hs = 64;
@@ -454,9 +502,6 @@ hipError_t launch_segment_build(const SegParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(seg_emit_kernel, dim3(n_tiles), dim3(SB_NT), 0, s, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(seg_order_kernel, dim3((unsigned)p.B), dim3(SB_NT), 0, s, p);
   return hipGetLastError();
 }
 
