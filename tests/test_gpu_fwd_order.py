@@ -60,7 +60,10 @@ def _docs(rng, S, hi):
 
 def test_order_matches_host_ranking():
     rng = np.random.default_rng(7)
-    cases = [(1, 256, 128, 64), (3, 4000, 1000, -1), (2, 9000, 8193, 700), (1, 300, 1, 0), (4, 8192, 4096, 512)]
+    # (the builder ranks up to 256 tiles per batch row by counting and sorts beyond; the last two cases take the
+    # sort (313 tiles) and the identity past 2048 tiles)
+    cases = [(1, 256, 128, 64), (3, 4000, 1000, -1), (2, 9000, 8193, 700), (1, 300, 1, 0), (4, 8192, 4096, 512),
+             (2, 45000, 40000, 900), (1, 270000, 263000, 300)]
     for trial, (B, S, L, W) in enumerate(cases):
         ids = np.stack([_docs(rng, S, int(rng.choice([8, 200, 3000]))) for _ in range(B)])
         pad = (rng.random((B, S)) < 0.05).astype(np.uint8) if trial % 2 else None
