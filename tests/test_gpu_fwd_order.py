@@ -94,3 +94,25 @@ def test_order_leaves_results_unchanged():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
     assert torch.equal(s1.lse, s2.lse)
+
+
+def test_multi_round_forward_full_parity():
+    """A forward whose grid exceeds one round of workgroups (18 query tiles x 32 heads = 576 workgroups, two per
+    CU at D = 128) runs in the builder's order; O, LSE and the gradients match the oracle element by element."""
+    from gpu_cases import custom_inputs, full_parity
+
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    B, Hq, Hkv, D, L, S, W = 1, 32, 8, 128, 2200, 2600, 300
+    assert ((L + ROWS - 1) // ROWS) * Hq * B > 2 * n_cu, "the grid must take more than one round here"
+    rng = np.random.default_rng(11)
+    ids = _docs(rng, S, 400)[None]
+    # padding as whole documents (every 7th) and a tail: every document stays one run of its id
+    ids[np.isin(ids, np.arange(7, ids.max() + 1, 7))] = 0
+    pad = np.zeros((B, S), np.uint8)
+    pad[:, -60:] = 1
+    say(f"[fwd order] multi-round forward B={B} Hq={Hq} Hkv={Hkv} D={D} L={L} S={S} W={W}")
+    seg = nb.segment_build(torch.from_numpy(ids).cuda(), L, W, torch.from_numpy(pad).cuda())
+    assert seg.header_host()["status"] == 0
+    order = seg.fwd_order.cpu().numpy()
+    assert not np.array_equal(order, np.arange(order.size)), "the order should differ from grid order"
+    full_parity(custom_inputs(ids, pad, Hq, Hkv, D, L, W, "bf16", seed=5), "bf16")
