@@ -130,6 +130,10 @@ struct DkvSmemTilesFirst : DkvTiles<T, D>, DkvMeta<T, D> {};
 template <typename T, int D>
 using DkvSmem = typename std::conditional<DkvCfg<T, D>::SKEW, DkvSmemMetaFirst<T, D>, DkvSmemTilesFirst<T, D>>::type;
 
+// The dK/dV item's rows on their way out (nb_device.h: RowStage).
+template <typename T, int D>
+using DkvStage = RowStage<T, DkvCfg<T, D>::NW, DkvCfg<T, D>::DA>;
+
 // Slot of key k (0..31) in a row of a stored 32 x 32 dS block: k with bits 2
 // and 3 swapped.  A lane's B fragment of a 32x32x16 product covers keys
 // 4g + {0..3} and 8 + 4g + {0..3} of a 16-key half (g = lane / 32), the
@@ -142,7 +146,7 @@ __device__ __forceinline__ constexpr int ds_slot(int k) { return (k & 0x13) | ((
 // DS: the item may store dS (p.dsbuf non-null); compiled into the dK/dV-only
 // kernel alone, so the combined kernel carries none of its registers.
 template <typename T, int D, bool CH, bool DS>
-__device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm, int f) {
+__device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm, DkvStage<T, D>& stage, int f) {
   typedef DkvCfg<T, D> C;
   typedef Tile<T, C::BQ, D> TL;
   typedef typename Frag<T>::type F;
@@ -599,6 +603,24 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
     }
   }
 
+  if constexpr (DkvStage<T, D>::ON) {
+    const float sc = role_a ? 1.f : p.scale;
+    const int bh = b * p.Hkv + kvh;
+    const int nrows = min(32, p.S - jw);
+    __syncthreads();   // every wave is done with the ring and the hand-over the staging overwrites
+    if constexpr (CH) {
+      const KvSpan<T> sp(p.kv, role_a ? kDV : kDK, bh, j0, jmax, D);
+      stage_rows_in<T, C::DA>(&stage.r[w][0][0], gacc, sc);
+      stage_rows_store_at<T, C::DA>(&stage.r[w][0][0], nrows, [&](int r) {
+        return (sp.ok ? sp.row(jw + r, D) : kv_row<T>(p.kv, role_a ? kDV : kDK, bh, jw + r, D)) + hf * C::DA;
+      });
+    } else {
+      T* const base = reinterpret_cast<T*>(role_a ? p.kv.dv[0] : p.kv.dk[0]) + ((size_t)bh * p.S + jw) * D + hf * C::DA;
+      stage_rows_in<T, C::DA>(&stage.r[w][0][0], gacc, sc);
+      stage_rows_store<T, C::DA>(&stage.r[w][0][0], base, D, nrows);
+    }
+    return;
+  }
   if (j < p.S) {
     T* dst;
     if constexpr (CH) {
@@ -643,7 +665,11 @@ struct DqCfg {
   static constexpr int BN = (D * sizeof(T) <= 256) ? 64 : 32;   // keys per tile
   // operand fragments read ahead of their MFMA; 0 = plain loop (float path)
   static constexpr int AHEAD = (sizeof(T) != 2) ? 0 : (D <= 128) ? 4 : 2;
+  static constexpr int DQW = FUSED ? D : D / 2;   // columns of one wave's dQ part
 };
+// The dQ item's rows on their way out (nb_device.h: RowStage).
+template <typename T, int D>
+using DqStage = RowStage<T, DqCfg<T, D>::NW, DqCfg<T, D>::DQW>;
 
 // LDS of one dQ item: two K/V tile pairs (one filled by DMA while the other is
 // read) and the P / dP exchange of each query group.
@@ -670,7 +696,7 @@ struct DqSmem {
 // whose key range touches three or more chunks is appended to p.cross and left
 // to the follow-up kernel, which runs it as kKvAny.
 template <typename T, int D, int KV>
-__device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, int f) {
+__device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, DqStage<T, D>& stage, int f) {
   typedef DqCfg<T, D> C;
   typedef Tile<T, C::BN, D> TL;
   typedef typename Frag<T>::type F;
@@ -964,6 +990,18 @@ __device__ __forceinline__ void dq_item(const BwdParams& p, DqSmem<T, D>& sm, in
     }
   }
 
+  if constexpr (DqStage<T, D>::ON) {
+    static_assert(DH * 32 == C::DQW, "a wave's dQ part");
+    if (p.dq_mode == kDqStore) {
+      const int i_grp = qt * C::BM + 32 * qg;   // the wave's first row (uniform: a scalar store base)
+      T* const st = &stage.r[w][0][0];
+      __syncthreads();   // every wave is done with the K/V ring and the exchange the staging overwrites
+      stage_rows_in<T, C::DQW>(st, dqacc, p.scale);
+      stage_rows_store<T, C::DQW>(st, reinterpret_cast<T*>(p.dq) + (((size_t)b * p.Hq + h) * p.L + i_grp) * D + 32 * dh0,
+                                  D, min(32, p.L - i_grp));
+      return;
+    }
+  }
   if (in_range && p.dq_mode == kDqStore) {
     T* dqp = reinterpret_cast<T*>(p.dq) + qrow * D;
 #pragma unroll
@@ -1020,14 +1058,30 @@ struct DqsCfg {
   static constexpr int OCC = (sizeof(T) == 2 && D <= 256) ? 2 : 1;
 };
 
+// Its LDS: two K tiles and the key-range reduction; after the loop, the dQ rows
+// on their way out.
+template <typename T, int D>
+struct DqsSmem {
+  typedef DqsCfg<T, D> C;
+  union {
+    struct {
+      __attribute__((aligned(1024))) T K0[Tile<T, C::BN, D>::ELEMS];
+      __attribute__((aligned(1024))) T K1[Tile<T, C::BN, D>::ELEMS];
+      int red[C::NW][2];
+    };
+    RowStage<T, C::NW, D> st;
+  };
+};
+
 template <typename T, int D, int KV>
 __global__ __launch_bounds__(256, (DqsCfg<T, D>::OCC)) void dq_ds_kernel(BwdParams p) {
   typedef DqsCfg<T, D> C;
   typedef Tile<T, C::BN, D> TL;
   typedef typename Frag<T>::type F;
-  __shared__ __attribute__((aligned(1024))) T K0[TL::ELEMS];
-  __shared__ __attribute__((aligned(1024))) T K1[TL::ELEMS];
-  __shared__ int red[C::NW][2];
+  __shared__ DqsSmem<T, D> sm;
+  T* const K0 = sm.K0;
+  T* const K1 = sm.K1;
+  int (*red)[2] = sm.red;
   const int grp = p.Hq / p.Hkv;
   const int ngroups = p.B * p.Hkv;
   const int gid = blockIdx.x % ngroups, rest = blockIdx.x / ngroups;
@@ -1151,6 +1205,15 @@ __global__ __launch_bounds__(256, (DqsCfg<T, D>::OCC)) void dq_ds_kernel(BwdPara
     compute(K1, f1, j0 + C::BN);
   }
 
+  if constexpr (RowStage<T, C::NW, D>::ON) {
+    if (p.dq_mode == kDqStore) {
+      __syncthreads();   // every wave is done with the K tiles the staging overwrites
+      T* const base = reinterpret_cast<T*>(p.dq) + (((size_t)b * p.Hq + h) * p.L + i0) * D;
+      stage_rows_in<T, D>(&sm.st.r[w][0][0], oacc, p.scale);
+      stage_rows_store<T, D>(&sm.st.r[w][0][0], base, D, min(32, p.L - i0));
+      return;
+    }
+  }
   if (!in_range || (!w_any && p.dq_mode == kDqAddF32)) return;   // (no key: nothing to add)
   const size_t qrow = ((size_t)b * p.Hq + h) * p.L + i;
 #pragma unroll
@@ -1363,15 +1426,19 @@ size_t dq_cross_elems(int B, int Hq, int L) { return (size_t)B * Hq * ((L + 31) 
 template <typename T, int D>
 union BwdSmemBoth {
   DkvSmem<T, D> kv;
+  DkvStage<T, D> kst;
   DqSmem<T, D> q;
+  DqStage<T, D> qst;
 };
 template <typename T, int D>
-struct BwdSmemKvOnly {
+union BwdSmemKvOnly {
   DkvSmem<T, D> kv;
+  DkvStage<T, D> kst;
 };
 template <typename T, int D>
-struct BwdSmemQOnly {
+union BwdSmemQOnly {
   DqSmem<T, D> q;
+  DqStage<T, D> qst;
 };
 template <typename T, int D, int MODE>
 struct BwdSmemFor {
@@ -1397,7 +1464,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void b
   // runs alone, and a float32 dQ item's tiles would not fit beside nothing)
   __shared__ typename BwdSmemFor<T, D, MODE>::type sm;
   auto dkdv = [&](int f) {
-    if constexpr (MODE != 2) dkdv_item<T, D, KV != kKvConcat, MODE == 1>(p, sm.kv, f);
+    if constexpr (MODE != 2) dkdv_item<T, D, KV != kKvConcat, MODE == 1>(p, sm.kv, sm.kst, f);
   };
   const int n_kv = (MODE & 1) ? p.B * ((p.S + DkvCfg<T, D>::BK - 1) / DkvCfg<T, D>::BK) * p.Hkv : 0;
   const int n_q = (MODE & 2) ? p.B * ((p.L + DqCfg<T, D>::BM - 1) / DqCfg<T, D>::BM) * p.Hq : 0;
@@ -1414,10 +1481,10 @@ __global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void b
     if constexpr (MODE == 1) {
       dkdv(f);
     } else if constexpr (MODE == 2) {
-      dq_item<T, D, KV>(p, sm.q, f);
+      dq_item<T, D, KV>(p, sm.q, sm.qst, f);
     } else {
       if (f < n_kv) dkdv(f);
-      else dq_item<T, D, KV>(p, sm.q, f - n_kv);
+      else dq_item<T, D, KV>(p, sm.q, sm.qst, f - n_kv);
     }
     __syncthreads();  // this item's LDS is dead before the next fetch
   }
@@ -1427,7 +1494,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void b
 // or more chunks), taken from p.cross in the order they were appended.
 template <typename T, int D>
 __global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void bwd_dq_cross_kernel(BwdParams p) {
-  __shared__ DqSmem<T, D> sm;
+  __shared__ BwdSmemQOnly<T, D> sm;
   int* const slot = reinterpret_cast<int*>(&sm);  // the fetched item, between items only
   for (;;) {
     if (threadIdx.x == 0) {
@@ -1438,7 +1505,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void b
     const int f = *slot;
     __syncthreads();
     if (f < 0) break;
-    dq_item<T, D, kKvAny>(p, sm, f);
+    dq_item<T, D, kKvAny>(p, sm.q, sm.qst, f);
     __syncthreads();
   }
 }

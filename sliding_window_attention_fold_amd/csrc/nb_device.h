@@ -134,6 +134,15 @@ __device__ __forceinline__ void store_quad_split(T* hi, T* lo, float a, float b,
   }
 }
 
+// This lane's index in its wave, from an instruction the compiler cannot move:
+// values derived from it are formed where they are used, not hoisted out of
+// the loops before that point to sit in registers across them.
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // The value lane l ^ 32 holds (the other half of the wave), through
 // v_permlane32_swap: no LDS round trip and no wait on outstanding LDS reads.
 // The swap trades the upper half of its first operand with the lower half of
@@ -173,6 +182,66 @@ constexpr int kLdsPadBytes = 16;
 template <typename T> struct Pad { static constexpr int elems = kLdsPadBytes / sizeof(T); };
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// Rows of a result leave through LDS (bf16): a lane's accumulators hold four
+// columns of one row, so stored directly a store instruction writes 16 bytes
+// to each of 32 rows (32 cache lines for 512 bytes); staged and read back as
+// 16-byte row pieces, an instruction writes whole row segments.  NWS waves
+// stage 32 rows of W columns each; rows padded by 16 bytes (the 8-byte writes
+// down a column spread over the banks; rows stay 16-byte aligned).
+template <typename T, int NWS, int W>
+struct RowStage {
+  static constexpr bool ON = sizeof(T) == 2;
+  static constexpr int RS = W + 8;
+  __attribute__((aligned(1024))) T r[ON ? NWS : 1][ON ? 32 : 1][ON ? RS : 1];
+};
+// One wave's 32 x W block (lane: row ln, columns 32 d + 8 rq + 4 g .. + 3 of
+// block d, values x[d][4 rq + e] * sc) written to its staging rows st.
+// Wave-local: LDS operations of one wave complete in order, so the read-back
+// below sees every lane's writes without a barrier.
+template <typename T, int W, typename Acc>
+__device__ __forceinline__ void stage_rows_in(T* st, const Acc& x, float sc) {
+  typedef typename Quad<T>::type Q4;
+  constexpr int RS = W + 8;
+  const int lane = lane_here(), ln = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int d = 0; d < W / 32; ++d) {
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      Q4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = to_elem<T>(x[d][4 * rq + e] * sc);
+      *reinterpret_cast<Q4*>(st + ln * RS + 32 * d + 8 * rq + 4 * g) = v;
+    }
+  }
+}
+// The staged rows r < nrows stored as 16-byte pieces: row r at base + r * ld
+// elements (base wave-uniform, so each store takes a scalar base and a 32-bit
+// lane offset).
+template <typename T, int W>
+__device__ __forceinline__ void stage_rows_store(const T* st, T* base, size_t ld, int nrows) {
+  constexpr int RS = W + 8, LPR = W / 8, RPI = 64 / LPR;
+  const int lane = lane_here(), rl = lane / LPR, c = 8 * (lane % LPR);
+  const uint32_t voff = (uint32_t)((rl * ld + c) * sizeof(T));
+#pragma unroll
+  for (int r0 = 0; r0 < 32; r0 += RPI) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(st + (r0 + rl) * RS + c);
+    char* const row = reinterpret_cast<char*>(base + r0 * ld);
+    if (r0 + rl < nrows) *reinterpret_cast<u32x4*>(row + voff) = v;
+  }
+}
+// As above, with each row's address from row_ptr(r) (rows not evenly spaced).
+template <typename T, int W, typename RowPtr>
+__device__ __forceinline__ void stage_rows_store_at(const T* st, int nrows, RowPtr row_ptr) {
+  constexpr int RS = W + 8, LPR = W / 8, RPI = 64 / LPR;
+  const int lane = lane_here(), rl = lane / LPR, c = 8 * (lane % LPR);
+#pragma unroll
+  for (int r0 = 0; r0 < 32; r0 += RPI) {
+    const int r = r0 + rl;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * RS + c);
+    if (r < nrows) *reinterpret_cast<u32x4*>(row_ptr(r) + c) = v;
+  }
+}
 
 // ---------------------------------------------------------------------------
 // LDS tiles.  A tile holds ROWS rows of a row-major [*, D] matrix, row-major in
