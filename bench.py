@@ -334,7 +334,7 @@ def main() -> int:
     nseg = lib.nb_segment_buffer_elems(B, L, S)
     segbuf = torch.empty((nseg,), dtype=torch.int32, device=dev)
     out = torch.empty_like(qd)
-    resid = torch.empty_like(qd)
+    resid = torch.empty(qd.shape, dtype=torch.int8, device=dev)   # the forward's residual codes
     lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
     dq = torch.empty_like(qd)
     dk = torch.empty_like(kd)
@@ -531,7 +531,7 @@ def chunks_main(args) -> int:
     folded = torch.empty((B, S2), dtype=torch.int32, device=dev)
     nseg = lib.nb_segment_buffer_elems(B, L, S2)
     segbuf = torch.empty((nseg,), dtype=torch.int32, device=dev)
-    out, resid = torch.empty_like(qd), torch.empty_like(qd)
+    out, resid = torch.empty_like(qd), torch.empty(qd.shape, dtype=torch.int8, device=dev)
     lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
     dq = torch.empty_like(qd)
     dks = [torch.empty_like(c.k) for c in chunks]
@@ -666,7 +666,7 @@ def ring_main(args) -> int:
     lse_step = torch.empty((B, Hq, Lc), dtype=torch.float32, device=dev)
     out_acc = torch.empty((B, Hq, Lc, D), dtype=torch.float32, device=dev)
     lse_acc = torch.empty((B, Hq, Lc), dtype=torch.float32, device=dev)
-    out, resid = torch.empty_like(qd), torch.empty_like(qd)
+    out, resid = torch.empty_like(qd), torch.empty(qd.shape, dtype=torch.int8, device=dev)
     live_idx = torch.empty((B * Lc,), dtype=torch.int32, device=dev)
     n_live = torch.empty((1,), dtype=torch.int32, device=dev)
     dq_c = torch.empty_like(qd)

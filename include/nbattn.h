@@ -148,10 +148,15 @@ size_t nb_attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, 
  *   _cp_blockdiag_varlen.
  *   q   [B,Hq,L,D], k/v [B,Hkv,S,D]   (dtype), device
  *   o   [B,Hq,L,D] out (dtype); padding rows written 0
- *   o_resid [B,Hq,L,D] out (dtype) or NULL: the rounding residual of o (the
- *       fp32 result minus the stored value, rounded to dtype).  Saved for the
- *       backward, whose Delta = dO . O then uses an fp32-accurate O; for bf16
- *       the backward is only within tolerance with it (for float32 pass NULL).
+ *   o_resid [B,Hq,L,D] int8 out, or NULL: the rounding residual of o, one
+ *       signed byte per element.  With a the fp32 result, v = bf16(a) the
+ *       stored value and u = 2^(max(e, 1) - 134) its ulp (e = v's biased
+ *       exponent field), the code is a - v in units of u / 254, rounded to
+ *       nearest even and clamped to [-127, 127]; v + code * u / 254 is within
+ *       u / 508 of a (about 17 significant bits).  Saved for the backward,
+ *       whose Delta = dO . O then uses an fp32-accurate O; for bf16 the
+ *       backward is only within tolerance with it.  float32: ignored (pass
+ *       NULL; O is the fp32 result itself).
  *   lse [B,Hq,L] float32 out: natural-log sum of exp(scale * q.k) over the
  *       band; -inf for padding rows
  *   seg_buf from nb_segment_build with the same B, L, S and window_left
@@ -183,7 +188,8 @@ size_t nb_attn_bwd_workspace_bytes_window(int B, int Hq, int Hkv, int L, int S, 
  *   cp_local_ring page, sliding_ring_compute_fa_bwd (returns dQ and per-owner
  *   dK/dV) and _owner_grad_dict (owners this shard did not attend get zeros).
  *   dout, q, o [B,Hq,L,D]; k, v [B,Hkv,S,D]; lse [B,Hq,L] (from nb_attn_fwd);
- *   o_resid    the residual nb_attn_fwd saved, or NULL (Delta from o alone)
+ *   o_resid    the int8 residual codes nb_attn_fwd saved, or NULL (Delta from o
+ *              alone); ignored for float32
  *   dq [B,Hq,L,D] out (0 on padding rows)
  *   dk, dv [B,Hkv,S,D] out; every row is written, keys no query attended are 0
  *   owner_off  HOST int32 [n_owner + 1], ascending neighbourhood offsets of the

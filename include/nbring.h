@@ -84,9 +84,10 @@ int nb_ring_merge_live(float* out_acc, float* lse_acc, const void* out_step, con
                        int dtype, void* stream);
 
 /* The merged fp32 output as the attention output: out = out_acc rounded to
- * dtype, out_resid (optional, may be NULL) = the rounding residual
- * out_acc - out rounded to dtype, which the backward adds back for an
- * fp32-accurate Delta.  R rows of D values. */
+ * dtype; for bf16, out_resid (optional, may be NULL; int8, R * D bytes) = the
+ * rounding residual codes of out (as nb_attn_fwd's o_resid, nbattn.h), which
+ * the backward adds back for an fp32-accurate Delta; for float32 out_resid is
+ * ignored.  R rows of D values. */
 int nb_ring_finalize(const float* out_acc, void* out, void* out_resid, int64_t R, int D, int dtype, void* stream);
 
 /* Flags of nb_ring_chunk_bwd. */

@@ -152,7 +152,7 @@ class Saved(NamedTuple):
     k: torch.Tensor
     v: torch.Tensor
     out: torch.Tensor
-    out_resid: Optional[torch.Tensor]  # rounding residual of out (bf16 path), None for float32
+    out_resid: Optional[torch.Tensor]  # int8 rounding-residual codes of out (bf16 path), None for float32
     lse: torch.Tensor
     seg: Segments
     scale: float
@@ -216,7 +216,7 @@ def attn_fwd(q: torch.Tensor, k_nb: torch.Tensor, v_nb: torch.Tensor, seg: Segme
     B, Hq, Hkv, L, S, D = _check_qkv(q, k_nb, v_nb, seg)
     scale = D ** -0.5 if scale is None else float(scale)
     out = torch.empty_like(q)
-    resid = torch.empty_like(q) if q.dtype == torch.bfloat16 else None
+    resid = torch.empty(q.shape, dtype=torch.int8, device=q.device) if q.dtype == torch.bfloat16 else None
     lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
     _lib.check(lib.nb_attn_fwd(_ptr(q), _ptr(k_nb), _ptr(v_nb), _ptr(out), _ptr(resid), _ptr(lse), _ptr(seg.buf),
                                B, Hq, Hkv, L, S, D, scale, seg.window, float(dropout_p), _DTYPES[q.dtype],
@@ -364,7 +364,7 @@ def attn_fwd_chunks(q: torch.Tensor, chunks: List[KvChunk], seg: Segments, scale
     B, Hq, Hkv, L, S, D, n, kp, vp, ln, st, rw = _chunk_args(chunks, q, seg)
     scale = D ** -0.5 if scale is None else float(scale)
     out = torch.empty_like(q)
-    resid = torch.empty_like(q) if q.dtype == torch.bfloat16 else None
+    resid = torch.empty(q.shape, dtype=torch.int8, device=q.device) if q.dtype == torch.bfloat16 else None
     lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
     _lib.check(lib.nb_attn_fwd_chunks(_ptr(q), ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp, ctypes.c_void_p),
                                       ctypes.cast(ln, ctypes.c_void_p), ctypes.cast(st, ctypes.c_void_p),

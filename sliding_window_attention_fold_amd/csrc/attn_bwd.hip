@@ -1263,10 +1263,14 @@ template <typename T, int D>
 __device__ __forceinline__ void delta_rows(const BwdParams& p, int wg) {
   typedef DeltaCfg<T, D> C;
   typedef T VE __attribute__((ext_vector_type(C::V)));   // one 16-byte (or wider) load
+  typedef int8_t VR __attribute__((ext_vector_type(C::V)));   // the residual codes of the same elements
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int sub = lane % C::LPR, rsub = lane / C::LPR;
   const long long n_rows = (long long)p.B * p.Hq * p.L;
-  VE dv[C::IT], ov[C::IT], lv[C::IT];
+  // (bf16: O plus its saved residual codes, nb_device.h: resid_value; float32 O is exact)
+  const bool with_resid = sizeof(T) == 2 && p.o_lo != nullptr;
+  VE dv[C::IT], ov[C::IT];
+  VR lv[C::IT];
   long long row[C::IT];
 #pragma unroll
   for (int r = 0; r < C::IT; ++r) {
@@ -1275,13 +1279,19 @@ __device__ __forceinline__ void delta_rows(const BwdParams& p, int wg) {
     const size_t e0 = (size_t)rr * D + (size_t)sub * C::V;
     dv[r] = *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.dout) + e0);
     ov[r] = *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.o) + e0);
-    lv[r] = p.o_lo ? *reinterpret_cast<const VE*>(reinterpret_cast<const T*>(p.o_lo) + e0) : ov[r];
+    lv[r] = with_resid ? *reinterpret_cast<const VR*>(reinterpret_cast<const int8_t*>(p.o_lo) + e0) : VR{};
   }
 #pragma unroll
   for (int r = 0; r < C::IT; ++r) {
     float part = 0.f;
 #pragma unroll
-    for (int e = 0; e < C::V; ++e) part += to_f32(dv[r][e]) * (to_f32(ov[r][e]) + (p.o_lo ? to_f32(lv[r][e]) : 0.f));
+    for (int e = 0; e < C::V; ++e) {
+      float o = to_f32(ov[r][e]);
+      if constexpr (sizeof(T) == 2) {
+        if (with_resid) o += resid_value(lv[r][e], ov[r][e]);
+      }
+      part += to_f32(dv[r][e]) * o;
+    }
 #pragma unroll
     for (int o = C::LPR / 2; o > 0; o >>= 1) part += __shfl_xor(part, o);
     if (row[r] < n_rows && sub == 0) {

@@ -345,31 +345,26 @@ __global__ __launch_bounds__((FwdCfg<T, D>::NT), (FwdCfg<T, D>::OCC)) void attn_
     stage_rows_in<T, C::DW>(st, oacc, inv);
     stage_rows_store<T, C::DW>(st, reinterpret_cast<T*>(p.o) + grp0, D, nrows);
     if (p.o_lo != nullptr) {
-      // what the rounding to bf16 left over (the same products rounded again)
-#pragma unroll
-      for (int d = 0; d < C::DW / 32; ++d) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float a = oacc[d][e] * inv;
-          oacc[d][e] = a - to_f32(to_elem<T>(a));
-        }
-      }
-      stage_rows_in<T, C::DW>(st, oacc, 1.f);
-      stage_rows_store<T, C::DW>(st, reinterpret_cast<T*>(p.o_lo) + grp0, D, nrows);
+      // what the rounding to bf16 left over, as one byte per element (the
+      // same products rounded again; the staged O rows were read back first:
+      // a wave's LDS operations complete in order)
+      uint8_t* const sc = reinterpret_cast<uint8_t*>(st);
+      stage_codes_in<C::DW>(sc, oacc, inv);
+      stage_codes_store<C::DW>(sc, reinterpret_cast<uint8_t*>(p.o_lo) + grp0, D, nrows);
     }
     if (g == 0 && hf == 0 && in_range) p.lse[qrow] = real ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
     return;
   }
+  // float32: O is the fp32 result itself (no residual)
   if (!in_range) return;
   T* op = reinterpret_cast<T*>(p.o) + qrow * D + hf * C::DW;
-  T* olp = p.o_lo ? reinterpret_cast<T*>(p.o_lo) + qrow * D + hf * C::DW : nullptr;
 #pragma unroll
   for (int d = 0; d < C::DW / 32; ++d) {
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       const int dd = 32 * d + 8 * rq + 4 * g;
-      store_quad_split<T>(op + dd, olp ? olp + dd : nullptr, oacc[d][4 * rq] * inv, oacc[d][4 * rq + 1] * inv,
-                          oacc[d][4 * rq + 2] * inv, oacc[d][4 * rq + 3] * inv);
+      store_quad<T>(op + dd, oacc[d][4 * rq] * inv, oacc[d][4 * rq + 1] * inv, oacc[d][4 * rq + 2] * inv,
+                    oacc[d][4 * rq + 3] * inv);
     }
   }
   if (g == 0 && hf == 0) p.lse[qrow] = real ? (m_ref + log2f(l)) * kLn2 : -INFINITY;

@@ -120,18 +120,23 @@ __device__ __forceinline__ void store_quad(T* p, float a, float b, float c, floa
   *reinterpret_cast<typename Quad<T>::type*>(p) = v;
 }
 
-// Store four values rounded to T and, when lo != nullptr, the rounding residuals
-// (value - stored value, rounded to T): hi + lo carries ~16 significant bits for bf16.
-template <typename T>
-__device__ __forceinline__ void store_quad_split(T* hi, T* lo, float a, float b, float c, float d) {
-  typename Quad<T>::type v, r;
-  v[0] = to_elem<T>(a); v[1] = to_elem<T>(b); v[2] = to_elem<T>(c); v[3] = to_elem<T>(d);
-  *reinterpret_cast<typename Quad<T>::type*>(hi) = v;
-  if (lo != nullptr) {
-    r[0] = to_elem<T>(a - to_f32(v[0])); r[1] = to_elem<T>(b - to_f32(v[1]));
-    r[2] = to_elem<T>(c - to_f32(v[2])); r[3] = to_elem<T>(d - to_f32(v[3]));
-    *reinterpret_cast<typename Quad<T>::type*>(lo) = r;
-  }
+// The saved rounding residual of a bf16 output, for the backward's Delta: one
+// signed byte per element, r = a - bf16(a) in units of 1/254 of the stored
+// value's ulp.  |r| <= ulp / 2, so the code lies in [-127, 127]; decoded, the
+// stored value plus the residual carries about 17 significant bits (the error
+// is at most ulp / 508), half the bytes of a bf16 residual (about 16 bits).
+// Encoder and decoder take the ulp from the stored value's exponent field
+// (subnormals and zero: the subnormal ulp 2^-133).
+__device__ __forceinline__ int resid_ulp_exp(bf16 v) {
+  const unsigned be = (__builtin_bit_cast(unsigned short, v) >> 7) & 0xFFu;
+  return (int)(be > 1u ? be : 1u) - 127 - 7;
+}
+__device__ __forceinline__ uint32_t resid_code(float a, bf16 v) {
+  const float x = rintf(ldexpf(a - (float)v, -resid_ulp_exp(v)) * 254.f);
+  return (uint32_t)(int32_t)fminf(fmaxf(x, -127.f), 127.f) & 0xFFu;
+}
+__device__ __forceinline__ float resid_value(int8_t q, bf16 v) {
+  return ldexpf((float)q * (1.f / 254.f), resid_ulp_exp(v));
 }
 
 // This lane's index in its wave, from an instruction the compiler cannot move:
@@ -240,6 +245,38 @@ __device__ __forceinline__ void stage_rows_store_at(const T* st, int nrows, RowP
     const int r = r0 + rl;
     const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * RS + c);
     if (r < nrows) *reinterpret_cast<u32x4*>(row_ptr(r) + c) = v;
+  }
+}
+// The residual codes of one wave's 32 x W bf16 block (values x[d][4 rq + e] * sc
+// as in stage_rows_in) staged as bytes: rows of W bytes padded by 16.
+template <int W, typename Acc>
+__device__ __forceinline__ void stage_codes_in(uint8_t* st, const Acc& x, float sc) {
+  constexpr int RS = W + 16;
+  const int lane = lane_here(), ln = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int d = 0; d < W / 32; ++d) {
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = x[d][4 * rq + e] * sc;
+        word |= resid_code(a, (bf16)a) << (8 * e);
+      }
+      *reinterpret_cast<uint32_t*>(st + ln * RS + 32 * d + 8 * rq + 4 * g) = word;
+    }
+  }
+}
+// The staged code rows r < nrows stored as 16-byte pieces at base + r * ld bytes.
+template <int W>
+__device__ __forceinline__ void stage_codes_store(const uint8_t* st, uint8_t* base, size_t ld, int nrows) {
+  constexpr int RS = W + 16, LPR = W / 16, RPI = 64 / LPR;
+  const int lane = lane_here(), rl = lane / LPR, c = 16 * (lane % LPR);
+  const uint32_t voff = (uint32_t)(rl * ld + c);
+#pragma unroll
+  for (int r0 = 0; r0 < 32; r0 += RPI) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(st + (r0 + rl) * RS + c);
+    if (r0 + rl < nrows) *reinterpret_cast<u32x4*>(base + r0 * ld + voff) = v;
   }
 }
 

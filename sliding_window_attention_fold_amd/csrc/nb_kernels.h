@@ -76,7 +76,7 @@ struct FwdParams {
   const void* q;
   KvChunks kv;
   void* o;
-  void* o_lo;        // optional: rounding residual of o (fp32 value minus stored value)
+  void* o_lo;        // optional (bf16): rounding residual codes of o, one byte per element (nb_device.h: resid_code)
   float* lse;
   const int32_t* row_klo;
   // Optional (null: grid order): per batch row, its query tiles in the order
@@ -105,7 +105,7 @@ struct BwdParams {
   const void* q;
   KvChunks kv;       // K, V read and dK, dV written through the chunk table
   const void* o;
-  const void* o_lo;  // optional residual saved by the forward
+  const void* o_lo;  // optional residual codes saved by the forward (bf16; ignored for float32)
   const void* dout;
   const float* lse;
   float* delta;

@@ -133,11 +133,19 @@ __global__ __launch_bounds__(kScanThreads) void live_rows_kernel(const int32_t* 
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void finalize_kernel(const float* acc, T* out, T* resid, int64_t n4) {
+__global__ __launch_bounds__(kThreads) void finalize_kernel(const float* acc, T* out, uint8_t* resid, int64_t n4) {
   const int64_t x = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (x >= n4) return;
   const f32x4 a = reinterpret_cast<const f32x4*>(acc)[x];
-  store_quad_split<T>(out + 4 * x, resid ? resid + 4 * x : nullptr, a[0], a[1], a[2], a[3]);
+  store_quad<T>(out + 4 * x, a[0], a[1], a[2], a[3]);
+  if constexpr (sizeof(T) == 2) {   // bf16: the residual codes (nb_device.h: resid_code)
+    if (resid != nullptr) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) word |= resid_code(a[e], (bf16)a[e]) << (8 * e);
+      reinterpret_cast<uint32_t*>(resid)[x] = word;
+    }
+  }
 }
 
 template <typename T>
@@ -234,10 +242,10 @@ int nb_ring_finalize(const float* out_acc, void* out, void* out_resid, int64_t R
   hipStream_t s = (hipStream_t)stream;
   if (dtype == NB_F32)
     hipLaunchKernelGGL(finalize_kernel<float>, dim3((unsigned)grid), dim3(kThreads), 0, s, out_acc, (float*)out,
-                       (float*)out_resid, n4);
+                       nullptr, n4);
   else
     hipLaunchKernelGGL(finalize_kernel<bf16>, dim3((unsigned)grid), dim3(kThreads), 0, s, out_acc, (bf16*)out,
-                       (bf16*)out_resid, n4);
+                       (uint8_t*)out_resid, n4);
   return status(hipGetLastError());
 }
 

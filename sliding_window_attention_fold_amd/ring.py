@@ -119,9 +119,11 @@ def merge_live_(out_acc, lse_acc, out_step, lse_step, live_index, n_live, n_live
 
 
 def finalize(out_acc: torch.Tensor, dtype: torch.dtype, with_resid: bool = True):
-    """``(out, resid)``: the merged output rounded to ``dtype`` and its rounding residual."""
+    """``(out, resid)``: the merged output rounded to ``dtype`` and, for bf16, its rounding-residual codes
+    (int8, one per element; None for float32)."""
     out = torch.empty(out_acc.shape, dtype=dtype, device=out_acc.device)
-    resid = torch.empty_like(out) if with_resid else None
+    resid = (torch.empty(out.shape, dtype=torch.int8, device=out.device)
+             if with_resid and dtype == torch.bfloat16 else None)
     D = out_acc.shape[-1]
     _lib.check(_lib.load().nb_ring_finalize(_p(out_acc), _p(out), _p(resid), out_acc.numel() // D, D,
                                             _DTYPES[dtype], _s(out_acc.device)), "nb_ring_finalize")

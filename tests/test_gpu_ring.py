@@ -135,15 +135,36 @@ def test_merge_edge_rows():
     assert torch.equal(oa_d[0, 0, 3:5].cpu(), torch.zeros((2, D)))
 
 
+def resid_codes(acc: torch.Tensor):
+    """The residual codes as include/nbattn.h defines them, computed on the host in float32: r = a - bf16(a) in
+    units of 1/254 of the bf16 value's ulp (2^(max(biased exponent, 1) - 134)), rounded to nearest even and
+    clamped to [-127, 127]; with that ulp."""
+    a = acc.float().numpy()
+    v = acc.to(torch.bfloat16)
+    vf = v.float().numpy()
+    be = (v.view(torch.int16).numpy().astype(np.int32) >> 7) & 0xFF
+    e = np.maximum(be, 1) - 134
+    x = np.rint(np.ldexp(a - vf, -e).astype(np.float32) * np.float32(254))
+    return np.clip(x, -127, 127).astype(np.int8), np.ldexp(np.float32(1), e).astype(np.float32)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_finalize_and_grad_add(dt):
     say(f"[ring] finalize / grad_add {dt}")
     g = torch.Generator("cpu").manual_seed(11)
     acc = torch.randn((3, 5, 17, 64), generator=g)
+    acc[0, 0, 0, :4] = torch.tensor([0.0, -2.5, 1e30, 3e-30])   # zero, exact in bf16, large, small
     out, resid = ring.finalize(acc.to(DEV), DT[dt])
     assert torch.equal(out.cpu(), acc.to(DT[dt]))
-    want = (acc - acc.to(DT[dt]).float()).to(DT[dt])
-    assert torch.equal(resid.cpu(), want)
+    if dt == "f32":
+        assert resid is None   # float32 O is exact: no residual
+    else:
+        want, ulp = resid_codes(acc)
+        got = resid.cpu().numpy()
+        assert np.array_equal(got, want)
+        # decoded, O is within 1/508 of a bf16 ulp (plus the decode's own rounding)
+        dec = out.cpu().float().numpy() + got.astype(np.float32) / np.float32(254) * ulp
+        assert np.all(np.abs(dec - acc.numpy()) <= ulp * (1.0 / 508 + 2.0 ** -20))
     a = torch.randn((4, 1000), generator=g)
     s = torch.randn((4, 1000), generator=g).to(DT[dt])
     a_d = a.to(DEV)
