@@ -370,3 +370,52 @@ def test_training_step_never_synchronises():
     assert_close("dQ chunks", dq_c.float().cpu().numpy(), res.dq.float().cpu().numpy(), "bf16")
     for c in range(len(chunks)):
         assert att_c[c] == bool(dks[c].any() or dvs[c].any())
+
+
+@pytest.mark.parametrize("name", ["w2s", "w2s_d64", "w5s"])
+def test_output_residual_codes_and_delta(name):
+    """The forward's byte residual of O (include/nbattn.h, o_resid): every code in [-127, 127]; the decoded residual
+    (code / 254 of the bf16 value's ulp) moves O toward the fp64 oracle's O; and the prep's Delta, dO . (O +
+    decoded residual) on every real row and 0 on the others, equals the same sum formed on the host in fp64 from the
+    header's definition.  The kernel's fp32 O is itself about as far from the exact O as its bf16 rounding (P is
+    rounded to bf16 before P V), so the residual cannot close the whole gap: a CPU emulation of that arithmetic gives
+    a median-error ratio of 0.60-0.67, a max-error ratio near 0.33 and a correlation of 0.81-0.85 between the
+    residual and the oracle's correction, at 40 to 300 keys per row.  Codes of the wrong sign, scale or none at all
+    fail the bounds below."""
+    inp = workload_inputs(SMALL[name], "bf16")
+    say(f"[residual codes] {name}")
+    dev = torch.device("cuda:0")
+    lib = _lib.load()
+    ids = torch.from_numpy(inp.ids).to(dev)
+    pad = None if inp.pad is None else torch.from_numpy(np.ascontiguousarray(inp.pad)).to(dev)
+    seg = nb.segment_build(ids, inp.L, inp.window, pad)
+    q, k, v, do = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v, inp.do))
+    out, saved = nb.attn_fwd(q, k, v, seg)
+    B, Hq, L, D = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    wsb = lib.nb_attn_bwd_workspace_bytes(B, Hq, Hkv, L, S, D, _lib.NB_BF16)
+    ws = torch.full((wsb,), 255, dtype=torch.uint8, device=dev)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    _lib.check(lib.nb_attn_bwd_prep(P(do), P(out), P(saved.out_resid), P(seg.buf), B, Hq, Hkv, L, S, D, inp.window,
+                                    _lib.NB_BF16, P(ws), wsb, sp), "prep")
+    torch.cuda.synchronize()
+    assert saved.out_resid.dtype == torch.int8 and saved.out_resid.shape == out.shape
+    codes = saved.out_resid.cpu().numpy().astype(np.float64)
+    assert codes.min() >= -127 and codes.max() <= 127
+    o_b = out.float().cpu().numpy().astype(np.float64)
+    be = (out.cpu().view(torch.int16).numpy().astype(np.int32) >> 7) & 0xFF
+    ulp = np.ldexp(1.0, np.maximum(be, 1) - 134)
+    o_fine = o_b + codes / 254.0 * ulp
+    O, _ = orc.attention_forward(inp.q, inp.k, inp.v, inp.folded, inp.window, D ** -0.5)
+    real = orc.real_rows(inp.folded, inp.L)
+    rr = np.broadcast_to(real[:, None, :, None], o_b.shape)
+    err_b, err_f = np.abs(o_b - O)[rr], np.abs(o_fine - O)[rr]
+    assert np.median(err_f) <= 0.8 * np.median(err_b), (np.median(err_f), np.median(err_b))
+    assert err_f.max() <= err_b.max()
+    corr = np.corrcoef((o_fine - o_b)[rr], (O - o_b)[rr])[0, 1]
+    assert corr > 0.6, corr
+    delta = ws[:B * Hq * L * 4].view(torch.float32).cpu().numpy().reshape(B, Hq, L).astype(np.float64)
+    want = (inp.do.double().numpy() * o_fine).sum(-1)
+    want[~np.broadcast_to(real[:, None, :], want.shape)] = 0.0
+    assert np.allclose(delta, want, rtol=1e-5, atol=1e-5 * np.abs(want).max())
