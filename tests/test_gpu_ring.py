@@ -16,6 +16,7 @@ from oracle import nbattn_oracle as orc
 from oracle import ring_oracle as ro
 from sliding_window_attention_fold_amd import ring
 from gpu_cases import assert_close, say
+from resid_code import resid_codes
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -133,19 +134,6 @@ def test_merge_edge_rows():
     assert_close("lse", la_d.cpu().numpy(), lse_ref, "f32")
     assert not torch.isnan(oa_d).any()
     assert torch.equal(oa_d[0, 0, 3:5].cpu(), torch.zeros((2, D)))
-
-
-def resid_codes(acc: torch.Tensor):
-    """The residual codes as include/nbattn.h defines them, computed on the host in float32: r = a - bf16(a) in
-    units of 1/254 of the bf16 value's ulp (2^(max(biased exponent, 1) - 134)), rounded to nearest even and
-    clamped to [-127, 127]; with that ulp."""
-    a = acc.float().numpy()
-    v = acc.to(torch.bfloat16)
-    vf = v.float().numpy()
-    be = (v.view(torch.int16).numpy().astype(np.int32) >> 7) & 0xFF
-    e = np.maximum(be, 1) - 134
-    x = np.rint(np.ldexp(a - vf, -e).astype(np.float32) * np.float32(254))
-    return np.clip(x, -127, 127).astype(np.int8), np.ldexp(np.float32(1), e).astype(np.float32)
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
