@@ -145,7 +145,11 @@ __device__ __forceinline__ constexpr int ds_slot(int k) { return (k & 0x13) | ((
 // (work_order_kernel), so the long tiles start first.
 // DS: the item may store dS (p.dsbuf non-null); compiled into the dK/dV-only
 // kernel alone, so the combined kernel carries none of its registers.
-template <typename T, int D, bool CH, bool DS>
+// AC (in-step schedules, D <= 128): role A issues every tile copy, so role B
+// waves never stall issuing copies; chosen for neighbourhoods without a left
+// window (long bands), where it measured 2-3 % faster -- on short windowed
+// bands (batched short documents) it measured 4 % slower.
+template <typename T, int D, bool CH, bool DS, bool AC = false>
 __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm, DkvStage<T, D>& stage, int f) {
   typedef DkvCfg<T, D> C;
   typedef Tile<T, C::BQ, D> TL;
@@ -169,7 +173,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
   // NKG - 1) issues every copy: role B's dS stores count in the same vector
   // memory counter as copies, so a role-B wait for a step's copies would also
   // wait for the stores issued after them -- and role A has the slack.
-  const TileDma<T, C::BQ, D, C::SKEW ? C::NKG : C::NW> dma;
+  const TileDma<T, C::BQ, D, (C::SKEW || AC) ? C::NKG : C::NW> dma;
   const int kvh = f % p.Hkv;
   const int code = p.order[f / p.Hkv];
   const int b = code / n_kt, kt = code % n_kt;
@@ -263,7 +267,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& p, DkvSmem<T, D>& sm,
     const int i0 = t * C::BQ;
     const int nr = min(C::BQ, Lr - i0);
     const size_t rb = (size_t)hh * Lr + i0;
-    if (!C::SKEW || role_a) {
+    if ((!C::SKEW && !AC) || role_a) {
       dma.issue_unseen(Qs, q_it + rb * D, nr);
       dma.issue_unseen(Gs, do_it + rb * D, nr);
     }
@@ -1466,7 +1470,7 @@ struct BwdSmemFor {
 // XCD, whose L2 then holds the K/V and Q/dO rows its items share.  Running
 // both passes in one grid lets the shorter dQ items fill the tail of the dK/dV
 // items.  Which workgroup computes an item never changes the result.
-template <typename T, int D, int MODE, int KV>
+template <typename T, int D, int MODE, int KV, bool AC = false>
 __global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void bwd_kernel(BwdParams p) {
   static_assert(DkvCfg<T, D>::NT == BwdShape<T, D>::NT && DqCfg<T, D>::NT == BwdShape<T, D>::NT,
                 "one block shape for both passes");
@@ -1474,7 +1478,7 @@ __global__ __launch_bounds__((BwdShape<T, D>::NT), (BwdShape<T, D>::OCC)) void b
   // runs alone, and a float32 dQ item's tiles would not fit beside nothing)
   __shared__ typename BwdSmemFor<T, D, MODE>::type sm;
   auto dkdv = [&](int f) {
-    if constexpr (MODE != 2) dkdv_item<T, D, KV != kKvConcat, MODE == 1>(p, sm.kv, sm.kst, f);
+    if constexpr (MODE != 2) dkdv_item<T, D, KV != kKvConcat, MODE == 1, AC>(p, sm.kv, sm.kst, f);
   };
   const int n_kv = (MODE & 1) ? p.B * ((p.S + DkvCfg<T, D>::BK - 1) / DkvCfg<T, D>::BK) * p.Hkv : 0;
   const int n_q = (MODE & 2) ? p.B * ((p.L + DqCfg<T, D>::BM - 1) / DqCfg<T, D>::BM) * p.Hq : 0;
@@ -1538,6 +1542,20 @@ static hipError_t launch_prep_t(const BwdParams& p, bool with_delta, int modes, 
   return hipGetLastError();
 }
 
+// The persistent backward kernel, with the dK/dV items' copy placement
+// (dkdv_item, AC): role A issues every copy in the in-step schedules when the
+// neighbourhood has no left window.
+template <typename T, int D, int MODE, int KV>
+static void launch_bwd_kernel(const BwdParams& p, dim3 grid, hipStream_t s) {
+  if constexpr ((MODE & 1) && !DkvCfg<T, D>::SKEW && D <= 128) {
+    if (p.window < 0) {
+      hipLaunchKernelGGL((bwd_kernel<T, D, MODE, KV, true>), grid, dim3(BwdShape<T, D>::NT), 0, s, p);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((bwd_kernel<T, D, MODE, KV>), grid, dim3(BwdShape<T, D>::NT), 0, s, p);
+}
+
 template <typename T, int D, int MODE>
 static hipError_t launch_main_t(const BwdParams& p, hipStream_t s) {
   const long long n_kv = (MODE & 1) ? (long long)p.B * ((p.S + DkvCfg<T, D>::BK - 1) / DkvCfg<T, D>::BK) * p.Hkv : 0;
@@ -1558,7 +1576,7 @@ static hipError_t launch_main_t(const BwdParams& p, hipStream_t s) {
       return hipGetLastError();
     }
     if (!concat) {
-      hipLaunchKernelGGL((bwd_kernel<T, D, MODE, kKvPair>), grid, dim3(BwdShape<T, D>::NT), 0, s, p);
+      launch_bwd_kernel<T, D, MODE, kKvPair>(p, grid, s);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess || !kv_may_need_general(p.kv, p.window, DqCfg<T, D>::BM, DqCfg<T, D>::BN)) return e;
       dim3 grid2((unsigned)std::min<long long>(n_q, (long long)device_cu_count() * BwdShape<T, D>::OCC));
@@ -1578,7 +1596,7 @@ static hipError_t launch_main_t(const BwdParams& p, hipStream_t s) {
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((bwd_kernel<T, D, MODE, kKvConcat>), grid, dim3(BwdShape<T, D>::NT), 0, s, p);
+  launch_bwd_kernel<T, D, MODE, kKvConcat>(p, grid, s);
   return hipGetLastError();
 }
 
