@@ -1258,7 +1258,7 @@ struct DeltaCfg {
   static constexpr int V = (16 / (int)sizeof(T)) * 64 >= D ? 16 / (int)sizeof(T) : D / 64;
   static constexpr int LPR = D / V;               // lanes per row
   static constexpr int RPI = 64 / LPR;            // rows of a wave per load round
-  static constexpr int IT = D >= 512 ? 2 : D >= 256 ? 1 : 4;   // load rounds in flight (measured per head dim)
+  static constexpr int IT = D >= 512 ? 2 : D >= 256 ? 1 : 2;   // load rounds in flight (measured per head dim)
   static constexpr int ROWS = 4 * RPI * IT;       // rows per workgroup (four waves)
   static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "a row's lanes tile the wave");
 };
