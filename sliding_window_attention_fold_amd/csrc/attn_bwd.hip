@@ -1248,10 +1248,12 @@ __global__ __launch_bounds__(256, (DqsCfg<T, D>::OCC)) void dq_ds_kernel(BwdPara
 // its saved rounding residual (fp32-accurate); 0 for padding rows.  Every lane
 // reads 16 bytes of a row per tensor (D / 8 lanes per bf16 row, D / 4 per
 // float32 row) and handles IT rows, all of whose loads are issued before any
-// arithmetic, so each lane keeps 3 x IT 16-byte loads in flight; the lanes of a
-// row reduce with shuffles.  (Eight rows per workgroup with 4- to 16-byte
-// loads launched one workgroup per 12 KB moved and measured about half the
-// HBM rate.)
+// arithmetic, so each lane keeps 2 x IT 16-byte loads and IT residual loads in
+// flight; the lanes of a row reduce with shuffles.  (Eight rows per workgroup
+// with 4- to 16-byte loads launched one workgroup per 12 KB moved and
+// measured about half the HBM rate; workgroups of 512 threads measured 5 %
+// faster than 256 on the sliding layer, 1024 and 128 slower.)
+constexpr int kPrepNT = 512;          // threads of the prep kernel's workgroups
 template <typename T, int D>
 struct DeltaCfg {
   // elements per load: 16 bytes, or more where a row would need more than a wave
@@ -1259,7 +1261,7 @@ struct DeltaCfg {
   static constexpr int LPR = D / V;               // lanes per row
   static constexpr int RPI = 64 / LPR;            // rows of a wave per load round
   static constexpr int IT = D >= 512 ? 2 : D >= 256 ? 1 : 2;   // load rounds in flight (measured per head dim)
-  static constexpr int ROWS = 4 * RPI * IT;       // rows per workgroup (four waves)
+  static constexpr int ROWS = (kPrepNT / 64) * RPI * IT;   // rows per workgroup
   static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "a row's lanes tile the wave");
 };
 
@@ -1318,7 +1320,6 @@ __device__ __forceinline__ void delta_rows(const BwdParams& p, int wg) {
 //          row's band start to the last row's position (an estimate when the
 //          first rows are padding -- the order only affects speed).
 // Also empties the work queues of the backward kernel.
-constexpr int kPrepNT = 256;          // threads of the prep kernel's workgroups
 constexpr int kOrderMax = 2048;       // items sorted in LDS
 constexpr int kOrderBandMax = 2048;   // query-tile band starts staged in LDS
 
