@@ -96,16 +96,19 @@ def test_order_leaves_results_unchanged():
     assert torch.equal(s1.lse, s2.lse)
 
 
-def test_multi_round_forward_full_parity():
-    """A forward whose grid exceeds one round of workgroups (18 query tiles x 32 heads = 576 workgroups, two per
-    CU at D = 128) runs in the builder's order; O, LSE and the gradients match the oracle element by element."""
+@pytest.mark.parametrize("B, W, per_cu", [(1, 600, 2), (2, 300, 3)])
+def test_multi_round_forward_full_parity(B, W, per_cu):
+    """A forward whose grid exceeds one round of workgroups runs in the builder's order; O, LSE and the gradients
+    match the oracle element by element.  At D = 128 the forward takes two workgroups per CU with 64-key tiles,
+    and three per CU with 32-key tiles when the left window is at most 512 keys: 18 query tiles x 32 heads x B
+    workgroups against per_cu workgroups per CU."""
     from gpu_cases import custom_inputs, full_parity
 
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    B, Hq, Hkv, D, L, S, W = 1, 32, 8, 128, 2200, 2600, 300
-    assert ((L + ROWS - 1) // ROWS) * Hq * B > 2 * n_cu, "the grid must take more than one round here"
+    Hq, Hkv, D, L, S = 32, 8, 128, 2200, 2600
+    assert ((L + ROWS - 1) // ROWS) * Hq * B > per_cu * n_cu, "the grid must take more than one round here"
     rng = np.random.default_rng(11)
-    ids = _docs(rng, S, 400)[None]
+    ids = np.stack([_docs(rng, S, 400) for _ in range(B)])
     # padding as whole documents (every 7th) and a tail: every document stays one run of its id
     ids[np.isin(ids, np.arange(7, ids.max() + 1, 7))] = 0
     pad = np.zeros((B, S), np.uint8)
@@ -113,6 +116,7 @@ def test_multi_round_forward_full_parity():
     say(f"[fwd order] multi-round forward B={B} Hq={Hq} Hkv={Hkv} D={D} L={L} S={S} W={W}")
     seg = nb.segment_build(torch.from_numpy(ids).cuda(), L, W, torch.from_numpy(pad).cuda())
     assert seg.header_host()["status"] == 0
-    order = seg.fwd_order.cpu().numpy()
-    assert not np.array_equal(order, np.arange(order.size)), "the order should differ from grid order"
+    order = seg.fwd_order.cpu().numpy().reshape(B, -1)
+    assert not np.array_equal(order, np.broadcast_to(np.arange(order.shape[1]), order.shape)), \
+        "the order should differ from grid order"
     full_parity(custom_inputs(ids, pad, Hq, Hkv, D, L, W, "bf16", seed=5), "bf16")
