@@ -192,14 +192,41 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 // columns of one row, so stored directly a store instruction writes 16 bytes
 // to each of 32 rows (32 cache lines for 512 bytes); staged and read back as
 // 16-byte row pieces, an instruction writes whole row segments.  NWS waves
-// stage 32 rows of W columns each; rows padded by 16 bytes (the 8-byte writes
-// down a column spread over the banks; rows stay 16-byte aligned).
+// stage 32 rows of W columns each, rows padded by 16 bytes (they stay 16-byte
+// aligned).
+//
+// Bank layout (64 banks of 4 bytes).  Writers: lanes 0..31 hold rows 0..31 at
+// the same 8-byte half of a 16-byte piece (lanes 32..63 the other half), so
+// rows 16..31 keep the two halves of every piece swapped; with the 16-byte pad
+// the 64 lanes of a 4-byte write (the residual codes) then cover the 64 banks
+// once, as do 32 lanes of an 8-byte write.  Readers: a row of W columns is LPR
+// pieces, read by LPR lanes; where the 16 lanes of one 16-byte read cycle span
+// several rows (LPR < 16), those rows sit LPR physical rows apart, in disjoint
+// banks.
 template <typename T, int NWS, int W>
 struct RowStage {
   static constexpr bool ON = sizeof(T) == 2;
   static constexpr int RS = W + 8;
   __attribute__((aligned(1024))) T r[ON ? NWS : 1][ON ? 32 : 1][ON ? RS : 1];
 };
+// Physical staging row of row r (0..31) for rows of LPR 16-byte pieces.  For r0
+// a multiple of 64 / LPR and rl < 64 / LPR it is additive:
+// stage_row(r0 + rl) = stage_row(r0) + stage_row(rl).
+template <int LPR>
+__device__ __forceinline__ constexpr int stage_row(int r) {
+  if constexpr (LPR >= 16) {
+    return r;
+  } else {
+    constexpr int P = 16 / LPR;
+    return (r & 16) | ((r & 15) / P) | ((r % P) * LPR);
+  }
+}
+// A staged 16-byte piece of row r as written by stage_rows_in / stage_codes_in,
+// halves back in order when hi (r >= 16; constant in the unrolled loops below).
+__device__ __forceinline__ u32x4 stage_piece(const void* p, bool hi) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  return hi ? u32x4{v[2], v[3], v[0], v[1]} : v;
+}
 // One wave's 32 x W block (lane: row ln, columns 32 d + 8 rq + 4 g .. + 3 of
 // block d, values x[d][4 rq + e] * sc) written to its staging rows st.
 // Wave-local: LDS operations of one wave complete in order, so the read-back
@@ -208,7 +235,8 @@ template <typename T, int W, typename Acc>
 __device__ __forceinline__ void stage_rows_in(T* st, const Acc& x, float sc) {
   typedef typename Quad<T>::type Q4;
   constexpr int RS = W + 8;
-  const int lane = lane_here(), ln = lane & 31, g = lane >> 5;
+  const int lane = lane_here(), ln = lane & 31, g = lane >> 5, h = ln >> 4;
+  T* const dst = st + stage_row<W / 8>(ln) * RS + 4 * (g ^ h);
 #pragma unroll
   for (int d = 0; d < W / 32; ++d) {
 #pragma unroll
@@ -216,7 +244,7 @@ __device__ __forceinline__ void stage_rows_in(T* st, const Acc& x, float sc) {
       Q4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = to_elem<T>(x[d][4 * rq + e] * sc);
-      *reinterpret_cast<Q4*>(st + ln * RS + 32 * d + 8 * rq + 4 * g) = v;
+      *reinterpret_cast<Q4*>(dst + 32 * d + 8 * rq) = v;
     }
   }
 }
@@ -228,9 +256,10 @@ __device__ __forceinline__ void stage_rows_store(const T* st, T* base, size_t ld
   constexpr int RS = W + 8, LPR = W / 8, RPI = 64 / LPR;
   const int lane = lane_here(), rl = lane / LPR, c = 8 * (lane % LPR);
   const uint32_t voff = (uint32_t)((rl * ld + c) * sizeof(T));
+  const T* const src = st + stage_row<LPR>(rl) * RS + c;
 #pragma unroll
   for (int r0 = 0; r0 < 32; r0 += RPI) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(st + (r0 + rl) * RS + c);
+    const u32x4 v = stage_piece(src + stage_row<LPR>(r0) * RS, r0 >= 16);
     char* const row = reinterpret_cast<char*>(base + r0 * ld);
     if (r0 + rl < nrows) *reinterpret_cast<u32x4*>(row + voff) = v;
   }
@@ -240,19 +269,23 @@ template <typename T, int W, typename RowPtr>
 __device__ __forceinline__ void stage_rows_store_at(const T* st, int nrows, RowPtr row_ptr) {
   constexpr int RS = W + 8, LPR = W / 8, RPI = 64 / LPR;
   const int lane = lane_here(), rl = lane / LPR, c = 8 * (lane % LPR);
+  const T* const src = st + stage_row<LPR>(rl) * RS + c;
 #pragma unroll
   for (int r0 = 0; r0 < 32; r0 += RPI) {
     const int r = r0 + rl;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * RS + c);
+    const u32x4 v = stage_piece(src + stage_row<LPR>(r0) * RS, r0 >= 16);
     if (r < nrows) *reinterpret_cast<u32x4*>(row_ptr(r) + c) = v;
   }
 }
 // The residual codes of one wave's 32 x W bf16 block (values x[d][4 rq + e] * sc
-// as in stage_rows_in) staged as bytes: rows of W bytes padded by 16.
+// as in stage_rows_in) staged as bytes: rows of W bytes padded by 16, in the
+// layout above (a lane's 4 codes at byte 32 d + 8 rq + 4 g of its row, the
+// 8-byte halves of each 16-byte piece swapped in rows 16..31).
 template <int W, typename Acc>
 __device__ __forceinline__ void stage_codes_in(uint8_t* st, const Acc& x, float sc) {
   constexpr int RS = W + 16;
-  const int lane = lane_here(), ln = lane & 31, g = lane >> 5;
+  const int lane = lane_here(), ln = lane & 31, g = lane >> 5, sw = 8 * (ln >> 4);
+  uint8_t* const dst = st + stage_row<W / 16>(ln) * RS + 4 * g;
 #pragma unroll
   for (int d = 0; d < W / 32; ++d) {
 #pragma unroll
@@ -263,7 +296,7 @@ __device__ __forceinline__ void stage_codes_in(uint8_t* st, const Acc& x, float 
         const float a = x[d][4 * rq + e] * sc;
         word |= resid_code(a, (bf16)a) << (8 * e);
       }
-      *reinterpret_cast<uint32_t*>(st + ln * RS + 32 * d + 8 * rq + 4 * g) = word;
+      *reinterpret_cast<uint32_t*>(dst + 32 * d + 8 * rq + ((rq & 1) ? -sw : sw)) = word;
     }
   }
 }
@@ -273,9 +306,10 @@ __device__ __forceinline__ void stage_codes_store(const uint8_t* st, uint8_t* ba
   constexpr int RS = W + 16, LPR = W / 16, RPI = 64 / LPR;
   const int lane = lane_here(), rl = lane / LPR, c = 16 * (lane % LPR);
   const uint32_t voff = (uint32_t)(rl * ld + c);
+  const uint8_t* const src = st + stage_row<LPR>(rl) * RS + c;
 #pragma unroll
   for (int r0 = 0; r0 < 32; r0 += RPI) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(st + (r0 + rl) * RS + c);
+    const u32x4 v = stage_piece(src + stage_row<LPR>(r0) * RS, r0 >= 16);
     if (r0 + rl < nrows) *reinterpret_cast<u32x4*>(base + r0 * ld + voff) = v;
   }
 }
