@@ -298,7 +298,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU "
               "path: each context-parallel rank's local attention is one GPU's work", file=sys.stderr)
         return 2
     if int(os.environ.get("WORLD_SIZE", "1")) != 1:
